@@ -1,0 +1,136 @@
+"""Oracle: shared-memory (LDS) layout maps and the bank-conflict model.
+
+TEST INFRASTRUCTURE (see the package docstring): not imported by the library.
+
+Source: "CUDA Swizzle & bank conflict" (whc-imageprocess.github.io):
+  * section "Bank Conflict" and the hardware background before it: memory is split into banks that
+    work in parallel; an access instruction costs one pass per phase of lanes, plus one more pass
+    for every extra distinct word that the phase needs from an already-busy bank; lanes reading the
+    same word share it (broadcast). 128-bit and 64-bit accesses are served in phases of 8 and 16
+    lanes of a 32-lane warp (section "memory coalesce").
+  * sections "Padding" / "Padding Row-Major Layout": row-major with one extra element per row.
+  * section "Case Study / Matrix Transpose", swizzling variant: physical column = column XOR row.
+  * section "Hopper TMA 的 swizzling": the 16-byte-chunk swizzle of a 128-byte row.
+  * section "Triton - Shared Layout swizzling": the vec / perPhase / maxPhase chunk XOR family.
+
+Layout maps return the physical element index of logical element (r, c) of a tile whose logical
+rows hold W elements.
+"""
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------- layout maps
+
+def naive(r, c, W):
+    """Row-major: element (r, c) at r*W + c."""
+    return r * W + c
+
+
+def padded(r, c, W, pad=1):
+    """Row-major with ``pad`` unused elements after every row: r*(W+pad) + c."""
+    return r * (W + pad) + c
+
+
+def xor_element(r, c, W):
+    """Element-wise XOR swizzle of the transpose case study: (r, c) stored at column c XOR r.
+
+    Defined for a square power-of-two tile (r, c < W), where c XOR r stays inside the row."""
+    return r * W + (c ^ r)
+
+
+def chunk_xor(r, c, W, vec, per_phase, max_phase):
+    """Triton shared-layout swizzle: chunks of ``vec`` elements are permuted inside a row.
+
+    Chunk c // vec of row r is stored at chunk (c // vec) XOR ((r // per_phase) mod max_phase);
+    the position inside a chunk is kept. XOR with a fixed value is its own inverse, so the same
+    formula also gives, for a physical position, the logical column stored there.
+    """
+    chunk = (c // vec) ^ ((r // per_phase) % max_phase)
+    return r * W + chunk * vec + c % vec
+
+
+def tma_swizzle(y, x, NX, elem_bytes, swizzle_bytes=128):
+    """The 16-byte-chunk swizzle the page describes for a ``T array[][NX]`` with NX*sizeof(T) equal
+    to the swizzle size: the flat byte offset of (y, x) is cut into 16-byte chunks; the chunk's row
+    (chunk index div 8) is kept and its column (chunk index mod 8) is XOR-ed with that row; the
+    element keeps its place inside the chunk. Returns the physical (y, x_swz)."""
+    if NX * elem_bytes != swizzle_bytes:
+        raise ValueError("row must be exactly one swizzle span")
+    per_chunk = 16 // elem_bytes
+    i16 = (y * NX + x) * elem_bytes // 16
+    y16 = i16 // 8
+    x16 = i16 % 8
+    x16_swz = y16 ^ x16
+    x_swz = (x16_swz * per_chunk) % NX + x % per_chunk
+    return y, x_swz
+
+
+# ----------------------------------------------------------------------------- bank model
+
+def instruction_passes(byte_addrs, access_bytes, num_banks=32, bank_bytes=4, lanes=None):
+    """Passes (wavefronts) one shared-memory instruction needs under the page's bank model.
+
+    ``byte_addrs``: start byte address of each active lane, in lane order. Every lane touches
+    ``access_bytes`` consecutive bytes, i.e. access_bytes/bank_bytes consecutive words; word w sits
+    in bank w mod num_banks. The lanes are served in phases of as many lanes as fill the banks once
+    (num_banks*bank_bytes/access_bytes lanes, at most the lane count). Within a phase, each bank
+    delivers one distinct word per pass and lanes asking for the same word share it, so the phase
+    needs as many passes as the busiest bank has distinct words.
+    Returns (passes, phases); passes - phases is the number of extra (conflict) passes.
+    """
+    addrs = np.asarray(byte_addrs, dtype=np.int64)
+    if lanes is None:
+        lanes = len(addrs)
+    words_per_lane = max(1, access_bytes // bank_bytes)
+    lanes_per_phase = max(1, min(lanes, (num_banks * bank_bytes) // access_bytes))
+    passes = 0
+    phases = 0
+    for start in range(0, len(addrs), lanes_per_phase):
+        phase = addrs[start:start + lanes_per_phase]
+        words = set()
+        for a in phase:
+            first = int(a) // bank_bytes
+            for w in range(words_per_lane):
+                words.add(first + w)
+        per_bank = {}
+        for w in words:
+            per_bank[w % num_banks] = per_bank.get(w % num_banks, 0) + 1
+        passes += max(per_bank.values())
+        phases += 1
+    return passes, phases
+
+
+def transpose_store_passes(M, N, tile, layout, elem_bytes=4, num_banks=32, bank_bytes=4,
+                           warp=32, pad=1):
+    """Shared-store passes of the transpose case study's kernels, over the whole launch.
+
+    The kernel runs (N/tile) x (M/tile) blocks of tile x tile threads, one element each; thread
+    (tx, ty) stores its element at logical shared position [tx][ty] (the transposed store) of a
+    tile x tile array laid out by ``layout`` ("naive", "padded" or "xor"). Warps are formed from
+    consecutive threads in x-fastest order. Shared addresses do not depend on the block index, so
+    one block is simulated and the counts are multiplied by the number of blocks.
+    Returns (total passes, total extra passes).
+    """
+    if M % tile or N % tile:
+        raise ValueError("the case study's sizes are tile multiples")
+    blocks = (M // tile) * (N // tile)
+    threads = [(tx, ty) for ty in range(tile) for tx in range(tile)]   # x fastest
+    passes = extra = 0
+    for w0 in range(0, len(threads), warp):
+        addrs = []
+        for tx, ty in threads[w0:w0 + warp]:
+            r, c = tx, ty                                  # transposed store: s[tx][ty]
+            if layout == "naive":
+                e = naive(r, c, tile)
+            elif layout == "padded":
+                e = padded(r, c, tile, pad)
+            elif layout == "xor":
+                e = xor_element(r, c, tile)
+            else:
+                raise ValueError(layout)
+            addrs.append(e * elem_bytes)
+        p, ph = instruction_passes(addrs, elem_bytes, num_banks, bank_bytes)
+        passes += p
+        extra += p - ph
+    return passes * blocks, extra * blocks

@@ -1,0 +1,94 @@
+"""Pins of the LDS layout maps and the bank model. CPU only.
+
+Pins: the five Triton shared-layout grids and the transpose case study's row-1 order printed on
+"CUDA Swizzle & bank conflict"; the page's TMA chunk formula, which must give the same map as the
+Triton family at vec = 16 bytes / element size, per_phase 1, max_phase 8; the three swizzle-map
+properties the page lists (one-to-one, range kept, distinct within a column); the page's stride
+claims (stride s gives an s-way conflict) and its closed-form conflict count for the naive
+1024 x 2048 transpose (2048 blocks x 32 warps x 31 extra passes, 2048 x 32 x 32 passes), with zero
+for the padded and XOR layouts.
+"""
+
+import numpy as np
+import pytest
+
+from conftest import golden_lines, golden_sections
+from oracle import lds
+
+
+def test_triton_grids():
+    sec = golden_sections("p2_triton_shared_layouts.txt")
+    assert len(sec) == 5
+    for name, (hdr, lines) in sec.items():
+        vec, pp, mp, W = (int(v) for v in hdr)
+        grid = np.array([[int(v) for v in ln.split()] for ln in lines])
+        for r in range(grid.shape[0]):
+            for c in range(W):
+                assert lds.chunk_xor(r, c, W, vec, pp, mp) == grid[r, c], (name, r, c)
+
+
+def test_transpose_xor_row1():
+    lines = golden_lines("p2_transpose_xor_row1.txt")
+    prefix = [int(v) for v in lines[0].split(":")[1].split()]
+    suffix = [int(v) for v in lines[1].split(":")[1].split()]
+    order = [lds.xor_element(1, c, 32) - 32 for c in range(32)]
+    assert order[:len(prefix)] == prefix and order[-len(suffix):] == suffix
+
+
+@pytest.mark.parametrize("elem_bytes", [1, 2, 4])
+def test_tma_formula_equals_triton_family(elem_bytes):
+    NX = 128 // elem_bytes
+    vec = 16 // elem_bytes
+    for y in range(24):
+        for x in range(NX):
+            yy, xs = lds.tma_swizzle(y, x, NX, elem_bytes)
+            assert yy == y
+            assert y * NX + xs == lds.chunk_xor(y, x, NX, vec, 1, 8)
+
+
+@pytest.mark.parametrize("W,vec,pp,mp", [(32, 1, 1, 32), (64, 8, 1, 8), (64, 8, 2, 8), (64, 4, 1, 16),
+                                          (8, 1, 2, 4), (128, 8, 1, 8)])
+def test_swizzle_properties(W, vec, pp, mp):
+    rows = 64
+    phys = np.array([[lds.chunk_xor(r, c, W, vec, pp, mp) for c in range(W)] for r in range(rows)])
+    # one-to-one and range kept: every row is a permutation of its own W slots
+    for r in range(rows):
+        assert sorted(phys[r] - r * W) == list(range(W))
+    # distinct within a column for rows of one full phase cycle (pp*mp rows share no column slot
+    # when vec == 1); for vec > 1 the chunk index is what differs
+    if vec == 1 and mp == W:
+        for c in range(W):
+            cols = [phys[r, c] - r * W for r in range(min(rows, pp * mp)) if r % pp == 0]
+            assert len(set(cols)) == len(cols)
+
+
+def test_xor_element_properties():
+    W = 64
+    phys = np.array([[lds.xor_element(r, c, W) - r * W for c in range(W)] for r in range(W)])
+    for r in range(W):
+        assert sorted(phys[r]) == list(range(W))
+    for c in range(W):
+        assert len(set(phys[:, c])) == W
+
+
+@pytest.mark.parametrize("stride", [1, 2, 4, 8, 16, 32])
+def test_stride_conflict_degree(stride):
+    passes, phases = lds.instruction_passes([4 * stride * lane for lane in range(32)], 4)
+    assert phases == 1 and passes == stride
+
+
+def test_broadcast_and_vector_phases():
+    assert lds.instruction_passes([0] * 32, 4) == (1, 1)
+    assert lds.instruction_passes([16 * lane for lane in range(32)], 16) == (4, 4)
+    assert lds.instruction_passes([8 * lane for lane in range(32)], 8) == (2, 2)
+    # 8 lanes of a 128-bit phase reading the same 16-byte column of 8 rows of 128 bytes: 8 passes
+    assert lds.instruction_passes([128 * lane for lane in range(8)], 16) == (8, 1)
+
+
+def test_page_closed_form_naive_transpose():
+    want = {k: int(v) for k, v in (ln.split() for ln in golden_lines("p2_bank_conflict_counts.txt"))}
+    passes, extra = lds.transpose_store_passes(1024, 2048, 32, "naive")
+    assert passes == want["store_wavefronts_naive"]
+    assert extra == want["store_conflicts_naive"]
+    assert lds.transpose_store_passes(1024, 2048, 32, "padded")[1] == want["store_conflicts_padded"]
+    assert lds.transpose_store_passes(1024, 2048, 32, "xor")[1] == want["store_conflicts_xor"]
