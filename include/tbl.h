@@ -1,0 +1,185 @@
+/*
+ * tbl.h -- C ABI of the MI355X (gfx950) swizzled-GEMM / LDS-transpose library (libtbl.so).
+ *
+ * Operations and where they are defined:
+ *   - tbl_gemm / tbl_gemm_tiled: the tiled dense GEMM C = A * B whose program-id -> output-tile
+ *     mapping is swizzled ("CUDA Thread Block Swizzle", leimao.github.io: sections "Linear Swizzle",
+ *     "Grouped 2D Panel Swizzle", "Morton / Z-order Swizzle", "Bitwise XOR Swizzle", and the GEMM
+ *     kernel with its persistent tile loop in section "CUDA Thread Block Swizzle Benchmark"), plus the
+ *     group-major and serpentine orders of the tvm_tirx ClusterPersistentScheduler2D page
+ *     (tvm.apache.org: "Tile Ordering", "Serpentine Mode", "Example 1").
+ *   - tbl_tile_map: the program-id -> (m, n) table of any order, computed by the same device code
+ *     the GEMM uses.
+ *   - tbl_transpose_i32: the int32 shared-memory transpose with naive, padded and XOR-swizzled LDS
+ *     layouts ("CUDA Swizzle & bank conflict", whc-imageprocess.github.io: section
+ *     "Case Study / Matrix Transpose").
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are dense and row-major with no padding: A is M x K, B is K x N, C is M x N.
+ *   - Every pointer is device memory owned by the caller. The library never allocates or frees
+ *     device memory in these calls and keeps no pointer after a call returns. Outputs must not alias
+ *     inputs. GEMM and transpose base pointers must be 16-byte aligned.
+ *   - ``stream`` is a hipStream_t (NULL = the null stream). Calls enqueue work and return; only
+ *     launch-time errors are reported, device-side faults surface at the caller's next
+ *     synchronisation.
+ *   - Every argument is validated before any HIP call, so invalid arguments return an error with
+ *     nothing enqueued, also on a machine without a GPU.
+ *   - Return value: TBL_OK (0) on success, a negative TBL_ERR_* on error, a positive TBL_WARN_* on
+ *     success with a warning. tbl_status_string() gives text for any code.
+ *   - Thread safety: the only global state is a per-device cache of device properties filled on
+ *     first use; calls from several host threads are safe. Calls that write the same output race.
+ */
+#ifndef TBL_H_
+#define TBL_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------------- */
+enum {
+  TBL_OK = 0,
+  TBL_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, unknown mode/layout, bad group */
+  TBL_ERR_DTYPE = -2,         /* unknown dtype code */
+  TBL_ERR_SHAPE = -3,         /* sizes not multiples of the tile, too large, or unsupported tile */
+  TBL_ERR_NOT_BIJECTIVE = -4, /* GEMM with Morton/XOR on a grid that is not a square power of two */
+  TBL_ERR_HIP = -5,           /* a HIP runtime call failed (no device, launch failure, ...) */
+  TBL_ERR_ALIGN = -6,         /* a GEMM or transpose pointer is not 16-byte aligned */
+  TBL_WARN_NOT_BIJECTIVE = 1  /* tbl_tile_map wrote the table, but it is not a bijection */
+};
+
+/* ---- element types of a GEMM: A and B share the input type; C is the output type -------------- */
+enum {
+  TBL_F16 = 0,          /* A, B, C fp16 (IEEE binary16); fp32 accumulation; C rounded to nearest even */
+  TBL_BF16 = 1,         /* A, B, C bfloat16; fp32 accumulation; C rounded to nearest even */
+  TBL_F16_F32OUT = 2,   /* A, B fp16; C fp32 (the accumulator itself) */
+  TBL_BF16_F32OUT = 3   /* A, B bf16; C fp32 */
+};
+
+/* ---- tile orders (swizzle modes) --------------------------------------------------------------
+ * A tile id t in [0, T), T = grid_m * grid_n, is mapped to output tile (m, n):
+ *   TBL_ROW        m = t / grid_n, n = t % grid_n                                 (linear, row-major)
+ *   TBL_COL        m = t % grid_m, n = t / grid_m                                 (linear, column-major)
+ *   TBL_PANEL      groups of ``group`` tile rows taken in row order; inside a group ids run down a
+ *                  column of the group, then along the columns; the last group keeps the rows that
+ *                  remain, and the row inside it is t modulo its height (grouped 2D panel; also the
+ *                  group-major order of the tvm page)
+ *   TBL_MORTON     bit 2i of t -> bit i of m, bit 2i+1 -> bit i of n (16 bit pairs), then modulo
+ *                  the grid (Z-order; a bijection only on square power-of-two grids)
+ *   TBL_XOR        x = t % grid_n, y = t / grid_n; m = (x ^ y) % grid_m, n = y % grid_n
+ *                  (a bijection only on square power-of-two grids)
+ *   TBL_SERPENTINE column strips ``group`` tiles wide, left to right; even strips walked top to
+ *                  bottom, odd strips bottom to top, columns ascending along each strip row; the last
+ *                  strip keeps the columns that remain (the reading of the tvm page's serpentine mode
+ *                  that reproduces its 4x4 table)
+ * TBL_XCD_REMAP may be OR-ed into any mode: before the order is applied, t is replaced by
+ *   t' = (t % 8) * (T8 / 8) + t / 8 for t < T8 = 8 * floor(T / 8) (t' = t otherwise), so that the
+ *   workgroups that round-robin dispatch places on one of the 8 XCDs (each with a private L2) walk one
+ *   contiguous eighth of the order.
+ */
+enum {
+  TBL_ROW = 0,
+  TBL_COL = 1,
+  TBL_PANEL = 2,
+  TBL_MORTON = 3,
+  TBL_XOR = 4,
+  TBL_SERPENTINE = 5,
+  TBL_XCD_REMAP = 0x100
+};
+
+/* ---- LDS layouts of the transpose ---------------------------------------------------------- */
+enum {
+  TBL_T_NAIVE = 0,   /* 64 x 64 int32 tile, element (r, c) at r*64 + c */
+  TBL_T_PADDED = 1,  /* 64 x 65 array, element (r, c) at r*65 + c */
+  TBL_T_XOR = 2      /* element (r, c) at r*64 + (c XOR r) */
+};
+
+/*
+ * tbl_gemm -- C = A * B with a swizzled, optionally persistent tile schedule.
+ *   A, B, C       device pointers (row-major M x K, K x N, M x N), 16-byte aligned, C not aliasing.
+ *   M, N, K       sizes, > 0. The tile shape is fixed by a rule (tbl_gemm_tile_shape): 64x64x64 when
+ *                 max(M, N) <= 1024, else 256x256x64; M, N, K must be multiples of it
+ *                 (TBL_ERR_SHAPE otherwise). Each size must be <= 2^20.
+ *   dtype         TBL_F16, TBL_BF16, TBL_F16_F32OUT or TBL_BF16_F32OUT.
+ *   swizzle_mode  a TBL_* order, optionally | TBL_XCD_REMAP. Morton and XOR need a square
+ *                 power-of-two tile grid (TBL_ERR_NOT_BIJECTIVE otherwise).
+ *   group_size    group (TBL_PANEL) or strip width (TBL_SERPENTINE), >= 1; ignored by other modes.
+ *   persistent    0: one workgroup per tile (num_programs defaults to T). 1: num_programs defaults
+ *                 to min(T, CUs x resident workgroups per CU).
+ *   num_programs  0 = the default above; > 0 = exactly this many workgroups. Workgroup p computes
+ *                 tiles p, p + num_programs, p + 2 num_programs, ... < T (page 1's static stride
+ *                 schedule); < 0 is TBL_ERR_INVALID_ARG.
+ *   stream        hipStream_t or NULL.
+ * Every output element is computed by exactly one workgroup with fp32 accumulation over k in
+ * ascending 64-wide steps, so for one tile shape the result does not depend on the order,
+ * the remap flag, persistence or num_programs.
+ */
+int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+             int swizzle_mode, int group_size, int persistent, int num_programs, void* stream);
+
+/*
+ * tbl_gemm_tiled -- tbl_gemm with an explicit tile shape and an optional schedule trace.
+ *   block_m, block_n, block_k  one of the compiled shapes: 64x64x64, 128x128x64, 256x256x64
+ *                 (TBL_ERR_SHAPE otherwise).
+ *   trace         NULL, or device int32[5 * T]: for every tile id t the workgroup that ran it writes
+ *                 {program id, iteration of its tile loop, m, n, XCC id}. Caller-owned.
+ *   All other arguments as tbl_gemm.
+ */
+int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                   int swizzle_mode, int group_size, int persistent, int num_programs, int block_m,
+                   int block_n, int block_k, int32_t* trace, void* stream);
+
+/*
+ * tbl_tile_map -- write the forward table of an order: tile_m[t], tile_n[t] for t in [0, T).
+ *   swizzle_mode  as tbl_gemm (TBL_XCD_REMAP allowed).
+ *   grid_m, grid_n  the tile grid, each in [1, 2^20], with grid_m * grid_n < 2^31.
+ *   group_size    as tbl_gemm (>= 1 for TBL_PANEL / TBL_SERPENTINE).
+ *   tile_m, tile_n  device int32[T], caller-owned.
+ * Returns TBL_WARN_NOT_BIJECTIVE (after enqueueing) for Morton/XOR on a grid that is not a square
+ * power of two: the table is still written, exactly as the formulas give it.
+ */
+int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32_t* tile_m,
+                 int32_t* tile_n, void* stream);
+
+/*
+ * tbl_transpose_i32 -- out (cols x rows) = transpose of in (rows x cols), int32, bit-exact,
+ * staged through a 64 x 64 LDS tile in the given layout.
+ *   in, out       device pointers, 16-byte aligned, not aliasing.
+ *   rows, cols    > 0, multiples of 64, each <= 2^20 (TBL_ERR_SHAPE otherwise).
+ *   layout        TBL_T_NAIVE, TBL_T_PADDED or TBL_T_XOR.
+ */
+int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t cols, int layout,
+                      void* stream);
+
+/* tbl_gemm_tile_shape -- the tile shape tbl_gemm uses for these sizes (host only, no HIP call). */
+int tbl_gemm_tile_shape(int64_t M, int64_t N, int64_t K, int* block_m, int* block_n, int* block_k);
+
+/*
+ * tbl_default_num_programs -- the num_programs tbl_gemm launches for num_programs = 0:
+ * T when persistent = 0, else min(T, CUs x resident workgroups per CU of the chosen kernel, from
+ * the HIP occupancy query). Writes *num_programs. Needs a device unless persistent = 0.
+ */
+int tbl_default_num_programs(int64_t M, int64_t N, int64_t K, int dtype, int persistent,
+                             int* num_programs);
+
+/*
+ * tbl_device_info -- properties of the current device: compute units, XCDs (assumed 8 on gfx950),
+ * LDS bytes per workgroup, L2 bytes (as reported by HIP), and the architecture name (written into
+ * ``arch`` with at most arch_len bytes including the terminator; ``arch`` may be NULL).
+ */
+int tbl_device_info(int* num_cus, int* num_xcds, int* lds_bytes, int* l2_bytes, char* arch,
+                    int arch_len);
+
+/* tbl_status_string -- static text for a status code (never NULL). */
+const char* tbl_status_string(int status);
+
+/* tbl_version -- ABI version of this header (major * 100 + minor). */
+int tbl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TBL_H_ */

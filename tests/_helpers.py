@@ -1,0 +1,42 @@
+"""Helpers for the GPU parity tests: host <-> device copies and the acceptance tolerances.
+
+Tolerances (stated once, used by every GEMM parity test):
+  * fp16 / bf16 output: |gpu - ref| <= 1e-2 + 1e-2 * |ref| for every element;
+  * fp32 output:        |gpu - ref| <= 1e-4 * sqrt(K) * max |ref|.
+ref is the fp64 oracle value.
+"""
+
+import numpy as np
+import torch
+
+
+def dev16(bits, dtype):
+    """uint16 bit patterns (numpy) -> fp16/bf16 CUDA tensor holding the same bytes."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16).cuda()
+
+
+def host64(t):
+    """CUDA tensor -> float64 numpy array (exact for fp16 / bf16 / fp32)."""
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bits16(t):
+    """fp16/bf16 CUDA tensor -> its uint16 bit patterns (numpy)."""
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_tol(gpu, ref, K, f32_out=False, what=""):
+    err = np.abs(gpu - ref)
+    if f32_out:
+        bound = 1e-4 * np.sqrt(K) * np.max(np.abs(ref))
+        ok = err <= bound
+    else:
+        bound = 1e-2 + 1e-2 * np.abs(ref)
+        ok = err <= bound
+    if not np.all(ok):
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} elements out of tolerance; first at {i}: "
+                             f"gpu {gpu[i]!r} ref {ref[i]!r}")
+    return float(np.max(err))

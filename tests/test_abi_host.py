@@ -1,0 +1,112 @@
+"""The C-ABI library on the host: it loads, exports every entry point include/tbl.h declares, and
+rejects invalid arguments before any HIP call (so these run without a GPU). CPU only.
+
+Every call here fails validation; none reaches a kernel launch, so the fake device addresses used
+are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import thread_block_lds_amd as tbl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tbl.h")
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+NULL = ctypes.c_void_p(0)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tbl_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = tbl.lib()
+    declared = _declared()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(tbl.exported_names()) == declared
+    assert tbl.version() == 100
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5, -6, 1, 12345):
+        assert isinstance(tbl.status_string(st), str) and tbl.status_string(st)
+
+
+def _gemm(A=FAKE, B=FAKE, C=FAKE, M=512, N=512, K=512, dtype=0, mode=0, group=1, persistent=0, P=0):
+    return tbl.lib().tbl_gemm(A, B, C, M, N, K, dtype, mode, group, persistent, P, NULL)
+
+
+def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=64, A=FAKE, dtype=0):
+    return tbl.lib().tbl_gemm_tiled(A, FAKE, FAKE, M, N, K, dtype, mode, group, 0, 0, bm, bn, bk, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(A=NULL), tbl.ERR_INVALID_ARG), (dict(B=NULL), tbl.ERR_INVALID_ARG), (dict(C=NULL), tbl.ERR_INVALID_ARG),
+    (dict(M=0), tbl.ERR_INVALID_ARG), (dict(N=-64), tbl.ERR_INVALID_ARG), (dict(K=0), tbl.ERR_INVALID_ARG),
+    (dict(dtype=4), tbl.ERR_DTYPE), (dict(dtype=-1), tbl.ERR_DTYPE),
+    (dict(mode=6), tbl.ERR_INVALID_ARG), (dict(mode=0x200), tbl.ERR_INVALID_ARG), (dict(mode=-1), tbl.ERR_INVALID_ARG),
+    (dict(mode=tbl.PANEL, group=0), tbl.ERR_INVALID_ARG), (dict(mode=tbl.SERPENTINE, group=-2), tbl.ERR_INVALID_ARG),
+    (dict(persistent=2), tbl.ERR_INVALID_ARG), (dict(P=-1), tbl.ERR_INVALID_ARG),
+    (dict(M=520), tbl.ERR_SHAPE), (dict(N=500), tbl.ERR_SHAPE), (dict(K=100), tbl.ERR_SHAPE),
+    (dict(M=2048 + 64), tbl.ERR_SHAPE),             # 256-tile rule: not a multiple of 256
+    (dict(M=(1 << 20) + 256, N=2048), tbl.ERR_SHAPE),
+    (dict(M=10240, N=6144, K=2048, mode=tbl.MORTON), tbl.ERR_NOT_BIJECTIVE),
+    (dict(M=10240, N=6144, K=2048, mode=tbl.XOR | tbl.XCD_REMAP), tbl.ERR_NOT_BIJECTIVE),
+    (dict(M=1024, N=512, mode=tbl.XOR), tbl.ERR_NOT_BIJECTIVE),
+    (dict(M=768, N=768, mode=tbl.MORTON), tbl.ERR_NOT_BIJECTIVE),   # 12 x 12 grid
+    (dict(A=MISALIGNED), tbl.ERR_ALIGN), (dict(C=MISALIGNED), tbl.ERR_ALIGN),
+])
+def test_gemm_validation(kw, want):
+    assert _gemm(**kw) == want
+
+
+def test_gemm_tiled_validation():
+    assert _tiled(bm=32, bn=32) == tbl.ERR_SHAPE
+    assert _tiled(bm=64, bn=128) == tbl.ERR_SHAPE
+    assert _tiled(bk=32) == tbl.ERR_SHAPE
+    assert _tiled(M=512 + 128, bm=256, bn=256) == tbl.ERR_SHAPE
+    assert _tiled(mode=tbl.MORTON, M=1024, N=512, bm=128, bn=128) == tbl.ERR_NOT_BIJECTIVE
+    assert _tiled(A=MISALIGNED) == tbl.ERR_ALIGN
+    assert _tiled(dtype=9) == tbl.ERR_DTYPE
+
+
+def test_tile_map_validation():
+    f = tbl.lib().tbl_tile_map
+    assert f(0, 8, 8, 1, NULL, FAKE, NULL) == tbl.ERR_INVALID_ARG
+    assert f(7, 8, 8, 1, FAKE, FAKE, NULL) == tbl.ERR_INVALID_ARG
+    assert f(tbl.PANEL, 8, 8, 0, FAKE, FAKE, NULL) == tbl.ERR_INVALID_ARG
+    assert f(0, 0, 8, 1, FAKE, FAKE, NULL) == tbl.ERR_SHAPE
+    assert f(0, 8, -1, 1, FAKE, FAKE, NULL) == tbl.ERR_SHAPE
+    assert f(0, 1 << 16, 1 << 16, 1, FAKE, FAKE, NULL) == tbl.ERR_SHAPE     # 2^32 tiles
+
+
+def test_transpose_validation():
+    f = tbl.lib().tbl_transpose_i32
+    assert f(NULL, FAKE, 64, 64, 0, NULL) == tbl.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 0, 64, 0, NULL) == tbl.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 64, 64, 3, NULL) == tbl.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 100, 64, 0, NULL) == tbl.ERR_SHAPE
+    assert f(FAKE, FAKE, 64, 96, 2, NULL) == tbl.ERR_SHAPE
+    assert f(FAKE, MISALIGNED, 64, 64, 1, NULL) == tbl.ERR_ALIGN
+
+
+def test_tile_shape_rule_and_default_programs():
+    assert tbl.gemm_tile_shape(512, 512, 512) == (64, 64, 64)
+    assert tbl.gemm_tile_shape(1024, 1024, 8192) == (64, 64, 64)
+    assert tbl.gemm_tile_shape(4096, 4096, 4096) == (256, 256, 64)
+    assert tbl.gemm_tile_shape(10240, 6144, 2048) == (256, 256, 64)
+    # non-persistent default needs no device: one workgroup per tile
+    assert tbl.default_num_programs(512, 512, 512, persistent=False) == 64
+    assert tbl.default_num_programs(8192, 8192, 8192, persistent=False) == 1024
+    assert tbl.default_num_programs(10240, 6144, 2048, persistent=False) == 960
+    with pytest.raises(tbl.TblError):
+        tbl.default_num_programs(520, 512, 512)

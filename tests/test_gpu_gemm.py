@@ -1,0 +1,189 @@
+"""GPU parity of tbl_gemm / tbl_gemm_tiled against the fp64 oracle.
+
+Bars (see tests/_helpers.py): fp16/bf16 output |gpu - ref| <= 1e-2 + 1e-2 |ref|; fp32 output
+|gpu - ref| <= 1e-4 sqrt(K) max|ref|. Integer-valued inputs make the fp32 accumulation exact, so
+those tests compare bits: fp32 output equals the exact product, and fp16 / bf16 output equals the
+exact product rounded to nearest even. For one tile shape every output element is accumulated by
+the same code in the same k order whatever the tile order, so outputs must be bit-identical
+across orders, the XCD remap, persistence and program counts.
+
+Workloads (inputs from thread_block_lds_amd.synth, A seed s, B seed s+1):
+  512^3 fp16 uniform[-1,1], 64x64 tiles (8x8 grid), every order, full oracle;
+  4096^3 fp16 uniform[-1,1], 256x256 tiles (16x16 grid), row / panel 4,8,16 / Morton / XOR;
+  8192^3 bf16 N(0,1)/sqrt(K), persistent group-major 8 and serpentine 8;
+  10240 x 6144 x 2048 fp16, 40x24 grid, panel 8/16 and serpentine 8/16, both launch styles.
+Large workloads are checked on sampled rows that touch every tile row (every tile column is in
+every row), plus bit-identity of the whole output across orders.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import thread_block_lds_amd as tbl
+from _helpers import bits16, check_tol, dev16, host64
+from oracle import gemm as og
+from oracle import tile_maps as tm
+from thread_block_lds_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(M, BM):
+    """Two rows in every tile row, at offsets that vary from tile row to tile row."""
+    rows = []
+    for r in range(M // BM):
+        rows.append(r * BM + (r * 37) % BM)
+        rows.append(r * BM + (BM - 1 - (r * 11) % BM))
+    return np.array(sorted(set(rows)))
+
+
+def test_c1_every_order_full_oracle():
+    M = N = K = 512
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
+    ref = og.gemm(a, b, "f16")
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    outs = []
+    for mode, g in [(tm.ROW, 1), (tm.COL, 1), (tm.PANEL, 4), (tm.MORTON, 1), (tm.XOR, 1),
+                    (tm.SERPENTINE, 2), (tm.PANEL | tm.XCD_REMAP, 4), (tm.SERPENTINE | tm.XCD_REMAP, 2)]:
+        c = tbl.gemm(ad, bd, mode=mode, group=g)
+        torch.cuda.synchronize()
+        check_tol(host64(c), ref, K, what=f"512^3 mode {mode} g{g}")
+        outs.append(c)
+    for c in outs[1:]:
+        assert torch.equal(c, outs[0])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("tile", [64, 128, 256])
+def test_integer_inputs_exact_fp32_out(dtype, tile):
+    M, N, K = 512, 768, 1024
+    a = synth.int_valued((M, K), 21, -2, 2, dtype)
+    b = synth.int_valued((K, N), 22, -2, 2, dtype)
+    ref = og.gemm(a, b, dtype)
+    c = tbl.gemm(dev16(a, dtype), dev16(b, dtype), out_dtype=torch.float32, tile=(tile, tile, 64),
+                 mode=tm.PANEL, group=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(c), ref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_output_rounding_is_nearest_even(dtype):
+    # |C| up to 8*8*512 = 32768: exact in fp32, so the only rounding is the final cast
+    M, N, K = 256, 256, 512
+    a = synth.int_valued((M, K), 31, -8, 8, dtype)
+    b = synth.int_valued((K, N), 32, -8, 8, dtype)
+    exact = og.gemm(a, b, dtype)
+    if dtype == "f16":
+        want = exact.astype(np.float16).view(np.uint16)
+    else:
+        want = synth.f32_to_bf16_bits(exact.astype(np.float32))
+    for tile in (64, 256):
+        c = tbl.gemm(dev16(a, dtype), dev16(b, dtype), tile=(tile, tile, 64))
+        torch.cuda.synchronize()
+        assert np.array_equal(bits16(c), want), tile
+
+
+@pytest.mark.parametrize("tile", [64, 128, 256])
+def test_schedule_variants_bit_identical(tile):
+    M = N = 1024
+    K = 512
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=5)
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    T = (M // tile) * (N // tile)
+    base = tbl.gemm(ad, bd, tile=(tile, tile, 64))
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, tile)
+    check_tol(host64(base)[rows], og.gemm_rows(a, b, "f16", rows), K, what=f"tile {tile}")
+    for mode, g in [(tm.COL, 1), (tm.PANEL, 3), (tm.MORTON, 1), (tm.XOR, 1), (tm.SERPENTINE, 3)]:
+        for remap in (0, tm.XCD_REMAP):
+            for persistent, P in [(0, 0), (1, 0), (0, 1), (0, 7), (1, 13), (0, T + 5)]:
+                c = tbl.gemm(ad, bd, tile=(tile, tile, 64), mode=mode | remap, group=g,
+                             persistent=persistent, num_programs=P)
+                torch.cuda.synchronize()
+                assert torch.equal(c, base), (mode, remap, persistent, P)
+
+
+def test_c2_4096_fp16_orders():
+    M = N = K = 4096
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    rows = _sample_rows(M, 256)
+    ref = og.gemm_rows(a, b, "f16", rows)
+    base = None
+    for mode, g in [(tm.ROW, 1), (tm.PANEL, 4), (tm.PANEL, 8), (tm.PANEL, 16), (tm.MORTON, 1), (tm.XOR, 1)]:
+        for remap in (0, tm.XCD_REMAP):
+            c = tbl.gemm(ad, bd, mode=mode | remap, group=g)
+            torch.cuda.synchronize()
+            if base is None:
+                base = c
+                check_tol(host64(c)[rows], ref, K, what="4096^3 row")
+            else:
+                assert torch.equal(c, base), (mode, g, remap)
+    c32 = tbl.gemm(ad, bd, out_dtype=torch.float32, mode=tm.PANEL, group=8)
+    torch.cuda.synchronize()
+    check_tol(host64(c32)[rows], ref, K, f32_out=True, what="4096^3 fp32 out")
+
+
+def test_c3_8192_bf16_persistent():
+    M = N = K = 8192
+    a, b = synth.gemm_operands(M, N, K, "bf16", "normal", seed=0)
+    ad, bd = dev16(a, "bf16"), dev16(b, "bf16")
+    rows = _sample_rows(M, 256)
+    ref = og.gemm_rows(a, b, "bf16", rows)
+    base = None
+    for mode in (tm.PANEL, tm.SERPENTINE, tm.PANEL | tm.XCD_REMAP, tm.SERPENTINE | tm.XCD_REMAP):
+        c = tbl.gemm(ad, bd, mode=mode, group=8, persistent=True)
+        torch.cuda.synchronize()
+        if base is None:
+            base = c
+            check_tol(host64(c)[rows], ref, K, what="8192^3 bf16")
+        else:
+            assert torch.equal(c, base), mode
+
+
+def test_c4_rectangular_partial_groups():
+    M, N, K = 10240, 6144, 2048
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    rows = _sample_rows(M, 256)
+    ref = og.gemm_rows(a, b, "f16", rows)
+    base = None
+    for mode, g in [(tm.PANEL, 8), (tm.PANEL, 16), (tm.SERPENTINE, 8), (tm.SERPENTINE, 16)]:
+        for persistent in (False, True):
+            c = tbl.gemm(ad, bd, mode=mode, group=g, persistent=persistent)
+            torch.cuda.synchronize()
+            if base is None:
+                base = c
+                check_tol(host64(c)[rows], ref, K, what="10240x6144x2048")
+            else:
+                assert torch.equal(c, base), (mode, g, persistent)
+    with pytest.raises(tbl.TblError) as e:
+        tbl.gemm(ad, bd, mode=tm.MORTON)
+    assert e.value.status == tbl.ERR_NOT_BIJECTIVE
+
+
+@pytest.mark.parametrize("mode,g,persistent,P", [(tm.PANEL, 8, True, 0), (tm.SERPENTINE, 8, True, 0),
+                                                 (tm.PANEL | tm.XCD_REMAP, 8, True, 0),
+                                                 (tm.ROW, 1, False, 0), (tm.XOR, 1, False, 100)])
+def test_trace_matches_oracle_schedule(mode, g, persistent, P):
+    M = N = 8192
+    K = 64
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=3)
+    T = (M // 256) * (N // 256)
+    trace = torch.full((5 * T,), -1, dtype=torch.int32, device="cuda")
+    tbl.gemm(dev16(a, "f16"), dev16(b, "f16"), mode=mode, group=g, persistent=persistent,
+             num_programs=P, trace=trace)
+    torch.cuda.synchronize()
+    tr = trace.cpu().numpy().reshape(T, 5).astype(np.int64)
+    programs = P or (tbl.default_num_programs(M, N, K, persistent=persistent))
+    om, on = tm.tile_table(mode, M // 256, N // 256, g)
+    for t in range(T):
+        assert tr[t, 0] == t % programs and tr[t, 1] == t // programs, t
+    assert np.array_equal(tr[:, 2], om) and np.array_equal(tr[:, 3], on)
+    xcc = tr[:, 4]
+    assert np.all((xcc >= 0) & (xcc < 8))
+    for p in range(min(programs, T)):
+        assert len(set(xcc[p::programs])) == 1, p           # a workgroup never changes XCD
+    rr = np.mean(xcc[:min(programs, T)] == np.arange(min(programs, T)) % 8)
+    print(f"workgroups on XCD (program mod 8): {rr:.3f}")

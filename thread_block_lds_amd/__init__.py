@@ -1,0 +1,211 @@
+"""MI355X (gfx950) swizzled GEMM and LDS-swizzle transpose: Python binding of libtbl.so.
+
+A thin ctypes layer over the C ABI in include/tbl.h, with the same entry-point names (without the
+``tbl_`` prefix). It only marshals arguments: torch tensors provide device pointers and the current
+HIP stream; every step of the computation runs in the library's HIP kernels. There is no CPU
+fallback: if libtbl.so is missing or fails to load, every call raises.
+
+    import torch, thread_block_lds_amd as tbl
+    c = tbl.gemm(a, b, mode=tbl.PANEL, group=8)              # a: (M, K), b: (K, N), fp16 or bf16
+    m, n = tbl.tile_map(tbl.SERPENTINE, 32, 32, group=8)    # int32 device tensors of length 1024
+    out = tbl.transpose_i32(x, layout=tbl.T_XOR)
+"""
+
+import ctypes
+import os
+
+from . import synth  # noqa: F401  (seeded input generators; no compute)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtbl.so")
+
+OK, ERR_INVALID_ARG, ERR_DTYPE, ERR_SHAPE, ERR_NOT_BIJECTIVE, ERR_HIP, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
+WARN_NOT_BIJECTIVE = 1
+F16, BF16, F16_F32OUT, BF16_F32OUT = 0, 1, 2, 3
+ROW, COL, PANEL, MORTON, XOR, SERPENTINE = 0, 1, 2, 3, 4, 5
+XCD_REMAP = 0x100
+T_NAIVE, T_PADDED, T_XOR = 0, 1, 2
+
+_EXPORTS = {
+    # name: (restype, argtypes)
+    "tbl_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "tbl_gemm_tiled": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
+    "tbl_tile_map": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tbl_transpose_i32": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]),
+    "tbl_gemm_tile_shape": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                           ctypes.POINTER(ctypes.c_int)]),
+    "tbl_default_num_programs": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int, ctypes.c_int,
+                                                ctypes.POINTER(ctypes.c_int)]),
+    "tbl_device_info": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                       ctypes.c_char_p, ctypes.c_int]),
+    "tbl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tbl_version": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+class TblError(RuntimeError):
+    """A libtbl entry point returned an error status."""
+
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """The loaded libtbl.so (loaded on first use; raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m thread_block_lds_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def exported_names():
+    return list(_EXPORTS)
+
+
+def status_string(status):
+    return lib().tbl_status_string(int(status)).decode()
+
+
+def _check(status, where, allow_warning=False):
+    if status < 0 or (status > 0 and not allow_warning):
+        raise TblError(status, where)
+    return status
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _gemm_dtype(a, out_dtype):
+    import torch
+    if a.dtype == torch.float16:
+        return F16_F32OUT if out_dtype == torch.float32 else F16
+    if a.dtype == torch.bfloat16:
+        return BF16_F32OUT if out_dtype == torch.float32 else BF16
+    raise TypeError(f"unsupported input dtype {a.dtype}")
+
+
+def gemm(a, b, c=None, mode=ROW, group=1, persistent=False, num_programs=0, out_dtype=None,
+         tile=None, trace=None, stream=None):
+    """C = A @ B on the GPU through tbl_gemm (or tbl_gemm_tiled when ``tile`` or ``trace`` is given).
+
+    a: (M, K), b: (K, N) contiguous fp16/bf16 CUDA tensors. c: optional (M, N) output of
+    ``out_dtype`` (default: the input dtype; torch.float32 selects fp32 output). ``mode`` may include
+    XCD_REMAP. ``tile`` = (block_m, block_n, block_k); ``trace`` = int32 CUDA tensor of 5*T entries.
+    Returns c.
+    """
+    import torch
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shape mismatch {tuple(a.shape)} x {tuple(b.shape)}")
+    if a.dtype != b.dtype:
+        raise TypeError("A and B must share a dtype")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("A and B must be contiguous row-major")
+    M, K = a.shape
+    N = b.shape[1]
+    out_dtype = out_dtype or (c.dtype if c is not None else a.dtype)
+    dt = _gemm_dtype(a, out_dtype)
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if c.shape != (M, N) or not c.is_contiguous() or c.dtype != out_dtype:
+        raise ValueError("C must be a contiguous (M, N) tensor of the output dtype")
+    s = _stream(stream)
+    if tile is None and trace is None:
+        st = lib().tbl_gemm(_ptr(a), _ptr(b), _ptr(c), M, N, K, dt, int(mode), int(group),
+                            int(bool(persistent)), int(num_programs), s)
+        _check(st, "tbl_gemm")
+    else:
+        if tile is None:
+            bm, bn, bk = gemm_tile_shape(M, N, K)
+        else:
+            bm, bn, bk = tile
+        st = lib().tbl_gemm_tiled(_ptr(a), _ptr(b), _ptr(c), M, N, K, dt, int(mode), int(group),
+                                  int(bool(persistent)), int(num_programs), int(bm), int(bn), int(bk),
+                                  _ptr(trace), s)
+        _check(st, "tbl_gemm_tiled")
+    return c
+
+
+def tile_map(mode, grid_m, grid_n, group=1, out_m=None, out_n=None, device="cuda", stream=None):
+    """(tile_m, tile_n) int32 CUDA tensors of length grid_m*grid_n through tbl_tile_map.
+
+    Returns (tile_m, tile_n, status); status is WARN_NOT_BIJECTIVE for Morton/XOR off square
+    power-of-two grids (the table is still written)."""
+    import torch
+    T = grid_m * grid_n
+    if out_m is None:
+        out_m = torch.empty(T, dtype=torch.int32, device=device)
+    if out_n is None:
+        out_n = torch.empty(T, dtype=torch.int32, device=device)
+    st = lib().tbl_tile_map(int(mode), int(grid_m), int(grid_n), int(group), _ptr(out_m), _ptr(out_n),
+                            _stream(stream))
+    _check(st, "tbl_tile_map", allow_warning=True)
+    return out_m, out_n, st
+
+
+def transpose_i32(x, out=None, layout=T_XOR, stream=None):
+    """out (cols x rows) = x.T for a contiguous int32 CUDA tensor, through tbl_transpose_i32."""
+    import torch
+    if x.dim() != 2 or x.dtype != torch.int32 or not x.is_contiguous():
+        raise ValueError("expected a contiguous 2-D int32 tensor")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=torch.int32, device=x.device)
+    st = lib().tbl_transpose_i32(_ptr(x), _ptr(out), rows, cols, int(layout), _stream(stream))
+    _check(st, "tbl_transpose_i32")
+    return out
+
+
+def gemm_tile_shape(M, N, K):
+    bm, bn, bk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().tbl_gemm_tile_shape(M, N, K, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(bk)),
+           "tbl_gemm_tile_shape")
+    return bm.value, bn.value, bk.value
+
+
+def default_num_programs(M, N, K, dtype=F16, persistent=False):
+    out = ctypes.c_int()
+    _check(lib().tbl_default_num_programs(M, N, K, int(dtype), int(bool(persistent)), ctypes.byref(out)),
+           "tbl_default_num_programs")
+    return out.value
+
+
+def device_info():
+    cus, xcds, lds, l2 = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    arch = ctypes.create_string_buffer(64)
+    _check(lib().tbl_device_info(ctypes.byref(cus), ctypes.byref(xcds), ctypes.byref(lds),
+                                 ctypes.byref(l2), arch, 64), "tbl_device_info")
+    return {"num_cus": cus.value, "num_xcds": xcds.value, "lds_bytes": lds.value,
+            "l2_bytes": l2.value, "arch": arch.value.decode()}
+
+
+def version():
+    return lib().tbl_version()

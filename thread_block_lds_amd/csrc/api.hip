@@ -1,0 +1,244 @@
+// C ABI of libtbl.so (declared and documented in include/tbl.h): argument validation, the tile
+// shape rule, default program counts, device properties, and dispatch to the kernels.
+//
+// Every argument is checked before the first HIP call, so the error paths run without a GPU.
+// The checks mirror the benchmark script of "CUDA Thread Block Swizzle" (leimao.github.io):
+// positive sizes and group sizes, and Morton / XOR used only on square power-of-two tile grids
+// (elsewhere those orders drop some tiles and repeat others).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/tbl.h"
+#include "internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t{1} << 20;
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  bool valid = false;
+  int cus = 0;
+  int lds = 0;
+  int l2 = 0;
+  char arch[64] = {0};
+};
+
+std::mutex g_info_mutex;
+DeviceInfo g_info[kMaxDevices];
+
+int device_info(DeviceInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TBL_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_info_mutex);
+  DeviceInfo& d = g_info[dev];
+  if (!d.valid) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return TBL_ERR_HIP;
+    d.cus = p.multiProcessorCount;
+    d.lds = static_cast<int>(p.sharedMemPerBlock);
+    d.l2 = p.l2CacheSize;
+    strncpy(d.arch, p.gcnArchName, sizeof(d.arch) - 1);
+    d.valid = true;
+  }
+  *out = d;
+  return TBL_OK;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_order(int swizzle_mode, int64_t gm, int64_t gn, int group) {
+  const int mode = swizzle_mode & 0xFF;
+  if ((swizzle_mode & ~(0xFF | TBL_XCD_REMAP)) != 0) return TBL_ERR_INVALID_ARG;
+  if (mode < TBL_ROW || mode > TBL_SERPENTINE) return TBL_ERR_INVALID_ARG;
+  if ((mode == TBL_PANEL || mode == TBL_SERPENTINE) && group < 1) return TBL_ERR_INVALID_ARG;
+  if (gm < 1 || gn < 1 || gm > kMaxDim || gn > kMaxDim || gm * gn > INT32_MAX) return TBL_ERR_SHAPE;
+  return TBL_OK;
+}
+
+bool bijective_grid(int swizzle_mode, int64_t gm, int64_t gn) {
+  const int mode = swizzle_mode & 0xFF;
+  if (mode != TBL_MORTON && mode != TBL_XOR) return true;
+  return gm == gn && is_pow2(gm);
+}
+
+tbl::TileOrder make_order(int swizzle_mode, int gm, int gn, int group) {
+  tbl::TileOrder o;
+  o.mode = swizzle_mode & 0xFF;
+  o.remap = (swizzle_mode & TBL_XCD_REMAP) ? 1 : 0;
+  o.grid_m = gm;
+  o.grid_n = gn;
+  // A panel group taller than the grid, or a serpentine strip wider than it, orders the tiles
+  // exactly as one of the grid's own height / width does; clamping keeps the device arithmetic in
+  // 32 bits.
+  if (o.mode == TBL_PANEL) o.group = group < gm ? group : gm;
+  else if (o.mode == TBL_SERPENTINE) o.group = group < gn ? group : gn;
+  else o.group = 1;
+  o.tiles = gm * gn;
+  return o;
+}
+
+void tile_rule(int64_t M, int64_t N, int* bm, int* bn, int* bk) {
+  const int t = (M > 1024 || N > 1024) ? 256 : 64;
+  *bm = t;
+  *bn = t;
+  *bk = 64;
+}
+
+int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                  int swizzle_mode, int group, int persistent, int num_programs, int bm, int bn,
+                  int bk) {
+  if (A == nullptr || B == nullptr || C == nullptr) return TBL_ERR_INVALID_ARG;
+  if (M <= 0 || N <= 0 || K <= 0) return TBL_ERR_INVALID_ARG;
+  if (dtype < TBL_F16 || dtype > TBL_BF16_F32OUT) return TBL_ERR_DTYPE;
+  if (persistent != 0 && persistent != 1) return TBL_ERR_INVALID_ARG;
+  if (num_programs < 0) return TBL_ERR_INVALID_ARG;
+  if (!tbl::gemm_tile_supported(bm, bn, bk)) return TBL_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
+  if (M % bm || N % bn || K % bk) return TBL_ERR_SHAPE;
+  int rc = check_order(swizzle_mode, M / bm, N / bn, group);
+  if (rc != TBL_OK) return rc;
+  if (!bijective_grid(swizzle_mode, M / bm, N / bn)) return TBL_ERR_NOT_BIJECTIVE;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return TBL_ERR_ALIGN;
+  return TBL_OK;
+}
+
+int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persistent,
+                     int num_programs, int* out) {
+  if (num_programs > 0) {
+    *out = num_programs;
+    return TBL_OK;
+  }
+  if (!persistent) {
+    *out = static_cast<int>(tiles);
+    return TBL_OK;
+  }
+  DeviceInfo d;
+  int rc = device_info(&d);
+  if (rc != TBL_OK) return rc;
+  int per_cu = 0;
+  if (tbl::gemm_blocks_per_cu(dtype, bm, bn, bk, &per_cu) != hipSuccess) return TBL_ERR_HIP;
+  if (per_cu < 1) per_cu = 1;
+  const int64_t cap = static_cast<int64_t>(d.cus) * per_cu;
+  *out = static_cast<int>(tiles < cap ? tiles : cap);
+  return TBL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tbl_version(void) { return 100; }
+
+const char* tbl_status_string(int status) {
+  switch (status) {
+    case TBL_OK: return "ok";
+    case TBL_ERR_INVALID_ARG: return "invalid argument";
+    case TBL_ERR_DTYPE: return "unknown dtype";
+    case TBL_ERR_SHAPE: return "unsupported shape (not a tile multiple, too large, or unsupported tile)";
+    case TBL_ERR_NOT_BIJECTIVE: return "order is not a bijection on this tile grid (Morton/XOR need a square power-of-two grid)";
+    case TBL_ERR_HIP: return "HIP runtime error";
+    case TBL_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case TBL_WARN_NOT_BIJECTIVE: return "warning: table written, but the order is not a bijection on this grid";
+    default: return "unknown status";
+  }
+}
+
+int tbl_gemm_tile_shape(int64_t M, int64_t N, int64_t K, int* block_m, int* block_n, int* block_k) {
+  if (block_m == nullptr || block_n == nullptr || block_k == nullptr) return TBL_ERR_INVALID_ARG;
+  if (M <= 0 || N <= 0 || K <= 0) return TBL_ERR_INVALID_ARG;
+  tile_rule(M, N, block_m, block_n, block_k);
+  return TBL_OK;
+}
+
+int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                   int swizzle_mode, int group_size, int persistent, int num_programs, int block_m,
+                   int block_n, int block_k, int32_t* trace, void* stream) {
+  int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent, num_programs,
+                         block_m, block_n, block_k);
+  if (rc != TBL_OK) return rc;
+  const int gm = static_cast<int>(M / block_m), gn = static_cast<int>(N / block_n);
+  int programs = 0;
+  rc = resolve_programs(dtype, block_m, block_n, block_k, static_cast<int64_t>(gm) * gn, persistent,
+                        num_programs, &programs);
+  if (rc != TBL_OK) return rc;
+  tbl::GemmLaunch a;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.order = make_order(swizzle_mode, gm, gn, group_size);
+  a.num_programs = programs;
+  a.trace = trace;
+  if (tbl::launch_gemm(dtype, block_m, block_n, block_k, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TBL_ERR_HIP;
+  return TBL_OK;
+}
+
+int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+             int swizzle_mode, int group_size, int persistent, int num_programs, void* stream) {
+  if (M <= 0 || N <= 0 || K <= 0) return TBL_ERR_INVALID_ARG;
+  int bm, bn, bk;
+  tile_rule(M, N, &bm, &bn, &bk);
+  return tbl_gemm_tiled(A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent, num_programs,
+                        bm, bn, bk, nullptr, stream);
+}
+
+int tbl_default_num_programs(int64_t M, int64_t N, int64_t K, int dtype, int persistent,
+                             int* num_programs) {
+  if (num_programs == nullptr || M <= 0 || N <= 0 || K <= 0) return TBL_ERR_INVALID_ARG;
+  if (dtype < TBL_F16 || dtype > TBL_BF16_F32OUT) return TBL_ERR_DTYPE;
+  if (persistent != 0 && persistent != 1) return TBL_ERR_INVALID_ARG;
+  int bm, bn, bk;
+  tile_rule(M, N, &bm, &bn, &bk);
+  if (M % bm || N % bn || K % bk || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
+  return resolve_programs(dtype, bm, bn, bk, (M / bm) * (N / bn), persistent, 0, num_programs);
+}
+
+int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32_t* tile_m,
+                 int32_t* tile_n, void* stream) {
+  if (tile_m == nullptr || tile_n == nullptr) return TBL_ERR_INVALID_ARG;
+  int rc = check_order(swizzle_mode, grid_m, grid_n, group_size);
+  if (rc != TBL_OK) return rc;
+  const tbl::TileOrder o = make_order(swizzle_mode, grid_m, grid_n, group_size);
+  if (tbl::launch_tile_map(o, tile_m, tile_n, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TBL_ERR_HIP;
+  return bijective_grid(swizzle_mode, grid_m, grid_n) ? TBL_OK : TBL_WARN_NOT_BIJECTIVE;
+}
+
+int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t cols, int layout,
+                      void* stream) {
+  if (in == nullptr || out == nullptr) return TBL_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0) return TBL_ERR_INVALID_ARG;
+  if (layout < TBL_T_NAIVE || layout > TBL_T_XOR) return TBL_ERR_INVALID_ARG;
+  if (rows % 64 || cols % 64 || rows > kMaxDim || cols > kMaxDim) return TBL_ERR_SHAPE;
+  if (!aligned16(in) || !aligned16(out)) return TBL_ERR_ALIGN;
+  if (tbl::launch_transpose_i32(in, out, static_cast<int>(rows), static_cast<int>(cols), layout,
+                                static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TBL_ERR_HIP;
+  return TBL_OK;
+}
+
+int tbl_device_info(int* num_cus, int* num_xcds, int* lds_bytes, int* l2_bytes, char* arch,
+                    int arch_len) {
+  DeviceInfo d;
+  int rc = device_info(&d);
+  if (rc != TBL_OK) return rc;
+  if (num_cus) *num_cus = d.cus;
+  if (num_xcds) *num_xcds = tbl::kNumXcds;
+  if (lds_bytes) *lds_bytes = d.lds;
+  if (l2_bytes) *l2_bytes = d.l2;
+  if (arch != nullptr && arch_len > 0) {
+    strncpy(arch, d.arch, static_cast<size_t>(arch_len) - 1);
+    arch[arch_len - 1] = '\0';
+  }
+  return TBL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tile_order.hpp"
+
+namespace tbl {
+
+struct GemmLaunch {
+  const void* A;
+  const void* B;
+  void* C;
+  int M, N, K;
+  TileOrder order;
+  int num_programs;
+  int32_t* trace;   // nullable
+};
+
+// dtype: TBL_F16 .. TBL_BF16_F32OUT. Returns hipSuccess or the launch error.
+hipError_t launch_gemm(int dtype, int bm, int bn, int bk, const GemmLaunch& a, hipStream_t s);
+// Resident workgroups per CU of the kernel for (dtype, tile), from the HIP occupancy query.
+hipError_t gemm_blocks_per_cu(int dtype, int bm, int bn, int bk, int* out);
+bool gemm_tile_supported(int bm, int bn, int bk);
+
+hipError_t launch_tile_map(const TileOrder& o, int32_t* tile_m, int32_t* tile_n, hipStream_t s);
+
+hipError_t launch_transpose_i32(const int32_t* in, int32_t* out, int rows, int cols, int layout,
+                                hipStream_t s);
+
+}  // namespace tbl
