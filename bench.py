@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the swizzled GEMM hot path on one MI355X.
+
+Workload: C = A * B at M = N = K = 4096, fp16 inputs uniform[-1, 1] (A seed 0, B seed 1), fp32
+accumulation, fp16 output, 256 x 256 x 64 tiles (a 16 x 16 tile grid), one workgroup per tile
+(non-persistent). One step runs the GEMM once in each tile order of the sweep -- row-major,
+grouped panel with groups 4, 8 and 16, Morton, XOR -- on the same HBM-resident inputs.
+
+Printed: one JSON line with
+  value        whole-step throughput, TFLOP/s (6 GEMMs x 2*4096^3 flops / step time);
+  modes        per-order average kernel time (HIP events on the launch stream), TFLOP/s, % of the
+               2.5 PFLOP/s dense fp16 MFMA peak, and the L2 (TCC) hit rate with its gain over
+               row-major from a separate rocprofv3 --pmc pass (not timed);
+  roofline     the GEMM kernel: average launch time -> TFLOP/s against the MFMA peak, and its HBM
+               traffic per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size);
+  cpu_baseline the fp64 CPU oracle on a sample of output rows of the same product.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-counters] [--no-cpu]
+"""
+
+import argparse
+import csv
+import glob
+import json
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+M = N = K = 4096
+TILE = 256
+PEAK_TFLOPS = 2500.0          # MI355X dense fp16/bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+MODES = [("row", 0, 1), ("panel_g4", 2, 4), ("panel_g8", 2, 8), ("panel_g16", 2, 16),
+         ("morton", 3, 1), ("xor", 4, 1)]
+FLOPS = 2.0 * M * N * K
+COPY_BYTES = 256 << 20        # calibration copy for the HBM traffic counters
+
+
+def _operands():
+    import numpy as np
+    import torch
+    from thread_block_lds_amd import synth
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
+    ad = torch.from_numpy(a.view(np.int16)).view(torch.float16).cuda()
+    bd = torch.from_numpy(b.view(np.int16)).view(torch.float16).cuda()
+    return a, b, ad, bd
+
+
+def counter_pass():
+    """Run under rocprofv3 --pmc by the parent: a calibration copy, then one GEMM per order."""
+    import torch
+    import thread_block_lds_amd as tbl
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    _, _, ad, bd = _operands()
+    c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for _, mode, g in MODES:
+        tbl.gemm(ad, bd, c, mode=mode, group=g)
+        torch.cuda.synchronize()
+    print("counter pass done", flush=True)
+
+
+def _run_pmc(counters, tag, tmp):
+    out = os.path.join(tmp, tag)
+    cmd = ["rocprofv3", "--pmc", *counters, "-d", out, "-o", tag, "--output-format", "csv", "--",
+           sys.executable, os.path.abspath(__file__), "--counter-pass"]
+    subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL, timeout=240,
+                   cwd=tmp, env=dict(os.environ, TMPDIR=tmp))
+    files = glob.glob(os.path.join(out, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise RuntimeError(f"rocprofv3 wrote no counter file for {tag}")
+    rows = {}
+    for r in csv.DictReader(open(files[0])):
+        d = int(r["Dispatch_Id"])
+        rows.setdefault(d, {"kernel": r["Kernel_Name"]})[r["Counter_Name"]] = float(r["Counter_Value"])
+    return [rows[d] for d in sorted(rows)]
+
+
+def counters():
+    """L2 hit rate per order and HBM traffic per GEMM launch, from three rocprofv3 --pmc passes."""
+    if shutil.which("rocprofv3") is None:
+        return None, "rocprofv3 not found"
+    tmp = tempfile.mkdtemp(prefix="tbl_bench_", dir="/tmp")
+    try:
+        res = {}
+        for tag, ctrs in (("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("fetch", ["FETCH_SIZE"]),
+                          ("write", ["WRITE_SIZE"])):
+            rows = _run_pmc(ctrs, tag, tmp)
+            first = next(i for i, r in enumerate(rows) if "gemm_kernel" in r["kernel"])
+            gemm = [r for r in rows if "gemm_kernel" in r["kernel"]]
+            if len(gemm) != len(MODES) or first == 0:
+                raise RuntimeError(f"{tag}: expected the copy then {len(MODES)} GEMM dispatches")
+            # the calibration copy is the dispatch just before the first GEMM
+            res[tag] = (rows[first - 1], gemm)
+        l2 = {}
+        for (name, _, _), r in zip(MODES, res["l2"][1]):
+            hit, miss = r["TCC_HIT_sum"], r["TCC_MISS_sum"]
+            l2[name] = 100.0 * hit / (hit + miss) if hit + miss > 0 else None
+        traffic = {}
+        for tag, key, true_kib in (("fetch", "FETCH_SIZE", COPY_BYTES / 1024.0),
+                                   ("write", "WRITE_SIZE", COPY_BYTES / 1024.0)):
+            copy, gemm = res[tag]
+            factor = (copy[key] / true_kib) if copy and copy.get(key) else None
+            traffic[tag] = {"factor": factor,
+                            "kib": {name: r[key] for (name, _, _), r in zip(MODES, gemm)}}
+        return {"l2": l2, "traffic": traffic}, None
+    except Exception as e:  # counters are reported as null with the reason
+        return None, f"{type(e).__name__}: {e}"
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def cpu_baseline(a, b, budget_s=10.0):
+    """The fp64 oracle on growing blocks of output rows until ~budget_s of work, as TFLOP/s."""
+    import numpy as np
+    from oracle import gemm as og
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    rows, total_rows, total_t = 64, 0, 0.0
+    start = 0
+    while total_t < budget_s and start < M:
+        r = np.arange(start, min(M, start + rows))
+        t0 = time.perf_counter()
+        og.gemm_rows(a, b, "f16", r)
+        total_t += time.perf_counter() - t0
+        total_rows += len(r)
+        start += len(r)
+        rows *= 2
+    flops = 2.0 * total_rows * N * K
+    return {"value": flops / total_t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle (numpy matmul on exactly decoded fp16) for output rows 0..{total_rows - 1} "
+                      f"of the 4096^3 product, {total_t:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-counters", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true")
+    args = ap.parse_args()
+
+    if args.counter_pass:
+        counter_pass()
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(output tiles shard across GPUs with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    # counters first, in child processes, before this process touches the GPU
+    ctr, ctr_err = (None, "skipped (--no-counters)") if args.no_counters else counters()
+
+    import torch
+    import thread_block_lds_amd as tbl
+    torch.cuda.set_device(0)
+    a, b, ad, bd = _operands()
+    c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for i, (_, mode, g) in enumerate(MODES):
+            if events is not None:
+                events[i][0].record(stream)
+            tbl.gemm(ad, bd, c, mode=mode, group=g, stream=stream.cuda_stream)
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in MODES] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    per_mode = {}
+    all_ms = []
+    for i, (name, mode, g) in enumerate(MODES):
+        ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
+        all_ms += ms
+        avg = sum(ms) / len(ms)
+        tf = FLOPS / (avg * 1e-3) / 1e12
+        per_mode[name] = {"mode": mode, "group": g, "ms": round(avg, 5), "tflops": round(tf, 1),
+                          "pct_peak": round(100 * tf / PEAK_TFLOPS, 2)}
+    if ctr:
+        row_hit = ctr["l2"].get("row")
+        for name in per_mode:
+            h = ctr["l2"].get(name)
+            per_mode[name]["l2_hit_pct"] = round(h, 2) if h is not None else None
+            per_mode[name]["l2_gain_pp_vs_row"] = round(h - row_hit, 2) if h is not None and row_hit is not None else None
+    kernel_ms = sum(all_ms) / len(all_ms)
+    achieved = FLOPS / (kernel_ms * 1e-3) / 1e12
+    traffic = None
+    if ctr:
+        fac_f = ctr["traffic"]["fetch"]["factor"]
+        fac_w = ctr["traffic"]["write"]["factor"]
+        if fac_f and fac_w:
+            kib = [ctr["traffic"]["fetch"]["kib"][n] / fac_f + ctr["traffic"]["write"]["kib"][n] / fac_w
+                   for n, _, _ in MODES]
+            traffic = round(1024.0 * sum(kib) / len(kib))
+    best = max(per_mode, key=lambda n: per_mode[n]["tflops"])
+    value = len(MODES) * FLOPS / (ms_step * 1e-3) / 1e12
+
+    out = {
+        "metric": "GEMM TFLOP/s + L2 hit rate per swizzle mode at 4096^3 fp16; % of MFMA peak",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: fp16 uniform[-1,1], A seed 0, B seed 1",
+        "config": {"workload": "gemm 4096x4096x4096 fp16->fp16 (fp32 accumulate), 256x256x64 tiles "
+                               "(16x16 grid), non-persistent, one GEMM per order per step: row, panel "
+                               "g4/g8/g16, morton, xor",
+                   "M": M, "N": N, "K": K, "tile": [TILE, TILE, 64], "orders": [n for n, _, _ in MODES],
+                   "parallelism": "single GPU"},
+        "pct_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "best_mode": best,
+        "modes": per_mode,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_kernel<256,256,f16,f16-out>", "kernel_avg_ms": round(kernel_ms, 5),
+                     "algorithmic_flops_per_launch": FLOPS,
+                     "algorithmic_bytes_per_launch": 2 * (M * K + K * N + M * N)},
+        "counters_note": ctr_err,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(a, b)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
