@@ -86,6 +86,19 @@ __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xF;
 }
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads past ``bytes`` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = bytes > 0xFFFFFFFFull ? -1 : static_cast<int>(static_cast<unsigned>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int BM, int BN, bool kBf16, bool kF32Out>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B,
@@ -94,15 +107,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
                                                         int32_t* __restrict__ trace) {
   constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;        // 32 x 32 MFMA blocks per wave
-  constexpr int kABytes = BM * kRowBytes;
-  constexpr int kStage = (BM + BN) * kRowBytes;
+  constexpr int kABytes = BM * kRowBytes;          // one A stage
+  constexpr int kBBytes = BN * kRowBytes;          // one B stage
+  constexpr int kBBase = 2 * kABytes;              // LDS: A0 A1 B0 B1
   constexpr int kALoads = BM * (kBK / 8) / kThreads;            // 16-byte chunks of A per thread
-  constexpr int kBBlocks = (BN / 8) * (kBK / 8);                // 8 x 8 blocks of B per stage
-  constexpr int kBPerThread = (kBBlocks + kThreads - 1) / kThreads;
+  constexpr int kNBlk = BN / 8;                                 // 8-column blocks of B
+  constexpr int kBBlocks = kNBlk * (kBK / 8);                   // 8 x 8 blocks of B per stage
   static_assert(kALoads >= 1 && BM * (kBK / 8) % kThreads == 0, "A tile must split over the threads");
-  static_assert(kBBlocks % 64 == 0, "B blocks must fill whole waves");
+  static_assert(kBBlocks <= kThreads && kBBlocks % 64 == 0, "B blocks must fill whole waves");
 
-  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+  __shared__ __attribute__((aligned(16))) char lds[2 * (kABytes + kBBytes)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,6 +124,30 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = K / kBK;
   (void)M;
+
+  // ---- per-thread constants (independent of the tile and of k) ----
+  // A: chunk (tid & 7) of tile rows (tid >> 3) + 32 j.
+  const int a_row0 = tid >> 3, a_chunk = tid & 7;
+  const int a_voff = (a_row0 * K + a_chunk * 8) * 2;
+  int a_st[kALoads];
+#pragma unroll
+  for (int j = 0; j < kALoads; ++j) a_st[j] = lds_offset(a_row0 + 32 * j, a_chunk);
+  // B: 8 x 8 block (k block kb, column block nb); rows kb*8 + e, columns nb*8 .. nb*8+7.
+  const bool b_active = tid < kBBlocks;
+  const int nb = tid % kNBlk, kb = tid / kNBlk;
+  const int b_voff = (kb * 8 * N + nb * 8) * 2;
+  int b_st[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) b_st[q] = kBBase + lds_offset(nb * 8 + q, kb);
+  // MFMA operand reads: lane reads row (lane mod 32) of a 32-row block, chunk 2s + lane/32.
+  int a_rd[2][4], b_rd[2][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a_rd[p][s] = lds_offset(wm * WM + p * 32 + (lane & 31), 2 * s + (lane >> 5));
+      b_rd[p][s] = kBBase + lds_offset(wn * WN + p * 32 + (lane & 31), 2 * s + (lane >> 5));
+    }
 
   int iter = 0;
   for (int t = blockIdx.x; t < order.tiles; t += num_programs, ++iter) {
@@ -123,53 +161,36 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
       rec[3] = tile_n;
       rec[4] = xcc_id();
     }
-    const uint16_t* a_tile = A + static_cast<size_t>(tile_m) * BM * K;
-    const uint16_t* b_tile = B + static_cast<size_t>(tile_n) * BN;
+    const size_t m0 = static_cast<size_t>(tile_m) * BM;
+    const size_t n0 = static_cast<size_t>(tile_n) * BN;
 
     uint4 a_reg[kALoads];
-    uint4 b_reg[kBPerThread][8];
+    uint4 b_reg[8];
 
-    auto global_load = [&](int k0) {
+    auto global_load = [&](int kt) {
+      const size_t k0 = static_cast<size_t>(kt) * kBK;
+      const uint16_t* a_base = A + m0 * K + k0;
+      const uint16_t* b_base = B + k0 * N + n0;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, (static_cast<size_t>(M) - m0) * K * 2 - k0 * 2);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, (static_cast<size_t>(K) - k0) * N * 2 - n0 * 2);
 #pragma unroll
-      for (int j = 0; j < kALoads; ++j) {
-        const int q = tid + j * kThreads;
-        const int row = q >> 3, chunk = q & 7;
-        a_reg[j] = *reinterpret_cast<const uint4*>(a_tile + static_cast<size_t>(row) * K + k0 + chunk * 8);
-      }
+      for (int j = 0; j < kALoads; ++j) a_reg[j] = buffer_load16(ra, a_voff, j * 32 * K * 2);
+      if (b_active) {
 #pragma unroll
-      for (int j = 0; j < kBPerThread; ++j) {
-        const int blk = tid + j * kThreads;
-        if (blk < kBBlocks) {
-          const int nb = blk % (BN / 8), kb = blk / (BN / 8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            b_reg[j][e] = *reinterpret_cast<const uint4*>(
-                b_tile + static_cast<size_t>(k0 + kb * 8 + e) * N + nb * 8);
-          }
-        }
+        for (int e = 0; e < 8; ++e) b_reg[e] = buffer_load16(rb, b_voff, e * N * 2);
       }
     };
 
     auto lds_store = [&](int stage) {
-      char* sa = lds + stage * kStage;
-      char* sb = sa + kABytes;
 #pragma unroll
-      for (int j = 0; j < kALoads; ++j) {
-        const int q = tid + j * kThreads;
-        *reinterpret_cast<uint4*>(sa + lds_offset(q >> 3, q & 7)) = a_reg[j];
-      }
+      for (int j = 0; j < kALoads; ++j)
+        *reinterpret_cast<uint4*>(lds + stage * kABytes + a_st[j]) = a_reg[j];
+      if (b_active) {
+        uint4 cols[8];
+        transpose_8x8_b16(b_reg, cols);
 #pragma unroll
-      for (int j = 0; j < kBPerThread; ++j) {
-        const int blk = tid + j * kThreads;
-        if (blk < kBBlocks) {
-          const int nb = blk % (BN / 8), kb = blk / (BN / 8);
-          uint4 cols[8];
-          transpose_8x8_b16(b_reg[j], cols);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            *reinterpret_cast<uint4*>(sb + lds_offset(nb * 8 + q, kb)) = cols[q];
-          }
-        }
+        for (int q = 0; q < 8; ++q)
+          *reinterpret_cast<uint4*>(lds + stage * kBBytes + b_st[q]) = cols[q];
       }
     };
 
@@ -179,44 +200,57 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
 
+    auto read_frags = [&](int stage, int s, uint4 (&af)[TM], uint4 (&bf)[TN]) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(lds + stage * kABytes + a_rd[i & 1][s] + (i >> 1) * 64 * kRowBytes);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const uint4*>(lds + stage * kBBytes + b_rd[j & 1][s] + (j >> 1) * 64 * kRowBytes);
+    };
+
+    auto compute = [&](int stage) {
+      uint4 af[2][TM], bf[2][TN];
+      read_frags(stage, 0, af[0], bf[0]);
+#pragma unroll
+      for (int s = 0; s < kBK / 16; ++s) {
+        if (s + 1 < kBK / 16) read_frags(stage, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = mfma32x32x16<kBf16>(bf[s & 1][j], af[s & 1][i], acc[i][j]);
+      }
+    };
+
+    // One k step: prefetch step kt+1 into registers, multiply from LDS stage ``stage``, then move
+    // the prefetched step into the other stage. The scheduling barriers keep the prefetch loads
+    // at the top, so their latency overlaps the whole multiply.
+    auto k_step = [&](int kt, int stage) {
+      const bool next = kt + 1 < nk;
+      if (next) global_load(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(stage);
+      __builtin_amdgcn_sched_barrier(0);
+      if (next) lds_store(stage ^ 1);
+      __syncthreads();
+    };
+
     global_load(0);
     lds_store(0);
     __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) global_load((kt + 1) * kBK);
-      const char* sa = lds + cur * kStage;
-      const char* sb = sa + kABytes;
-#pragma unroll
-      for (int s = 0; s < kBK / 16; ++s) {
-        const int chunk = 2 * s + (lane >> 5);
-        uint4 af[TM], bf[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const uint4*>(sa + lds_offset(wm * WM + i * 32 + (lane & 31), chunk));
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bf[j] = *reinterpret_cast<const uint4*>(sb + lds_offset(wn * WN + j * 32 + (lane & 31), chunk));
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<kBf16>(bf[j], af[i], acc[i][j]);
-      }
-      if (kt + 1 < nk) lds_store(cur ^ 1);
-      __syncthreads();
-    }
+    for (int kt = 0; kt < nk; ++kt) k_step(kt, kt & 1);
 
     // Lane l holds, for MFMA block (i, j) and group g, row (l mod 32) and columns
     // 8g + 4*(l div 32) .. +3 of that 32 x 32 block.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const size_t row = static_cast<size_t>(tile_m) * BM + wm * WM + i * 32 + (lane & 31);
+      const size_t row = m0 + wm * WM + i * 32 + (lane & 31);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = tile_n * BN + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          const size_t col = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
           const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
           const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
           if constexpr (kF32Out) {
