@@ -238,10 +238,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic: fp16 uniform[-1,1], A seed 0, B seed 1",
-        "config": {"workload": "gemm 4096x4096x4096 fp16->fp16 (fp32 accumulate), 256x256x64 tiles "
+        "config": {"workload": "gemm 4096x4096x4096 fp16->fp16 (fp32 accumulate), 256x256x32 tiles "
                                "(16x16 grid), non-persistent, one GEMM per order per step: row, panel "
                                "g4/g8/g16, morton, xor",
-                   "M": M, "N": N, "K": K, "tile": [TILE, TILE, 64], "orders": [n for n, _, _ in MODES],
+                   "M": M, "N": N, "K": K, "tile": [TILE, TILE, 32], "orders": [n for n, _, _ in MODES],
                    "parallelism": "single GPU"},
         "pct_peak": round(100 * value / PEAK_TFLOPS, 2),
         "best_mode": best,

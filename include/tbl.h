@@ -99,8 +99,9 @@ enum {
 /*
  * tbl_gemm -- C = A * B with a swizzled, optionally persistent tile schedule.
  *   A, B, C       device pointers (row-major M x K, K x N, M x N), 16-byte aligned, C not aliasing.
- *   M, N, K       sizes, > 0. The tile shape is fixed by a rule (tbl_gemm_tile_shape): 64x64x64 when
- *                 max(M, N) <= 1024, else 256x256x64; M, N, K must be multiples of it
+ *   M, N, K       sizes, > 0. The tile shape is fixed by a rule (tbl_gemm_tile_shape): 64x64x32 when
+ *                 max(M, N) <= 1024, else 256x256x32 (k advances through LDS 32 deep); M, N, K must
+ *                 be multiples of it
  *                 (TBL_ERR_SHAPE otherwise). Each size must be <= 2^20.
  *   dtype         TBL_F16, TBL_BF16, TBL_F16_F32OUT or TBL_BF16_F32OUT.
  *   swizzle_mode  a TBL_* order, optionally | TBL_XCD_REMAP. Morton and XOR need a square
@@ -113,15 +114,15 @@ enum {
  *                 schedule); < 0 is TBL_ERR_INVALID_ARG.
  *   stream        hipStream_t or NULL.
  * Every output element is computed by exactly one workgroup with fp32 accumulation over k in
- * ascending 64-wide steps, so for one tile shape the result does not depend on the order,
- * the remap flag, persistence or num_programs.
+ * ascending 16-deep MFMA steps, so the result does not depend on the order, the remap flag,
+ * persistence or num_programs.
  */
 int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
              int swizzle_mode, int group_size, int persistent, int num_programs, void* stream);
 
 /*
  * tbl_gemm_tiled -- tbl_gemm with an explicit tile shape and an optional schedule trace.
- *   block_m, block_n, block_k  one of the compiled shapes: 64x64x64, 128x128x64, 256x256x64
+ *   block_m, block_n, block_k  one of the compiled shapes: 64x64x32, 128x128x32, 256x256x32
  *                 (TBL_ERR_SHAPE otherwise).
  *   trace         NULL, or device int32[5 * T]: for every tile id t the workgroup that ran it writes
  *                 {program id, iteration of its tile loop, m, n, XCC id}. Caller-owned.

@@ -45,7 +45,7 @@ def _gemm(A=FAKE, B=FAKE, C=FAKE, M=512, N=512, K=512, dtype=0, mode=0, group=1,
     return tbl.lib().tbl_gemm(A, B, C, M, N, K, dtype, mode, group, persistent, P, NULL)
 
 
-def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=64, A=FAKE, dtype=0):
+def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=32, A=FAKE, dtype=0):
     return tbl.lib().tbl_gemm_tiled(A, FAKE, FAKE, M, N, K, dtype, mode, group, 0, 0, bm, bn, bk, NULL, NULL)
 
 
@@ -56,7 +56,7 @@ def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=64, A=FAKE, dt
     (dict(mode=6), tbl.ERR_INVALID_ARG), (dict(mode=0x200), tbl.ERR_INVALID_ARG), (dict(mode=-1), tbl.ERR_INVALID_ARG),
     (dict(mode=tbl.PANEL, group=0), tbl.ERR_INVALID_ARG), (dict(mode=tbl.SERPENTINE, group=-2), tbl.ERR_INVALID_ARG),
     (dict(persistent=2), tbl.ERR_INVALID_ARG), (dict(P=-1), tbl.ERR_INVALID_ARG),
-    (dict(M=520), tbl.ERR_SHAPE), (dict(N=500), tbl.ERR_SHAPE), (dict(K=100), tbl.ERR_SHAPE),
+    (dict(M=520), tbl.ERR_SHAPE), (dict(N=500), tbl.ERR_SHAPE), (dict(K=100), tbl.ERR_SHAPE), (dict(K=512 + 16), tbl.ERR_SHAPE),
     (dict(M=2048 + 64), tbl.ERR_SHAPE),             # 256-tile rule: not a multiple of 256
     (dict(M=(1 << 20) + 256, N=2048), tbl.ERR_SHAPE),
     (dict(M=10240, N=6144, K=2048, mode=tbl.MORTON), tbl.ERR_NOT_BIJECTIVE),
@@ -72,7 +72,8 @@ def test_gemm_validation(kw, want):
 def test_gemm_tiled_validation():
     assert _tiled(bm=32, bn=32) == tbl.ERR_SHAPE
     assert _tiled(bm=64, bn=128) == tbl.ERR_SHAPE
-    assert _tiled(bk=32) == tbl.ERR_SHAPE
+    assert _tiled(bk=64) == tbl.ERR_SHAPE
+    assert _tiled(K=512 + 16) == tbl.ERR_SHAPE
     assert _tiled(M=512 + 128, bm=256, bn=256) == tbl.ERR_SHAPE
     assert _tiled(mode=tbl.MORTON, M=1024, N=512, bm=128, bn=128) == tbl.ERR_NOT_BIJECTIVE
     assert _tiled(A=MISALIGNED) == tbl.ERR_ALIGN
@@ -100,10 +101,10 @@ def test_transpose_validation():
 
 
 def test_tile_shape_rule_and_default_programs():
-    assert tbl.gemm_tile_shape(512, 512, 512) == (64, 64, 64)
-    assert tbl.gemm_tile_shape(1024, 1024, 8192) == (64, 64, 64)
-    assert tbl.gemm_tile_shape(4096, 4096, 4096) == (256, 256, 64)
-    assert tbl.gemm_tile_shape(10240, 6144, 2048) == (256, 256, 64)
+    assert tbl.gemm_tile_shape(512, 512, 512) == (64, 64, 32)
+    assert tbl.gemm_tile_shape(1024, 1024, 8192) == (64, 64, 32)
+    assert tbl.gemm_tile_shape(4096, 4096, 4096) == (256, 256, 32)
+    assert tbl.gemm_tile_shape(10240, 6144, 2048) == (256, 256, 32)
     # non-persistent default needs no device: one workgroup per tile
     assert tbl.default_num_programs(512, 512, 512, persistent=False) == 64
     assert tbl.default_num_programs(8192, 8192, 8192, persistent=False) == 1024

@@ -61,7 +61,7 @@ def test_integer_inputs_exact_fp32_out(dtype, tile):
     a = synth.int_valued((M, K), 21, -2, 2, dtype)
     b = synth.int_valued((K, N), 22, -2, 2, dtype)
     ref = og.gemm(a, b, dtype)
-    c = tbl.gemm(dev16(a, dtype), dev16(b, dtype), out_dtype=torch.float32, tile=(tile, tile, 64),
+    c = tbl.gemm(dev16(a, dtype), dev16(b, dtype), out_dtype=torch.float32, tile=(tile, tile, 32),
                  mode=tm.PANEL, group=2)
     torch.cuda.synchronize()
     assert np.array_equal(host64(c), ref)
@@ -79,7 +79,7 @@ def test_output_rounding_is_nearest_even(dtype):
     else:
         want = synth.f32_to_bf16_bits(exact.astype(np.float32))
     for tile in (64, 256):
-        c = tbl.gemm(dev16(a, dtype), dev16(b, dtype), tile=(tile, tile, 64))
+        c = tbl.gemm(dev16(a, dtype), dev16(b, dtype), tile=(tile, tile, 32))
         torch.cuda.synchronize()
         assert np.array_equal(bits16(c), want), tile
 
@@ -91,14 +91,14 @@ def test_schedule_variants_bit_identical(tile):
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=5)
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     T = (M // tile) * (N // tile)
-    base = tbl.gemm(ad, bd, tile=(tile, tile, 64))
+    base = tbl.gemm(ad, bd, tile=(tile, tile, 32))
     torch.cuda.synchronize()
     rows = _sample_rows(M, tile)
     check_tol(host64(base)[rows], og.gemm_rows(a, b, "f16", rows), K, what=f"tile {tile}")
     for mode, g in [(tm.COL, 1), (tm.PANEL, 3), (tm.MORTON, 1), (tm.XOR, 1), (tm.SERPENTINE, 3)]:
         for remap in (0, tm.XCD_REMAP):
             for persistent, P in [(0, 0), (1, 0), (0, 1), (0, 7), (1, 13), (0, T + 5)]:
-                c = tbl.gemm(ad, bd, tile=(tile, tile, 64), mode=mode | remap, group=g,
+                c = tbl.gemm(ad, bd, tile=(tile, tile, 32), mode=mode | remap, group=g,
                              persistent=persistent, num_programs=P)
                 torch.cuda.synchronize()
                 assert torch.equal(c, base), (mode, remap, persistent, P)
@@ -168,7 +168,7 @@ def test_c4_rectangular_partial_groups():
                                                  (tm.ROW, 1, False, 0), (tm.XOR, 1, False, 100)])
 def test_trace_matches_oracle_schedule(mode, g, persistent, P):
     M = N = 8192
-    K = 64
+    K = 32
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=3)
     T = (M // 256) * (N // 256)
     trace = torch.full((5 * T,), -1, dtype=torch.int32, device="cuda")

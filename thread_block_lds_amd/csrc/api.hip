@@ -86,7 +86,7 @@ void tile_rule(int64_t M, int64_t N, int* bm, int* bn, int* bk) {
   const int t = (M > 1024 || N > 1024) ? 256 : 64;
   *bm = t;
   *bn = t;
-  *bk = 64;
+  *bk = 32;
 }
 
 int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,

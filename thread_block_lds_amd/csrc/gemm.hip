@@ -1,26 +1,30 @@
 // Tiled GEMM C = A * B for gfx950 with a swizzled, optionally persistent tile schedule.
 //
 // What is computed follows the GEMM kernel of "CUDA Thread Block Swizzle" (leimao.github.io),
-// section "CUDA Thread Block Swizzle Benchmark": every workgroup p walks tile ids p, p + P, p + 2P,
-// ... (P = workgroups launched), maps each id to an output tile (m, n) through the selected order,
-// and accumulates that tile in fp32 over k before casting to the output type. The order decides only
+// section "CUDA Thread Block Swizzle Benchmark": workgroup p walks tile ids p, p + P, p + 2P, ...
+// (P = workgroups launched), maps each id to an output tile (m, n) through the selected order, and
+// accumulates that tile in fp32 over k before casting to the output type. The order decides only
 // when a tile is computed, never its value.
 //
 // How it is computed on CDNA4:
 //   * 256 threads = 4 wave64s arranged 2 x 2; each wave owns a (BM/2) x (BN/2) sub-tile made of
 //     32 x 32 MFMA blocks (v_mfma_f32_32x32x16_{f16,bf16}) with fp32 accumulators.
-//   * Per 64-wide k step, A (BM x 64) and B (64 x BN) move global -> registers with 16-byte loads
-//     and registers -> LDS. LDS holds A as BM rows of 64 k values and B transposed, as BN rows of
-//     64 k values, so both MFMA operands read 8 consecutive k values (one 16-byte chunk) per lane.
-//     B is transposed in registers, in 8 x 8 blocks, on its way into LDS.
-//   * Each 128-byte LDS row is 8 chunks of 16 bytes; chunk c of row r is stored at chunk
-//     c XOR ((r XOR (r >> 3)) mod 8). This is the chunk-XOR swizzle of "CUDA Swizzle & bank
-//     conflict" (sections "Hopper TMA 的 swizzling" and "Triton - Shared Layout swizzling", vec = 8
-//     halves) with a phase that mixes two row bit-fields: the low 3 bits spread the 32 rows an MFMA
-//     operand read touches across all chunk columns, and bits 3..5 spread the rows 8 apart that the
-//     transposed B store writes in one instruction.
-//   * Two LDS stages: the loads of step k+1 are in flight while step k multiplies; one barrier per
-//     step.
+//   * A workgroup's tiles form one stream of 32-deep k steps (tile after tile). Operands move
+//     global -> LDS with direct-to-LDS 16-byte buffer loads (no registers in between) into five
+//     LDS stages of (BM + BN) x 32 sixteen-bit values, issued three steps ahead of their use, also
+//     across tile boundaries, so the next tile's first steps load during the current epilogue.
+//   * A sits in LDS row-major (one 64-byte row of k per m); B sits k-major as loaded (one row of
+//     BN values per k) and is read transposed by ds_read_b64_tr_b16, which hands each lane the
+//     8 consecutive k of one column that the MFMA B operand wants; no register transposes.
+//   * LDS swizzles (the chunk-XOR idea of "CUDA Swizzle & bank conflict", sections "Hopper TMA 的
+//     swizzling" and "Triton - Shared Layout swizzling", applied to 16-byte chunks and sized to
+//     gfx950's 64 x 4-byte banks): A chunk c of row r is stored at chunk c XOR ((r >> 2) mod 4);
+//     B chunk c of row k at chunk c XOR 4 (k mod 4). The XOR is applied on the global-address side
+//     of the direct loads, whose LDS destinations are fixed (lane l writes bytes 16 l .. 16 l + 15
+//     of its 1 KiB block). Both operand reads then hit 16 (A) or 32 (B) distinct 16-byte bank
+//     groups per service cycle.
+//   * One barrier per step, between its two 16-deep phases; operand reads run one phase ahead of
+//     the MFMAs that consume them.
 //   * The MFMA is issued with B as its first operand, so each lane ends up holding 4 consecutive
 //     output columns of one row and stores them with one 8-byte (16-bit output) or 16-byte (fp32
 //     output) store.
@@ -34,17 +38,14 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;          // k depth of one LDS stage
-constexpr int kRowBytes = 128;   // one LDS row: 64 sixteen-bit values = 8 chunks of 16 bytes
-
-__device__ __forceinline__ int swizzle_phase(int row) { return (row ^ (row >> 3)) & 7; }
-
-// Byte offset of logical chunk ``chunk`` of LDS row ``row``.
-__device__ __forceinline__ int lds_offset(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ swizzle_phase(row)) << 4);
-}
+constexpr int kBK = 32;          // k depth of one step / LDS stage
+constexpr int kStages = 5;       // LDS stages in flight
+constexpr int kARow = kBK * 2;   // bytes of one A row in LDS: 32 sixteen-bit values = 4 chunks
 
 template <bool kBf16>
 __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c) {
@@ -54,25 +55,6 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c) {
   } else {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
                                                   __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// rows[e] holds 8 sixteen-bit values of row e (columns 0..7); cols[q] receives column q (rows 0..7).
-__device__ __forceinline__ void transpose_8x8_b16(const uint4 (&rows)[8], uint4 (&cols)[8]) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = word(rows[2 * e], q >> 1);
-      const uint32_t hi = word(rows[2 * e + 1], q >> 1);
-      w[e] = (q & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-    cols[q] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -86,17 +68,58 @@ __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xF;
 }
 
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char_t;
 
-// Raw buffer resource over [base, base + bytes): loads past ``bytes`` return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
-  const int n = bytes > 0xFFFFFFFFull ? -1 : static_cast<int>(static_cast<unsigned>(bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+// Raw buffer descriptor over [base, base + bytes): loads past ``bytes`` return zero.
+__device__ __forceinline__ i32x4_t make_desc(const void* base, size_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const unsigned n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<unsigned>(bytes);
+  return i32x4_t{static_cast<int>(static_cast<unsigned>(b)), static_cast<int>((b >> 32) & 0xFFFFu),
+                 static_cast<int>(n), 0x00020000};
 }
 
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
+// 16 bytes per lane from desc + voffset straight into LDS: lane l writes lds_addr + 16 l.
+// Issued as inline asm so that the compiler's wait-count pass, which would otherwise make every
+// later LDS read wait for all direct loads in flight, leaves the waits to the explicit ones below.
+// M0 carries the LDS address; nothing else in this kernel keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_to_lds(i32x4_t desc, unsigned lds_addr, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(desc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+#define TBL_WAIT_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+
+// Wait until at most ``steps`` steps' worth (L loads each) of direct loads are still in flight.
+// Vector-memory operations retire in issue order on this architecture, so this also means every
+// older one has landed.
+template <int L>
+__device__ __forceinline__ void wait_steps(int steps) {
+  static_assert(L == 2 || L == 4 || L == 8, "loads per step");
+  if (steps >= 2) {
+    if constexpr (L == 8) TBL_WAIT_VMCNT(16);
+    else if constexpr (L == 4) TBL_WAIT_VMCNT(8);
+    else TBL_WAIT_VMCNT(4);
+  } else if (steps == 1) {
+    if constexpr (L == 8) TBL_WAIT_VMCNT(8);
+    else if constexpr (L == 4) TBL_WAIT_VMCNT(4);
+    else TBL_WAIT_VMCNT(2);
+  } else {
+    TBL_WAIT_VMCNT(0);
+  }
+}
+
+// Workgroup barrier that is also a compiler memory barrier, without the hardware waits that
+// __syncthreads() adds (those would drain the direct loads still in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ unsigned lds_address(const char* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_char_t*)p));   // generic -> LDS offset
 }
 
 template <int BM, int BN, bool kBf16, bool kF32Out>
@@ -107,163 +130,223 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
                                                         int32_t* __restrict__ trace) {
   constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;        // 32 x 32 MFMA blocks per wave
-  constexpr int kABytes = BM * kRowBytes;          // one A stage
-  constexpr int kBBytes = BN * kRowBytes;          // one B stage
-  constexpr int kBBase = 2 * kABytes;              // LDS: A0 A1 B0 B1
-  constexpr int kALoads = BM * (kBK / 8) / kThreads;            // 16-byte chunks of A per thread
-  constexpr int kNBlk = BN / 8;                                 // 8-column blocks of B
-  constexpr int kBBlocks = kNBlk * (kBK / 8);                   // 8 x 8 blocks of B per stage
-  static_assert(kALoads >= 1 && BM * (kBK / 8) % kThreads == 0, "A tile must split over the threads");
-  static_assert(kBBlocks <= kThreads && kBBlocks % 64 == 0, "B blocks must fill whole waves");
+  constexpr int kBRow = BN * 2;                    // bytes of one B row (one k) in LDS
+  constexpr int kAStage = BM * kARow;
+  constexpr int kBStage = kBK * kBRow;
+  constexpr int kStage = kAStage + kBStage;
+  constexpr int kAInst = kAStage / 1024 / 4;       // 1 KiB direct loads per wave per step
+  constexpr int kBInst = kBStage / 1024 / 4;
+  constexpr int kLoads = kAInst + kBInst;
+  constexpr int kBChunks = BN / 8;                 // 16-byte chunks per B row
+  static_assert(kAInst >= 1 && kBInst >= 1, "each wave loads at least one block of A and B");
+  static_assert(kStages == 5, "wait_steps assumes at most two newer steps in flight");
 
-  __shared__ __attribute__((aligned(16))) char lds[2 * (kABytes + kBBytes)];
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = K / kBK;
-  (void)M;
+  const int P = num_programs;
+  if (static_cast<int>(blockIdx.x) >= order.tiles) return;
+  const int my_tiles = (order.tiles - 1 - static_cast<int>(blockIdx.x)) / P + 1;
+  const int total = my_tiles * nk;
 
-  // ---- per-thread constants (independent of the tile and of k) ----
-  // A: chunk (tid & 7) of tile rows (tid >> 3) + 32 j.
-  const int a_row0 = tid >> 3, a_chunk = tid & 7;
-  const int a_voff = (a_row0 * K + a_chunk * 8) * 2;
-  int a_st[kALoads];
+  // ---- per-lane constants ----
+  // Direct loads. A block (16 rows of 64 bytes): lane l fills physical chunk l mod 4 of row l / 4,
+  // which holds logical chunk (l mod 4) XOR ((row >> 2) mod 4) = (l mod 4) XOR ((l >> 4) mod 4).
+  int a_voff[kAInst];
 #pragma unroll
-  for (int j = 0; j < kALoads; ++j) a_st[j] = lds_offset(a_row0 + 32 * j, a_chunk);
-  // B: 8 x 8 block (k block kb, column block nb); rows kb*8 + e, columns nb*8 .. nb*8+7.
-  const bool b_active = tid < kBBlocks;
-  const int nb = tid % kNBlk, kb = tid / kNBlk;
-  const int b_voff = (kb * 8 * N + nb * 8) * 2;
-  int b_st[8];
+  for (int j = 0; j < kAInst; ++j) {
+    const int row = (wave * kAInst + j) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    a_voff[j] = (row * K + chunk * 8) * 2;
+  }
+  // B block (1 KiB of k-major rows of BN values): lane l fills bytes 16 l of the block.
+  int b_voff[kBInst];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) b_st[q] = kBBase + lds_offset(nb * 8 + q, kb);
-  // MFMA operand reads: lane reads row (lane mod 32) of a 32-row block, chunk 2s + lane/32.
-  int a_rd[2][4], b_rd[2][4];
+  for (int j = 0; j < kBInst; ++j) {
+    const int o = (wave * kBInst + j) * 1024 + 16 * lane;
+    const int k = o / kBRow;
+    const int chunk = ((o % kBRow) >> 4) ^ ((4 * (k & 3)) & (kBChunks - 1));
+    b_voff[j] = (k * N + chunk * 8) * 2;
+  }
+  // MFMA operand reads. A: lane reads row (lane mod 32) of a 32-row block, logical chunk
+  // 2s + lane / 32 of phase s.
+  int a_rd[2];
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
+  for (int s = 0; s < 2; ++s) {
+    const int row = wm * WM + (lane & 31);
+    const int chunk = (2 * s + (lane >> 5)) ^ ((row >> 2) & 3);
+    a_rd[s] = row * kARow + chunk * 16;
+  }
+  // B: within each 16-lane group, lane r points at row k0 + r/4, columns n0 + 4 (r mod 4) .. +3;
+  // the transposing read then gives lane i column n0 + i at rows k0 .. k0 + 3.
+  int b_rd[TN];
+  {
+    const int g = lane >> 4, r = lane & 15;
+    const int k = 8 * (g >> 1) + (r >> 2);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      a_rd[p][s] = lds_offset(wm * WM + p * 32 + (lane & 31), 2 * s + (lane >> 5));
-      b_rd[p][s] = kBBase + lds_offset(wn * WN + p * 32 + (lane & 31), 2 * s + (lane >> 5));
+    for (int j = 0; j < TN; ++j) {
+      const int n = wn * WN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
+      const int chunk = (n >> 3) ^ ((4 * (k & 3)) & (kBChunks - 1));
+      b_rd[j] = kAStage + k * kBRow + chunk * 16 + (n & 7) * 2;
     }
+  }
 
-  int iter = 0;
-  for (int t = blockIdx.x; t < order.tiles; t += num_programs, ++iter) {
-    int tile_m, tile_n;
-    order_tile(order, t, tile_m, tile_n);
-    if (trace != nullptr && tid == 0) {
-      int32_t* rec = trace + 5 * static_cast<size_t>(t);
-      rec[0] = blockIdx.x;
-      rec[1] = iter;
-      rec[2] = tile_m;
-      rec[3] = tile_n;
-      rec[4] = xcc_id();
+  // ---- load cursor: the next step whose operands go to LDS ----
+  int ld_t = blockIdx.x, ld_kt = 0, ld_m = 0, ld_n = 0, ld_issued = 0, ld_stage = 0;
+  order_tile(order, ld_t, ld_m, ld_n);
+  auto issue_step = [&]() {
+    const size_t k0 = static_cast<size_t>(ld_kt) * kBK;
+    const size_t m0 = static_cast<size_t>(ld_m) * BM, n0 = static_cast<size_t>(ld_n) * BN;
+    const i32x4_t da = make_desc(A + m0 * K + k0, (static_cast<size_t>(M) - m0) * K * 2 - k0 * 2);
+    const i32x4_t db = make_desc(B + k0 * N + n0, (static_cast<size_t>(K) - k0) * N * 2 - n0 * 2);
+    const char* st = lds + ld_stage * kStage;
+#pragma unroll
+    for (int j = 0; j < kAInst; ++j)
+      load_to_lds(da, lds_address(st + (wave * kAInst + j) * 1024), a_voff[j]);
+#pragma unroll
+    for (int j = 0; j < kBInst; ++j)
+      load_to_lds(db, lds_address(st + kAStage + (wave * kBInst + j) * 1024), b_voff[j]);
+    ++ld_issued;
+    ld_stage = ld_stage == kStages - 1 ? 0 : ld_stage + 1;
+    if (++ld_kt == nk) {
+      ld_kt = 0;
+      ld_t += P;
+      if (ld_t < order.tiles) order_tile(order, ld_t, ld_m, ld_n);
     }
-    const size_t m0 = static_cast<size_t>(tile_m) * BM;
-    const size_t n0 = static_cast<size_t>(tile_n) * BN;
+  };
 
-    uint4 a_reg[kALoads];
-    uint4 b_reg[8];
+  auto read_a = [&](int stage, int s, uint4 (&af)[TM]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      af[i] = *reinterpret_cast<const uint4*>(lds + stage * kStage + a_rd[s] + i * 32 * kARow);
+  };
+  auto read_b = [&](int stage, int s, uint4 (&bf)[TN]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const char* p = lds + stage * kStage + b_rd[j] + s * 16 * kBRow;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kBRow));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      bf[j] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+    }
+  };
 
-    auto global_load = [&](int kt) {
-      const size_t k0 = static_cast<size_t>(kt) * kBK;
-      const uint16_t* a_base = A + m0 * K + k0;
-      const uint16_t* b_base = B + k0 * N + n0;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, (static_cast<size_t>(M) - m0) * K * 2 - k0 * 2);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, (static_cast<size_t>(K) - k0) * N * 2 - n0 * 2);
-#pragma unroll
-      for (int j = 0; j < kALoads; ++j) a_reg[j] = buffer_load16(ra, a_voff, j * 32 * K * 2);
-      if (b_active) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) b_reg[e] = buffer_load16(rb, b_voff, e * N * 2);
-      }
-    };
-
-    auto lds_store = [&](int stage) {
-#pragma unroll
-      for (int j = 0; j < kALoads; ++j)
-        *reinterpret_cast<uint4*>(lds + stage * kABytes + a_st[j]) = a_reg[j];
-      if (b_active) {
-        uint4 cols[8];
-        transpose_8x8_b16(b_reg, cols);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          *reinterpret_cast<uint4*>(lds + stage * kBBytes + b_st[q]) = cols[q];
-      }
-    };
-
-    f32x16_t acc[TM][TN];
+  f32x16_t acc[TM][TN];
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
-
-    auto read_frags = [&](int stage, int s, uint4 (&af)[TM], uint4 (&bf)[TN]) {
+  };
+  auto mfmas = [&](const uint4 (&af)[TM], const uint4 (&bf)[TN]) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(lds + stage * kABytes + a_rd[i & 1][s] + (i >> 1) * 64 * kRowBytes);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bf[j] = *reinterpret_cast<const uint4*>(lds + stage * kBBytes + b_rd[j & 1][s] + (j >> 1) * 64 * kRowBytes);
-    };
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<kBf16>(bf[j], af[i], acc[i][j]);
+  };
 
-    auto compute = [&](int stage) {
-      uint4 af[2][TM], bf[2][TN];
-      read_frags(stage, 0, af[0], bf[0]);
-#pragma unroll
-      for (int s = 0; s < kBK / 16; ++s) {
-        if (s + 1 < kBK / 16) read_frags(stage, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = mfma32x32x16<kBf16>(bf[s & 1][j], af[s & 1][i], acc[i][j]);
-      }
-    };
-
-    // One k step: prefetch step kt+1 into registers, multiply from LDS stage ``stage``, then move
-    // the prefetched step into the other stage. The scheduling barriers keep the prefetch loads
-    // at the top, so their latency overlaps the whole multiply.
-    auto k_step = [&](int kt, int stage) {
-      const bool next = kt + 1 < nk;
-      if (next) global_load(kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(stage);
-      __builtin_amdgcn_sched_barrier(0);
-      if (next) lds_store(stage ^ 1);
-      __syncthreads();
-    };
-
-    global_load(0);
-    lds_store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) k_step(kt, kt & 1);
-
-    // Lane l holds, for MFMA block (i, j) and group g, row (l mod 32) and columns
-    // 8g + 4*(l div 32) .. +3 of that 32 x 32 block.
+  // Lane l holds, for MFMA block (i, j) and group g, row (l mod 32) and columns
+  // 8g + 4*(l div 32) .. +3 of that 32 x 32 block. Accumulators stay in AGPRs until their block is
+  // stored: fp32 stores take AGPR data directly; the 16-bit path copies one block at a time to
+  // VGPRs (an explicit v_accvgpr_read keeps the compiler from copying all of them up front).
+  auto epilogue = [&](int tile_m, int tile_n) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const size_t row = m0 + wm * WM + i * 32 + (lane & 31);
+      const size_t row = static_cast<size_t>(tile_m) * BM + wm * WM + i * 32 + (lane & 31);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
+        float v[16];
+        if constexpr (kF32Out) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = acc[i][j][r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]));
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const size_t col = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-          const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          const size_t col = static_cast<size_t>(tile_n) * BN + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
           if constexpr (kF32Out) {
             float* C = static_cast<float*>(Cv);
-            *reinterpret_cast<float4*>(C + row * N + col) = make_float4(v0, v1, v2, v3);
+            *reinterpret_cast<float4*>(C + row * N + col) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
           } else {
             uint16_t* C = static_cast<uint16_t*>(Cv);
-            const uint32_t lo = to_out16(v0, kBf16) | (static_cast<uint32_t>(to_out16(v1, kBf16)) << 16);
-            const uint32_t hi = to_out16(v2, kBf16) | (static_cast<uint32_t>(to_out16(v3, kBf16)) << 16);
+            const uint32_t lo = to_out16(v[4 * g], kBf16) | (static_cast<uint32_t>(to_out16(v[4 * g + 1], kBf16)) << 16);
+            const uint32_t hi = to_out16(v[4 * g + 2], kBf16) | (static_cast<uint32_t>(to_out16(v[4 * g + 3], kBf16)) << 16);
             *reinterpret_cast<uint2*>(C + row * N + col) = make_uint2(lo, hi);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 block at a time
       }
+    }
+  };
+
+  // ---- compute cursor ----
+  int c_t = blockIdx.x, c_kt = 0, c_iter = 0, c_m = 0, c_n = 0, c_stage = 0;
+  order_tile(order, c_t, c_m, c_n);
+  auto record = [&]() {
+    if (trace != nullptr && tid == 0) {
+      int32_t* rec = trace + 5 * static_cast<size_t>(c_t);
+      rec[0] = blockIdx.x;
+      rec[1] = c_iter;
+      rec[2] = c_m;
+      rec[3] = c_n;
+      rec[4] = xcc_id();
+    }
+  };
+  record();
+
+  // prologue: up to kStages - 1 steps in flight; step 0 must have landed everywhere
+  const int pre = total < kStages - 1 ? total : kStages - 1;
+  for (int i = 0; i < pre; ++i) issue_step();
+  wait_steps<kLoads>(pre - 1);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  uint4 af0[TM], bf0[TN], af1[TM], bf1[TN];
+  read_a(0, 0, af0);
+  read_b(0, 0, bf0);
+  bool drained = false;   // an epilogue's stores are in flight: the next wait waits for everything
+  int g = 0;              // step index in this workgroup's stream
+
+  for (int tile = 0; tile < my_tiles; ++tile) {
+    zero_acc();
+    for (int kt = 0; kt < nk; ++kt, ++g) {
+      // phase 0: operands of phase 1 load while phase 0 multiplies
+      read_a(c_stage, 1, af1);
+      read_b(c_stage, 1, bf1);
+      mfmas(af0, bf0);
+      __builtin_amdgcn_sched_barrier(0);
+      // step g+1 must have landed in every wave's LDS blocks before anyone reads it
+      if (g + 1 < total) {
+        if (drained) TBL_WAIT_VMCNT(0);
+        else wait_steps<kLoads>(ld_issued - (g + 2));
+      }
+      lds_barrier();   // also: every wave's reads of the stage refilled below have completed
+      __builtin_amdgcn_sched_barrier(0);
+      drained = false;
+      // phase 1: refill the stage freed by step g-1, read step g+1's first operands, multiply
+      if (ld_issued < total) issue_step();
+      const int next_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
+      if (g + 1 < total) {
+        read_a(next_stage, 0, af0);
+        read_b(next_stage, 0, bf0);
+      }
+      mfmas(af1, bf1);
+      __builtin_amdgcn_sched_barrier(0);
+      c_stage = next_stage;
+    }
+    epilogue(c_m, c_n);
+    drained = true;
+    c_t += P;
+    ++c_iter;
+    if (c_t < order.tiles) {
+      order_tile(order, c_t, c_m, c_n);
+      record();
     }
   }
 }
