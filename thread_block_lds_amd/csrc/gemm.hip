@@ -75,8 +75,10 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 __device__ __forceinline__ i32x4_t make_desc(const void* base, size_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   const unsigned n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<unsigned>(bytes);
-  return i32x4_t{static_cast<int>(static_cast<unsigned>(b)), static_cast<int>((b >> 32) & 0xFFFFu),
-                 static_cast<int>(n), 0x00020000};
+  // The values are wave-uniform; readfirstlane makes that explicit so they live in SGPRs.
+  return i32x4_t{__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<unsigned>(b))),
+                 __builtin_amdgcn_readfirstlane(static_cast<int>((b >> 32) & 0xFFFFu)),
+                 __builtin_amdgcn_readfirstlane(static_cast<int>(n)), 0x00020000};
 }
 
 // 16 bytes per lane from desc + voffset straight into LDS: lane l writes lds_addr + 16 l.
@@ -87,7 +89,7 @@ __device__ __forceinline__ i32x4_t make_desc(const void* base, size_t bytes) {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_to_lds(i32x4_t desc, unsigned lds_addr, int voffset) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voffset), "s"(desc) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voffset), "s"(desc) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -196,20 +198,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   }
 
   // ---- load cursor: the next step whose operands go to LDS ----
+  // Every step issues exactly kLoads direct loads; past the end of this workgroup's stream they
+  // read a zero-length buffer (no memory access) into a stage nobody reads again, which keeps the
+  // number of loads in flight, and so every wait count, the same at each step.
   int ld_t = blockIdx.x, ld_kt = 0, ld_m = 0, ld_n = 0, ld_issued = 0, ld_stage = 0;
   order_tile(order, ld_t, ld_m, ld_n);
-  auto issue_step = [&]() {
+  i32x4_t ld_da, ld_db;
+  unsigned ld_lds = 0;
+  auto prepare_step = [&]() {
+    const bool real = ld_issued < total;
     const size_t k0 = static_cast<size_t>(ld_kt) * kBK;
     const size_t m0 = static_cast<size_t>(ld_m) * BM, n0 = static_cast<size_t>(ld_n) * BN;
-    const i32x4_t da = make_desc(A + m0 * K + k0, (static_cast<size_t>(M) - m0) * K * 2 - k0 * 2);
-    const i32x4_t db = make_desc(B + k0 * N + n0, (static_cast<size_t>(K) - k0) * N * 2 - n0 * 2);
-    const char* st = lds + ld_stage * kStage;
-#pragma unroll
-    for (int j = 0; j < kAInst; ++j)
-      load_to_lds(da, lds_address(st + (wave * kAInst + j) * 1024), a_voff[j]);
-#pragma unroll
-    for (int j = 0; j < kBInst; ++j)
-      load_to_lds(db, lds_address(st + kAStage + (wave * kBInst + j) * 1024), b_voff[j]);
+    ld_da = make_desc(A + m0 * K + k0, real ? (static_cast<size_t>(M) - m0) * K * 2 - k0 * 2 : 0);
+    ld_db = make_desc(B + k0 * N + n0, real ? (static_cast<size_t>(K) - k0) * N * 2 - n0 * 2 : 0);
+    ld_lds = lds_address(lds + ld_stage * kStage);
+  };
+  auto issue_load = [&](int q) {   // q-th of this wave's kLoads loads of the prepared step
+    if (q < kAInst) load_to_lds(ld_da, ld_lds + (wave * kAInst + q) * 1024, a_voff[q]);
+    else load_to_lds(ld_db, ld_lds + kAStage + (wave * kBInst + q - kAInst) * 1024, b_voff[q - kAInst]);
+  };
+  auto advance_load_cursor = [&]() {
     ++ld_issued;
     ld_stage = ld_stage == kStages - 1 ? 0 : ld_stage + 1;
     if (++ld_kt == nk) {
@@ -219,19 +227,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
     }
   };
 
-  auto read_a = [&](int stage, int s, uint4 (&af)[TM]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-      af[i] = *reinterpret_cast<const uint4*>(lds + stage * kStage + a_rd[s] + i * 32 * kARow);
-  };
-  auto read_b = [&](int stage, int s, uint4 (&bf)[TN]) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const char* p = lds + stage * kStage + b_rd[j] + s * 16 * kBRow;
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kBRow));
-      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-      bf[j] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+  // ---- operand fragments ----
+  // Read item q of phase s from a stage: items 0 .. TM-1 are A blocks (one 16-byte read each),
+  // items TM .. TM + 2 TN - 1 are halves of B blocks (one transposing 8-byte read each).
+  constexpr int kReads = TM + 2 * TN;
+  auto read_item = [&](int stage, int s, int q, uint4 (&af)[TM], uint4 (&bf)[TN]) {
+    if (q < TM) {
+      af[q] = *reinterpret_cast<const uint4*>(lds + stage * kStage + a_rd[s] + q * 32 * kARow);
+    } else {
+      const int j = (q - TM) >> 1, t = (q - TM) & 1;
+      const char* p = lds + stage * kStage + b_rd[j] + s * 16 * kBRow + t * 4 * kBRow;
+      const uint2 h = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+      if (t == 0) {
+        bf[j].x = h.x;
+        bf[j].y = h.y;
+      } else {
+        bf[j].z = h.x;
+        bf[j].w = h.y;
+      }
     }
   };
 
@@ -242,11 +255,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
   };
-  auto mfmas = [&](const uint4 (&af)[TM], const uint4 (&bf)[TN]) {
+
+  // One 16-deep phase: MFMA q of the phase, then (optionally) direct load q and operand read q
+  // for a later phase; the scheduling barrier after each group keeps this interleaving, so the
+  // matrix pipe always has an MFMA queued while loads and reads issue.
+  constexpr int kSlots = (TM * TN > kReads ? (TM * TN > kLoads ? TM * TN : kLoads)
+                                           : (kReads > kLoads ? kReads : kLoads));
+  auto phase = [&](const uint4 (&ua)[TM], const uint4 (&ub)[TN], bool loads, int rstage, int rs,
+                   uint4 (&ra)[TM], uint4 (&rb)[TN]) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<kBf16>(bf[j], af[i], acc[i][j]);
+    for (int q = 0; q < kSlots; ++q) {
+      if (q < TM * TN) {
+        const int i = q / TN, j = q % TN;
+        acc[i][j] = mfma32x32x16<kBf16>(ub[j], ua[i], acc[i][j]);
+      }
+      if (loads && q < kLoads) issue_load(q);
+      if (q < kReads) read_item(rstage, rs, q, ra, rb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Lane l holds, for MFMA block (i, j) and group g, row (l mod 32) and columns
@@ -286,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   };
 
   // ---- compute cursor ----
-  int c_t = blockIdx.x, c_kt = 0, c_iter = 0, c_m = 0, c_n = 0, c_stage = 0;
+  int c_t = blockIdx.x, c_iter = 0, c_m = 0, c_n = 0;
   order_tile(order, c_t, c_m, c_n);
   auto record = [&]() {
     if (trace != nullptr && tid == 0) {
@@ -300,44 +326,44 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   };
   record();
 
-  // prologue: up to kStages - 1 steps in flight; step 0 must have landed everywhere
-  const int pre = total < kStages - 1 ? total : kStages - 1;
-  for (int i = 0; i < pre; ++i) issue_step();
-  wait_steps<kLoads>(pre - 1);
+  // prologue: kStages - 1 steps in flight; step 0 must have landed everywhere
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i) {
+    prepare_step();
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) issue_load(q);
+    advance_load_cursor();
+  }
+  if constexpr (kLoads == 8) TBL_WAIT_VMCNT(24);
+  else if constexpr (kLoads == 4) TBL_WAIT_VMCNT(12);
+  else TBL_WAIT_VMCNT(6);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
   uint4 af0[TM], bf0[TN], af1[TM], bf1[TN];
-  read_a(0, 0, af0);
-  read_b(0, 0, bf0);
+#pragma unroll
+  for (int q = 0; q < kReads; ++q) read_item(0, 0, q, af0, bf0);
   bool drained = false;   // an epilogue's stores are in flight: the next wait waits for everything
-  int g = 0;              // step index in this workgroup's stream
+  int c_stage = 0;
 
   for (int tile = 0; tile < my_tiles; ++tile) {
     zero_acc();
-    for (int kt = 0; kt < nk; ++kt, ++g) {
-      // phase 0: operands of phase 1 load while phase 0 multiplies
-      read_a(c_stage, 1, af1);
-      read_b(c_stage, 1, bf1);
-      mfmas(af0, bf0);
-      __builtin_amdgcn_sched_barrier(0);
-      // step g+1 must have landed in every wave's LDS blocks before anyone reads it
-      if (g + 1 < total) {
-        if (drained) TBL_WAIT_VMCNT(0);
-        else wait_steps<kLoads>(ld_issued - (g + 2));
-      }
-      lds_barrier();   // also: every wave's reads of the stage refilled below have completed
+    for (int kt = 0; kt < nk; ++kt) {
+      // phase 0: multiply with phase-0 operands, read phase-1 operands of this step
+      phase(af0, bf0, false, c_stage, 1, af1, bf1);
+      // step + 1 must have landed in every wave's blocks (two newer steps may still be in flight),
+      // and every wave must be done reading the stage that is refilled next
+      if (drained) TBL_WAIT_VMCNT(0);
+      else wait_steps<kLoads>(2);
+      lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       drained = false;
-      // phase 1: refill the stage freed by step g-1, read step g+1's first operands, multiply
-      if (ld_issued < total) issue_step();
+      // phase 1: multiply with phase-1 operands, refill the stage of step - 1 with step + 4,
+      // read phase-0 operands of the next step (harmless stale data after the last step)
+      prepare_step();
       const int next_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
-      if (g + 1 < total) {
-        read_a(next_stage, 0, af0);
-        read_b(next_stage, 0, bf0);
-      }
-      mfmas(af1, bf1);
-      __builtin_amdgcn_sched_barrier(0);
+      phase(af1, bf1, true, next_stage, 0, af0, bf0);
+      advance_load_cursor();
       c_stage = next_stage;
     }
     epilogue(c_m, c_n);
