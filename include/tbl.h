@@ -124,8 +124,10 @@ int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_
  * tbl_gemm_tiled -- tbl_gemm with an explicit tile shape and an optional schedule trace.
  *   block_m, block_n, block_k  one of the compiled shapes: 64x64x32, 128x128x32, 256x256x32
  *                 (TBL_ERR_SHAPE otherwise).
- *   trace         NULL, or device int32[5 * T]: for every tile id t the workgroup that ran it writes
- *                 {program id, iteration of its tile loop, m, n, XCC id}. Caller-owned.
+ *   trace         NULL, or device int32[8 * T]: for every tile id t the workgroup that ran it writes
+ *                 {program id, iteration of its tile loop, m, n, XCC id, core-clock cycles and
+ *                 100 MHz real-time ticks from the tile's first k step to its epilogue, 0}.
+ *                 Caller-owned. Tracing adds a few instructions per tile.
  *   All other arguments as tbl_gemm.
  */
 int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,

@@ -171,11 +171,11 @@ def test_trace_matches_oracle_schedule(mode, g, persistent, P):
     K = 32
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=3)
     T = (M // 256) * (N // 256)
-    trace = torch.full((5 * T,), -1, dtype=torch.int32, device="cuda")
+    trace = torch.full((8 * T,), -1, dtype=torch.int32, device="cuda")
     tbl.gemm(dev16(a, "f16"), dev16(b, "f16"), mode=mode, group=g, persistent=persistent,
              num_programs=P, trace=trace)
     torch.cuda.synchronize()
-    tr = trace.cpu().numpy().reshape(T, 5).astype(np.int64)
+    tr = trace.cpu().numpy().reshape(T, 8).astype(np.int64)
     programs = P or (tbl.default_num_programs(M, N, K, persistent=persistent))
     om, on = tm.tile_table(mode, M // 256, N // 256, g)
     for t in range(T):

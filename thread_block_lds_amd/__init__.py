@@ -119,7 +119,7 @@ def gemm(a, b, c=None, mode=ROW, group=1, persistent=False, num_programs=0, out_
 
     a: (M, K), b: (K, N) contiguous fp16/bf16 CUDA tensors. c: optional (M, N) output of
     ``out_dtype`` (default: the input dtype; torch.float32 selects fp32 output). ``mode`` may include
-    XCD_REMAP. ``tile`` = (block_m, block_n, block_k); ``trace`` = int32 CUDA tensor of 5*T entries.
+    XCD_REMAP. ``tile`` = (block_m, block_n, block_k); ``trace`` = int32 CUDA tensor of 8*T entries.
     Returns c.
     """
     import torch

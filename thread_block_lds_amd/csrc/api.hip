@@ -67,19 +67,14 @@ bool bijective_grid(int swizzle_mode, int64_t gm, int64_t gn) {
 }
 
 tbl::TileOrder make_order(int swizzle_mode, int gm, int gn, int group) {
-  tbl::TileOrder o;
-  o.mode = swizzle_mode & 0xFF;
-  o.remap = (swizzle_mode & TBL_XCD_REMAP) ? 1 : 0;
-  o.grid_m = gm;
-  o.grid_n = gn;
+  const int mode = swizzle_mode & 0xFF;
   // A panel group taller than the grid, or a serpentine strip wider than it, orders the tiles
   // exactly as one of the grid's own height / width does; clamping keeps the device arithmetic in
   // 32 bits.
-  if (o.mode == TBL_PANEL) o.group = group < gm ? group : gm;
-  else if (o.mode == TBL_SERPENTINE) o.group = group < gn ? group : gn;
-  else o.group = 1;
-  o.tiles = gm * gn;
-  return o;
+  int g = 1;
+  if (mode == TBL_PANEL) g = group < gm ? group : gm;
+  else if (mode == TBL_SERPENTINE) g = group < gn ? group : gn;
+  return tbl::make_tile_order(mode, (swizzle_mode & TBL_XCD_REMAP) ? 1 : 0, gm, gn, g);
 }
 
 void tile_rule(int64_t M, int64_t N, int* bm, int* bn, int* bk) {

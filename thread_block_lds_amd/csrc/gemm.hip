@@ -46,6 +46,7 @@ constexpr int kThreads = 256;
 constexpr int kBK = 32;          // k depth of one step / LDS stage
 constexpr int kStages = 5;       // LDS stages in flight
 constexpr int kARow = kBK * 2;   // bytes of one A row in LDS: 32 sixteen-bit values = 4 chunks
+constexpr int kTraceInts = 8;    // int32 per tile in the optional schedule trace
 
 template <bool kBf16>
 __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c) {
@@ -115,9 +116,10 @@ __device__ __forceinline__ void wait_steps(int steps) {
 }
 
 // Workgroup barrier that is also a compiler memory barrier, without the hardware waits that
-// __syncthreads() adds (those would drain the direct loads still in flight).
+// __syncthreads() adds (those would drain the direct loads still in flight). Callers make sure
+// the LDS reads that must finish before it have been consumed already.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ unsigned lds_address(const char* p) {
@@ -201,16 +203,33 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   // Every step issues exactly kLoads direct loads; past the end of this workgroup's stream they
   // read a zero-length buffer (no memory access) into a stage nobody reads again, which keeps the
   // number of loads in flight, and so every wait count, the same at each step.
-  int ld_t = blockIdx.x, ld_kt = 0, ld_m = 0, ld_n = 0, ld_issued = 0, ld_stage = 0;
-  order_tile(order, ld_t, ld_m, ld_n);
+  int ld_t = blockIdx.x, ld_kt = 0, ld_issued = 0, ld_stage = 0;
+  // Running (wave-uniform) positions of the next step's A and B blocks; set with multiplies only
+  // when the cursor enters a new tile, then advanced by additions. Each step's buffer ranges are
+  // tile-local: A's rows of this tile from k0 on, B's 32 rows of this tile's columns; loads past
+  // them read zero instead of touching memory.
+  uint64_t ld_a = 0, ld_b = 0;
+  const unsigned a_step = kBK * 2;                                        // bytes per k step in A
+  const uint64_t b_step = static_cast<uint64_t>(kBK) * static_cast<unsigned>(N) * 2;
+  const unsigned a_range0 = static_cast<unsigned>(BM) * static_cast<unsigned>(K) * 2;
+  const unsigned b_range = (kBK - 1) * static_cast<unsigned>(N) * 2 + BN * 2;
+  unsigned a_range = a_range0;
+  auto enter_tile = [&]() {
+    int m, n;
+    order_tile(order, ld_t, m, n);
+    m = __builtin_amdgcn_readfirstlane(m);
+    n = __builtin_amdgcn_readfirstlane(n);
+    ld_a = reinterpret_cast<uint64_t>(A) + static_cast<uint64_t>(static_cast<unsigned>(m)) * a_range0;
+    ld_b = reinterpret_cast<uint64_t>(B) + static_cast<uint64_t>(static_cast<unsigned>(n)) * (BN * 2);
+    a_range = a_range0;
+  };
+  enter_tile();
   i32x4_t ld_da, ld_db;
   unsigned ld_lds = 0;
   auto prepare_step = [&]() {
     const bool real = ld_issued < total;
-    const size_t k0 = static_cast<size_t>(ld_kt) * kBK;
-    const size_t m0 = static_cast<size_t>(ld_m) * BM, n0 = static_cast<size_t>(ld_n) * BN;
-    ld_da = make_desc(A + m0 * K + k0, real ? (static_cast<size_t>(M) - m0) * K * 2 - k0 * 2 : 0);
-    ld_db = make_desc(B + k0 * N + n0, real ? (static_cast<size_t>(K) - k0) * N * 2 - n0 * 2 : 0);
+    ld_da = make_desc(reinterpret_cast<const void*>(ld_a), real ? a_range : 0u);
+    ld_db = make_desc(reinterpret_cast<const void*>(ld_b), real ? b_range : 0u);
     ld_lds = lds_address(lds + ld_stage * kStage);
   };
   auto issue_load = [&](int q) {   // q-th of this wave's kLoads loads of the prepared step
@@ -220,10 +239,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   auto advance_load_cursor = [&]() {
     ++ld_issued;
     ld_stage = ld_stage == kStages - 1 ? 0 : ld_stage + 1;
+    ld_a += a_step;
+    ld_b += b_step;
+    a_range -= a_step;
     if (++ld_kt == nk) {
       ld_kt = 0;
       ld_t += P;
-      if (ld_t < order.tiles) order_tile(order, ld_t, ld_m, ld_n);
+      if (ld_t < order.tiles) enter_tile();
     }
   };
 
@@ -248,19 +270,28 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
     }
   };
 
+  // Accumulators start from a zero the compiler cannot see through: a visible constant zero lets
+  // it peel the first k step (MFMA with a zero addend) and then shuffle accumulators between
+  // register tuples to join the peeled step and the loop.
   f32x16_t acc[TM][TN];
   auto zero_acc = [&]() {
+    float z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = z;
   };
 
-  // One 16-deep phase: MFMA q of the phase, then (optionally) direct load q and operand read q
-  // for a later phase; the scheduling barrier after each group keeps this interleaving, so the
-  // matrix pipe always has an MFMA queued while loads and reads issue.
-  constexpr int kSlots = (TM * TN > kReads ? (TM * TN > kLoads ? TM * TN : kLoads)
-                                           : (kReads > kLoads ? kReads : kLoads));
+  // One 16-deep phase: MFMA q of the phase, then (optionally) direct load q and two operand
+  // reads for a later phase; the scheduling barrier after each group keeps this interleaving, so
+  // the matrix pipe always has an MFMA queued while loads and reads issue, and the reads finish
+  // well before the phase that consumes them starts.
+  constexpr int kReadSlots = (kReads + 1) / 2;
+  constexpr int kSlots = (TM * TN > kReadSlots ? (TM * TN > kLoads ? TM * TN : kLoads)
+                                               : (kReadSlots > kLoads ? kReadSlots : kLoads));
   auto phase = [&](const uint4 (&ua)[TM], const uint4 (&ub)[TN], bool loads, int rstage, int rs,
                    uint4 (&ra)[TM], uint4 (&rb)[TN]) {
 #pragma unroll
@@ -270,7 +301,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
         acc[i][j] = mfma32x32x16<kBf16>(ub[j], ua[i], acc[i][j]);
       }
       if (loads && q < kLoads) issue_load(q);
-      if (q < kReads) read_item(rstage, rs, q, ra, rb);
+      if (2 * q < kReads) read_item(rstage, rs, 2 * q, ra, rb);
+      if (2 * q + 1 < kReads) read_item(rstage, rs, 2 * q + 1, ra, rb);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -291,7 +323,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
           for (int r = 0; r < 16; ++r) v[r] = acc[i][j][r];
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]));
+          for (int r = 0; r < 16; ++r)
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]) : "memory");
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -314,14 +347,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   // ---- compute cursor ----
   int c_t = blockIdx.x, c_iter = 0, c_m = 0, c_n = 0;
   order_tile(order, c_t, c_m, c_n);
+  // Schedule trace (optional): per tile id, the program, its loop iteration, (m, n), the XCD, and
+  // the core-clock cycles and 100 MHz real-time ticks from the tile's first step to its epilogue.
+  uint64_t clk0 = 0, rt0 = 0;
   auto record = [&]() {
+    if (trace != nullptr) {
+      if (tid == 0) {
+        int32_t* rec = trace + kTraceInts * static_cast<size_t>(c_t);
+        rec[0] = blockIdx.x;
+        rec[1] = c_iter;
+        rec[2] = c_m;
+        rec[3] = c_n;
+        rec[4] = xcc_id();
+      }
+      clk0 = __builtin_readcyclecounter();
+      rt0 = __builtin_amdgcn_s_memrealtime();
+    }
+  };
+  auto record_time = [&]() {
     if (trace != nullptr && tid == 0) {
-      int32_t* rec = trace + 5 * static_cast<size_t>(c_t);
-      rec[0] = blockIdx.x;
-      rec[1] = c_iter;
-      rec[2] = c_m;
-      rec[3] = c_n;
-      rec[4] = xcc_id();
+      int32_t* rec = trace + kTraceInts * static_cast<size_t>(c_t);
+      rec[5] = static_cast<int32_t>(__builtin_readcyclecounter() - clk0);
+      rec[6] = static_cast<int32_t>(__builtin_amdgcn_s_memrealtime() - rt0);
+      rec[7] = 0;
     }
   };
   record();
@@ -366,6 +414,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
       advance_load_cursor();
       c_stage = next_stage;
     }
+    record_time();
     epilogue(c_m, c_n);
     drained = true;
     c_t += P;

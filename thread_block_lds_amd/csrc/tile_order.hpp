@@ -8,10 +8,13 @@
 // the column-strip reading that reproduces that page's 4x4 table. The XCD remap is this library's
 // addition for gfx950's eight private L2s.
 //
-// All quantities are wave-uniform, so the compiler keeps them in scalar registers.
+// All quantities are wave-uniform, so in the GEMM they live in scalar registers. Every division is
+// by a launch constant whose reciprocal the host computes once (FastDiv), so a division costs a
+// scalar multiply-high, a multiply and one correction, and nothing needs hoisting out of loops.
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace tbl {
 
@@ -19,24 +22,52 @@ enum Order : int { kRow = 0, kCol = 1, kPanel = 2, kMorton = 3, kXor = 4, kSerpe
 constexpr int kXcdRemapFlag = 0x100;
 constexpr int kNumXcds = 8;
 
+// Division of a 32-bit unsigned n by a fixed d >= 1 through m = floor(2^32 / d) (0 when d = 1):
+// q0 = (n * m) >> 32 satisfies floor(n/d) - 1 <= q0 <= floor(n/d), so one correction is exact.
+struct FastDiv {
+  unsigned d;
+  unsigned m;
+};
+
+inline FastDiv make_fastdiv(unsigned d) {
+  FastDiv f;
+  f.d = d;
+  f.m = d <= 1 ? 0u : static_cast<unsigned>((uint64_t{1} << 32) / d);
+  return f;
+}
+
+__host__ __device__ inline unsigned fdiv(unsigned n, FastDiv f) {
+  if (f.d == 1) return n;
+  unsigned q = static_cast<unsigned>((static_cast<uint64_t>(n) * f.m) >> 32);
+  if (n - q * f.d >= f.d) ++q;
+  return q;
+}
+
+__host__ __device__ inline unsigned fmod_(unsigned n, FastDiv f) { return n - fdiv(n, f) * f.d; }
+
 struct TileOrder {
   int mode;      // kRow .. kSerpentine
   int remap;     // 1: apply the XCD remap before the order
   int grid_m;    // tile rows
   int grid_n;    // tile columns
-  int group;     // panel group / serpentine strip width, already clamped to [1, grid] by the host
+  int group;     // panel group / serpentine strip width, clamped by the host to [1, grid]
   int tiles;     // grid_m * grid_n
+  FastDiv div_m;         // grid_m
+  FastDiv div_n;         // grid_n
+  FastDiv div_span;      // panel: group * grid_n ids per group; serpentine: group * grid_m per strip
+  FastDiv div_full;      // panel: group rows; serpentine: group columns
+  FastDiv div_last;      // the same for the last, partial group / strip
 };
 
 // Round-robin dispatch puts workgroup w on XCD w % 8. Give XCD d the ids d*(T8/8) .. (d+1)*(T8/8)-1
 // of the order, in the order its workgroups arrive; ids past the last full group of 8 stay put.
 __host__ __device__ inline int xcd_remap(int t, int tiles) {
-  const int t8 = (tiles / kNumXcds) * kNumXcds;
+  const int t8 = tiles & ~(kNumXcds - 1);
   if (t >= t8) return t;
-  return (t % kNumXcds) * (t8 / kNumXcds) + t / kNumXcds;
+  return (t & (kNumXcds - 1)) * (t8 / kNumXcds) + (t >> 3);
 }
 
-// Gather the even (or odd) bits of a 32-bit id into the low 16 bits.
+// Gather the even bits of a 32-bit id into the low 16 bits.
 __host__ __device__ inline unsigned compact_even_bits(unsigned x) {
   x &= 0x55555555u;
   x = (x | (x >> 1)) & 0x33333333u;
@@ -46,49 +77,81 @@ __host__ __device__ inline unsigned compact_even_bits(unsigned x) {
   return x;
 }
 
-__host__ __device__ inline void order_tile(const TileOrder& o, int t, int& m, int& n) {
-  if (o.remap) t = xcd_remap(t, o.tiles);
-  const int gm = o.grid_m, gn = o.grid_n;
+__host__ __device__ inline void order_tile(const TileOrder& o, int t_in, int& m, int& n) {
+  const unsigned t = static_cast<unsigned>(o.remap ? xcd_remap(t_in, o.tiles) : t_in);
   switch (o.mode) {
-    case kRow:
-      m = t / gn;
-      n = t % gn;
+    case kRow: {
+      const unsigned q = fdiv(t, o.div_n);
+      m = static_cast<int>(q);
+      n = static_cast<int>(t - q * o.div_n.d);
       break;
-    case kCol:
-      m = t % gm;
-      n = t / gm;
+    }
+    case kCol: {
+      const unsigned q = fdiv(t, o.div_m);
+      n = static_cast<int>(q);
+      m = static_cast<int>(t - q * o.div_m.d);
       break;
+    }
     case kPanel: {
-      const int per_group = o.group * gn;
-      const int first = (t / per_group) * o.group;
-      const int height = min(gm - first, o.group);
-      m = first + t % height;
-      n = (t % per_group) / height;
+      // groups of `group` rows; the row inside a group is t modulo the group's height
+      const unsigned grp = fdiv(t, o.div_span);
+      const unsigned first = grp * o.div_full.d;
+      const unsigned in_group = t - grp * o.div_span.d;
+      const bool last = first + o.div_full.d > static_cast<unsigned>(o.grid_m);
+      const FastDiv h = last ? o.div_last : o.div_full;
+      m = static_cast<int>(first + fmod_(t, h));
+      n = static_cast<int>(fdiv(in_group, h));
       break;
     }
-    case kMorton: {
-      const unsigned u = static_cast<unsigned>(t);
-      m = static_cast<int>(compact_even_bits(u) % static_cast<unsigned>(gm));
-      n = static_cast<int>(compact_even_bits(u >> 1) % static_cast<unsigned>(gn));
+    case kMorton:
+      m = static_cast<int>(fmod_(compact_even_bits(t), o.div_m));
+      n = static_cast<int>(fmod_(compact_even_bits(t >> 1), o.div_n));
       break;
-    }
     case kXor: {
-      const int x = t % gn, y = t / gn;
-      m = (x ^ y) % gm;
-      n = y % gn;
+      const unsigned y = fdiv(t, o.div_n);
+      const unsigned x = t - y * o.div_n.d;
+      m = static_cast<int>(fmod_(x ^ y, o.div_m));
+      n = static_cast<int>(fmod_(y, o.div_n));
       break;
     }
-    default: {  // kSerpentine
-      const int per_strip = o.group * gm;
-      const int k = t / per_strip;
-      const int width = min(o.group, gn - k * o.group);
-      const int u = t - k * per_strip;
-      const int r = u / width;
-      m = (k & 1) ? gm - 1 - r : r;
-      n = k * o.group + u % width;
+    default: {  // kSerpentine: column strips of `group` columns, alternate strips walked upwards
+      const unsigned k = fdiv(t, o.div_span);
+      const unsigned u = t - k * o.div_span.d;
+      const bool last = (k + 1) * o.div_full.d > static_cast<unsigned>(o.grid_n);
+      const FastDiv w = last ? o.div_last : o.div_full;
+      const unsigned r = fdiv(u, w);
+      m = static_cast<int>((k & 1) ? static_cast<unsigned>(o.grid_m) - 1 - r : r);
+      n = static_cast<int>(k * o.div_full.d + (u - r * w.d));
       break;
     }
   }
+}
+
+// Host: the complete order description for a launch (group already clamped to the grid).
+inline TileOrder make_tile_order(int mode, int remap, int gm, int gn, int group) {
+  TileOrder o;
+  o.mode = mode;
+  o.remap = remap;
+  o.grid_m = gm;
+  o.grid_n = gn;
+  o.group = group;
+  o.tiles = gm * gn;
+  o.div_m = make_fastdiv(static_cast<unsigned>(gm));
+  o.div_n = make_fastdiv(static_cast<unsigned>(gn));
+  if (mode == kPanel) {
+    o.div_span = make_fastdiv(static_cast<unsigned>(group * gn));
+    o.div_full = make_fastdiv(static_cast<unsigned>(group));
+    const int rem = gm % group;
+    o.div_last = make_fastdiv(static_cast<unsigned>(rem == 0 ? group : rem));
+  } else if (mode == kSerpentine) {
+    o.div_span = make_fastdiv(static_cast<unsigned>(group * gm));
+    o.div_full = make_fastdiv(static_cast<unsigned>(group));
+    const int rem = gn % group;
+    o.div_last = make_fastdiv(static_cast<unsigned>(rem == 0 ? group : rem));
+  } else {
+    o.div_span = o.div_full = o.div_last = make_fastdiv(1);
+  }
+  return o;
 }
 
 }  // namespace tbl
