@@ -96,30 +96,30 @@ __device__ __forceinline__ void load_to_lds(i32x4_t desc, unsigned lds_addr, int
 
 #define TBL_WAIT_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 
-// Wait until at most ``steps`` steps' worth (L loads each) of direct loads are still in flight.
-// Vector-memory operations retire in issue order on this architecture, so this also means every
-// older one has landed.
-template <int L>
-__device__ __forceinline__ void wait_steps(int steps) {
-  static_assert(L == 2 || L == 4 || L == 8, "loads per step");
-  if (steps >= 2) {
-    if constexpr (L == 8) TBL_WAIT_VMCNT(16);
-    else if constexpr (L == 4) TBL_WAIT_VMCNT(8);
-    else TBL_WAIT_VMCNT(4);
-  } else if (steps == 1) {
-    if constexpr (L == 8) TBL_WAIT_VMCNT(8);
-    else if constexpr (L == 4) TBL_WAIT_VMCNT(4);
-    else TBL_WAIT_VMCNT(2);
-  } else {
-    TBL_WAIT_VMCNT(0);
-  }
+// s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this wave are in flight.
+// They retire in issue order on this architecture, so every older one has then completed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (N == 0) TBL_WAIT_VMCNT(0);
+  else if constexpr (N == 1) TBL_WAIT_VMCNT(1);
+  else if constexpr (N == 2) TBL_WAIT_VMCNT(2);
+  else if constexpr (N == 3) TBL_WAIT_VMCNT(3);
+  else if constexpr (N == 4) TBL_WAIT_VMCNT(4);
+  else if constexpr (N == 5) TBL_WAIT_VMCNT(5);
+  else if constexpr (N == 6) TBL_WAIT_VMCNT(6);
+  else if constexpr (N == 10) TBL_WAIT_VMCNT(10);
+  else if constexpr (N == 12) TBL_WAIT_VMCNT(12);
+  else if constexpr (N == 20) TBL_WAIT_VMCNT(20);
+  else if constexpr (N == 24) TBL_WAIT_VMCNT(24);
+  else static_assert(N < 0, "add this count");
 }
 
-// Workgroup barrier that is also a compiler memory barrier, without the hardware waits that
-// __syncthreads() adds (those would drain the direct loads still in flight). Callers make sure
-// the LDS reads that must finish before it have been consumed already.
+// Workgroup barrier that is also a compiler memory barrier. It first waits for this wave's LDS
+// reads (so no wave reads a stage that another wave refills after the barrier), but not for the
+// direct loads in flight, which __syncthreads() would drain.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_barrier" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ unsigned lds_address(const char* p) {
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   constexpr int kLoads = kAInst + kBInst;
   constexpr int kBChunks = BN / 8;                 // 16-byte chunks per B row
   static_assert(kAInst >= 1 && kBInst >= 1, "each wave loads at least one block of A and B");
-  static_assert(kStages == 5, "wait_steps assumes at most two newer steps in flight");
+  static_assert(kStages == 5, "the wait counts assume four steps in flight");
 
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
 
@@ -292,7 +292,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   constexpr int kReadSlots = (kReads + 1) / 2;
   constexpr int kSlots = (TM * TN > kReadSlots ? (TM * TN > kLoads ? TM * TN : kLoads)
                                                : (kReadSlots > kLoads ? kReadSlots : kLoads));
-  auto phase = [&](const uint4 (&ua)[TM], const uint4 (&ub)[TN], bool loads, int rstage, int rs,
+  static_assert(kLoads % 2 == 0, "loads split evenly between the two phases");
+  auto phase = [&](const uint4 (&ua)[TM], const uint4 (&ub)[TN], int load0, int rstage, int rs,
                    uint4 (&ra)[TM], uint4 (&rb)[TN]) {
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
@@ -300,7 +301,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
         const int i = q / TN, j = q % TN;
         acc[i][j] = mfma32x32x16<kBf16>(ub[j], ua[i], acc[i][j]);
       }
-      if (loads && q < kLoads) issue_load(q);
+      // half of the step's direct loads, on every other MFMA slot
+      if ((q & 1) == 0 && q / 2 < kLoads / 2) issue_load(load0 + q / 2);
       if (2 * q < kReads) read_item(rstage, rs, 2 * q, ra, rb);
       if (2 * q + 1 < kReads) read_item(rstage, rs, 2 * q + 1, ra, rb);
       __builtin_amdgcn_sched_barrier(0);
@@ -382,9 +384,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
     for (int q = 0; q < kLoads; ++q) issue_load(q);
     advance_load_cursor();
   }
-  if constexpr (kLoads == 8) TBL_WAIT_VMCNT(24);
-  else if constexpr (kLoads == 4) TBL_WAIT_VMCNT(12);
-  else TBL_WAIT_VMCNT(6);
+  wait_vm<3 * kLoads>();   // step 0 landed; steps 1..3 may still be in flight
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
@@ -394,23 +394,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   bool drained = false;   // an epilogue's stores are in flight: the next wait waits for everything
   int c_stage = 0;
 
+  // Step g: phase 0 multiplies with the operands read during the previous phase, reads phase 1's,
+  // and issues the first half of the loads of step g + 4 into the stage of step g - 1 (free since
+  // the previous barrier: its last reads were issued before it). The barrier certifies step g + 1
+  // in every wave's LDS blocks. Phase 1 multiplies, reads step g + 1's first operands and issues
+  // the second half of step g + 4's loads.
   for (int tile = 0; tile < my_tiles; ++tile) {
     zero_acc();
     for (int kt = 0; kt < nk; ++kt) {
-      // phase 0: multiply with phase-0 operands, read phase-1 operands of this step
-      phase(af0, bf0, false, c_stage, 1, af1, bf1);
-      // step + 1 must have landed in every wave's blocks (two newer steps may still be in flight),
-      // and every wave must be done reading the stage that is refilled next
-      if (drained) TBL_WAIT_VMCNT(0);
-      else wait_steps<kLoads>(2);
+      prepare_step();
+      phase(af0, bf0, 0, c_stage, 1, af1, bf1);
+      // newer than step g + 1's loads: steps g + 2 and g + 3, and half of step g + 4; after an
+      // epilogue its stores come first, so only the half step just issued may remain
+      if (drained) wait_vm<kLoads / 2>();
+      else wait_vm<2 * kLoads + kLoads / 2>();
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       drained = false;
-      // phase 1: multiply with phase-1 operands, refill the stage of step - 1 with step + 4,
-      // read phase-0 operands of the next step (harmless stale data after the last step)
-      prepare_step();
       const int next_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
-      phase(af1, bf1, true, next_stage, 0, af0, bf0);
+      phase(af1, bf1, kLoads / 2, next_stage, 0, af0, bf0);
       advance_load_cursor();
       c_stage = next_stage;
     }
