@@ -99,10 +99,11 @@ enum {
 /*
  * tbl_gemm -- C = A * B with a swizzled, optionally persistent tile schedule.
  *   A, B, C       device pointers (row-major M x K, K x N, M x N), 16-byte aligned, C not aliasing.
- *   M, N, K       sizes, > 0. The tile shape is fixed by a rule (tbl_gemm_tile_shape): 64x64x32 when
- *                 max(M, N) <= 1024, else 256x256x32 (k advances through LDS 32 deep); M, N, K must
- *                 be multiples of it
- *                 (TBL_ERR_SHAPE otherwise). Each size must be <= 2^20.
+ *   M, N, K       sizes, > 0, each <= 2^20. N and K must be multiples of 8 (rows are whole
+ *                 16-byte chunks); M is free. The tile shape is fixed by a rule
+ *                 (tbl_gemm_tile_shape): 64x64x32 when max(M, N) <= 1024, else 256x256x32 (k
+ *                 advances through LDS 32 deep). The tile grid is ceil(M/BM) x ceil(N/BN); edge tiles
+ *                 are masked (TBL_ERR_SHAPE for sizes outside these rules).
  *   dtype         TBL_F16, TBL_BF16, TBL_F16_F32OUT or TBL_BF16_F32OUT.
  *   swizzle_mode  a TBL_* order, optionally | TBL_XCD_REMAP. Morton and XOR need a square
  *                 power-of-two tile grid (TBL_ERR_NOT_BIJECTIVE otherwise).

@@ -56,13 +56,14 @@ def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=32, A=FAKE, dt
     (dict(mode=6), tbl.ERR_INVALID_ARG), (dict(mode=0x200), tbl.ERR_INVALID_ARG), (dict(mode=-1), tbl.ERR_INVALID_ARG),
     (dict(mode=tbl.PANEL, group=0), tbl.ERR_INVALID_ARG), (dict(mode=tbl.SERPENTINE, group=-2), tbl.ERR_INVALID_ARG),
     (dict(persistent=2), tbl.ERR_INVALID_ARG), (dict(P=-1), tbl.ERR_INVALID_ARG),
-    (dict(M=520), tbl.ERR_SHAPE), (dict(N=500), tbl.ERR_SHAPE), (dict(K=100), tbl.ERR_SHAPE), (dict(K=512 + 16), tbl.ERR_SHAPE),
-    (dict(M=2048 + 64), tbl.ERR_SHAPE),             # 256-tile rule: not a multiple of 256
+    (dict(N=500), tbl.ERR_SHAPE), (dict(K=100), tbl.ERR_SHAPE), (dict(N=512 + 4), tbl.ERR_SHAPE),
     (dict(M=(1 << 20) + 256, N=2048), tbl.ERR_SHAPE),
     (dict(M=10240, N=6144, K=2048, mode=tbl.MORTON), tbl.ERR_NOT_BIJECTIVE),
     (dict(M=10240, N=6144, K=2048, mode=tbl.XOR | tbl.XCD_REMAP), tbl.ERR_NOT_BIJECTIVE),
     (dict(M=1024, N=512, mode=tbl.XOR), tbl.ERR_NOT_BIJECTIVE),
     (dict(M=768, N=768, mode=tbl.MORTON), tbl.ERR_NOT_BIJECTIVE),   # 12 x 12 grid
+    (dict(M=8000, N=7000, mode=tbl.XOR), tbl.ERR_NOT_BIJECTIVE),    # 32 x 28 padded grid
+
     (dict(A=MISALIGNED), tbl.ERR_ALIGN), (dict(C=MISALIGNED), tbl.ERR_ALIGN),
 ])
 def test_gemm_validation(kw, want):
@@ -73,8 +74,7 @@ def test_gemm_tiled_validation():
     assert _tiled(bm=32, bn=32) == tbl.ERR_SHAPE
     assert _tiled(bm=64, bn=128) == tbl.ERR_SHAPE
     assert _tiled(bk=64) == tbl.ERR_SHAPE
-    assert _tiled(K=512 + 16) == tbl.ERR_SHAPE
-    assert _tiled(M=512 + 128, bm=256, bn=256) == tbl.ERR_SHAPE
+    assert _tiled(K=512 + 4) == tbl.ERR_SHAPE
     assert _tiled(mode=tbl.MORTON, M=1024, N=512, bm=128, bn=128) == tbl.ERR_NOT_BIJECTIVE
     assert _tiled(A=MISALIGNED) == tbl.ERR_ALIGN
     assert _tiled(dtype=9) == tbl.ERR_DTYPE
@@ -109,5 +109,7 @@ def test_tile_shape_rule_and_default_programs():
     assert tbl.default_num_programs(512, 512, 512, persistent=False) == 64
     assert tbl.default_num_programs(8192, 8192, 8192, persistent=False) == 1024
     assert tbl.default_num_programs(10240, 6144, 2048, persistent=False) == 960
+    assert tbl.default_num_programs(520, 512, 512, persistent=False) == 72     # 9 x 8 padded grid
+    assert tbl.default_num_programs(1, 8, 8, persistent=False) == 1
     with pytest.raises(tbl.TblError):
-        tbl.default_num_programs(520, 512, 512)
+        tbl.default_num_programs(520, 516, 512)

@@ -187,3 +187,57 @@ def test_trace_matches_oracle_schedule(mode, g, persistent, P):
         assert len(set(xcc[p::programs])) == 1, p           # a workgroup never changes XCD
     rr = np.mean(xcc[:min(programs, T)] == np.arange(min(programs, T)) % 8)
     print(f"workgroups on XCD (program mod 8): {rr:.3f}")
+
+
+RAGGED = [  # (M, N, K, tile): partial tiles at every edge, K tails of 8 .. 24, tiny and single-tile
+    (1, 8, 8, 64), (3, 8, 40, 64), (100, 136, 104, 64), (65, 72, 8, 64), (257, 264, 1000, 64),
+    (300, 200, 72, 128), (1000, 1000, 1000, 128), (129, 392, 520, 128),
+    (513, 264, 136, 256), (1100, 1032, 2056, 256), (255, 520, 4104, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K,tile", RAGGED)
+def test_ragged_edges_full_oracle(M, N, K, tile):
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=M + N + K)
+    ref = og.gemm(a, b, "f16")
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    c = tbl.gemm(ad, bd, tile=(tile, tile, 32), mode=tm.PANEL, group=2)
+    torch.cuda.synchronize()
+    check_tol(host64(c), ref, K, what=f"ragged {M}x{N}x{K} tile {tile}")
+    c32 = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=torch.float32, mode=tm.SERPENTINE,
+                   group=3, persistent=True)
+    torch.cuda.synchronize()
+    check_tol(host64(c32), ref, K, f32_out=True, what=f"ragged fp32 {M}x{N}x{K} tile {tile}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_ragged_integer_exact_and_untouched_padding(dtype):
+    # integer inputs: exact; the output is written into a larger buffer view to check that no
+    # element outside C is written
+    M, N, K = 300, 264, 200
+    a = synth.int_valued((M, K), 41, -3, 3, dtype)
+    b = synth.int_valued((K, N), 42, -3, 3, dtype)
+    ref = og.gemm(a, b, dtype)
+    big = torch.full((M + 64, N), 12345.0, dtype=torch.float32, device="cuda")
+    c = big[:M]
+    for tile in (64, 128, 256):
+        big.fill_(12345.0)
+        tbl.gemm(dev16(a, dtype), dev16(b, dtype), c=c, out_dtype=torch.float32, tile=(tile, tile, 32))
+        torch.cuda.synchronize()
+        assert np.array_equal(host64(c), ref), tile
+        assert torch.all(big[M:] == 12345.0), tile
+
+
+def test_k_tail_does_not_mix_rows():
+    # A K tail reads past the end of each row of A; those elements belong to the next row. An Inf
+    # placed at the start of row 1 must only reach row 1 of C.
+    M, N, K = 64, 64, 40
+    a = synth.f16_uniform((M, K), 51)
+    b = synth.f16_uniform((K, N), 52)
+    a[1, 0] = np.float16(np.inf).view(np.uint16)
+    for tile in (64, 128, 256):
+        c = tbl.gemm(dev16(a, "f16"), dev16(b, "f16"), out_dtype=torch.float32, tile=(tile, tile, 32))
+        torch.cuda.synchronize()
+        got = host64(c)
+        assert np.all(np.isfinite(np.delete(got, 1, axis=0))), tile
+        assert not np.all(np.isfinite(got[1])), tile

@@ -94,10 +94,12 @@ int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, i
   if (num_programs < 0) return TBL_ERR_INVALID_ARG;
   if (!tbl::gemm_tile_supported(bm, bn, bk)) return TBL_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
-  if (M % bm || N % bn || K % bk) return TBL_ERR_SHAPE;
-  int rc = check_order(swizzle_mode, M / bm, N / bn, group);
+  // rows of B and A must be whole 16-byte chunks; partial tiles at the M, N and K edges are masked
+  if (N % 8 || K % 8) return TBL_ERR_SHAPE;
+  const int64_t gm = (M + bm - 1) / bm, gn = (N + bn - 1) / bn;
+  int rc = check_order(swizzle_mode, gm, gn, group);
   if (rc != TBL_OK) return rc;
-  if (!bijective_grid(swizzle_mode, M / bm, N / bn)) return TBL_ERR_NOT_BIJECTIVE;
+  if (!bijective_grid(swizzle_mode, gm, gn)) return TBL_ERR_NOT_BIJECTIVE;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return TBL_ERR_ALIGN;
   return TBL_OK;
 }
@@ -156,7 +158,8 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
   int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent, num_programs,
                          block_m, block_n, block_k);
   if (rc != TBL_OK) return rc;
-  const int gm = static_cast<int>(M / block_m), gn = static_cast<int>(N / block_n);
+  const int gm = static_cast<int>((M + block_m - 1) / block_m);
+  const int gn = static_cast<int>((N + block_n - 1) / block_n);
   int programs = 0;
   rc = resolve_programs(dtype, block_m, block_n, block_k, static_cast<int64_t>(gm) * gn, persistent,
                         num_programs, &programs);
@@ -192,8 +195,9 @@ int tbl_default_num_programs(int64_t M, int64_t N, int64_t K, int dtype, int per
   if (persistent != 0 && persistent != 1) return TBL_ERR_INVALID_ARG;
   int bm, bn, bk;
   tile_rule(M, N, &bm, &bn, &bk);
-  if (M % bm || N % bn || K % bk || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
-  return resolve_programs(dtype, bm, bn, bk, (M / bm) * (N / bn), persistent, 0, num_programs);
+  if (N % 8 || K % 8 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
+  return resolve_programs(dtype, bm, bn, bk, ((M + bm - 1) / bm) * ((N + bn - 1) / bn), persistent, 0,
+                          num_programs);
 }
 
 int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32_t* tile_m,

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int nk = K / kBK;
+  const int nk = (K + kBK - 1) / kBK;
   const int P = num_programs;
   if (static_cast<int>(blockIdx.x) >= order.tiles) return;
   const int my_tiles = (order.tiles - 1 - static_cast<int>(blockIdx.x)) / P + 1;
@@ -160,12 +160,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   // ---- per-lane constants ----
   // Direct loads. A block (16 rows of 64 bytes): lane l fills physical chunk l mod 4 of row l / 4,
   // which holds logical chunk (l mod 4) XOR ((row >> 2) mod 4) = (l mod 4) XOR ((l >> 4) mod 4).
-  int a_voff[kAInst];
+  // In the last k step of a K that is not a multiple of 32, chunks at k >= K belong to the next
+  // row of A; a_voff_tail points those lanes past the buffer range, so they read zero.
+  constexpr int kOutOfRange = 0x7FFFFFF0;
+  int a_voff[kAInst], a_voff_tail[kAInst];
+  const int a_lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const bool a_tail_ok = a_lane_chunk * 8 + 8 <= K % kBK;
 #pragma unroll
   for (int j = 0; j < kAInst; ++j) {
     const int row = (wave * kAInst + j) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-    a_voff[j] = (row * K + chunk * 8) * 2;
+    a_voff[j] = (row * K + a_lane_chunk * 8) * 2;
+    a_voff_tail[j] = a_tail_ok ? a_voff[j] : kOutOfRange;
   }
   // B block (1 KiB of k-major rows of BN values): lane l fills bytes 16 l of the block.
   int b_voff[kBInst];
@@ -205,35 +210,42 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   // number of loads in flight, and so every wait count, the same at each step.
   int ld_t = blockIdx.x, ld_kt = 0, ld_issued = 0, ld_stage = 0;
   // Running (wave-uniform) positions of the next step's A and B blocks; set with multiplies only
-  // when the cursor enters a new tile, then advanced by additions. Each step's buffer ranges are
-  // tile-local: A's rows of this tile from k0 on, B's 32 rows of this tile's columns; loads past
-  // them read zero instead of touching memory.
+  // when the cursor enters a new tile, then advanced by additions. Each step's buffer ranges end
+  // at this tile's last row of A that exists (from k0 on) and at B's last row of this step that
+  // exists (k < K); loads past them read zero instead of touching memory. Tile rows past M and
+  // columns past N read values that only reach C elements that are never stored.
   uint64_t ld_a = 0, ld_b = 0;
   const unsigned a_step = kBK * 2;                                        // bytes per k step in A
   const uint64_t b_step = static_cast<uint64_t>(kBK) * static_cast<unsigned>(N) * 2;
-  const unsigned a_range0 = static_cast<unsigned>(BM) * static_cast<unsigned>(K) * 2;
-  const unsigned b_range = (kBK - 1) * static_cast<unsigned>(N) * 2 + BN * 2;
-  unsigned a_range = a_range0;
+  const unsigned b_row = static_cast<unsigned>(N) * 2;
+  unsigned a_range = 0, b_lead = 0;   // b_lead: n0 * 2, the base's offset into its row
   auto enter_tile = [&]() {
     int m, n;
     order_tile(order, ld_t, m, n);
     m = __builtin_amdgcn_readfirstlane(m);
     n = __builtin_amdgcn_readfirstlane(n);
-    ld_a = reinterpret_cast<uint64_t>(A) + static_cast<uint64_t>(static_cast<unsigned>(m)) * a_range0;
+    const int rows = min(BM, M - m * BM);
+    ld_a = reinterpret_cast<uint64_t>(A) +
+           static_cast<uint64_t>(static_cast<unsigned>(m)) * BM * static_cast<unsigned>(K) * 2;
     ld_b = reinterpret_cast<uint64_t>(B) + static_cast<uint64_t>(static_cast<unsigned>(n)) * (BN * 2);
-    a_range = a_range0;
+    a_range = static_cast<unsigned>(rows) * static_cast<unsigned>(K) * 2;
+    b_lead = static_cast<unsigned>(n) * (BN * 2);
   };
   enter_tile();
   i32x4_t ld_da, ld_db;
   unsigned ld_lds = 0;
+  bool ld_tail = false;   // the step being issued is a partial last k step
   auto prepare_step = [&]() {
     const bool real = ld_issued < total;
+    const int k_left = K - ld_kt * kBK;
+    const unsigned b_rows = static_cast<unsigned>(k_left < kBK ? k_left : kBK);
+    ld_tail = k_left < kBK;
     ld_da = make_desc(reinterpret_cast<const void*>(ld_a), real ? a_range : 0u);
-    ld_db = make_desc(reinterpret_cast<const void*>(ld_b), real ? b_range : 0u);
+    ld_db = make_desc(reinterpret_cast<const void*>(ld_b), real ? b_rows * b_row - b_lead : 0u);
     ld_lds = lds_address(lds + ld_stage * kStage);
   };
   auto issue_load = [&](int q) {   // q-th of this wave's kLoads loads of the prepared step
-    if (q < kAInst) load_to_lds(ld_da, ld_lds + (wave * kAInst + q) * 1024, a_voff[q]);
+    if (q < kAInst) load_to_lds(ld_da, ld_lds + (wave * kAInst + q) * 1024, ld_tail ? a_voff_tail[q] : a_voff[q]);
     else load_to_lds(ld_db, ld_lds + kAStage + (wave * kBInst + q - kAInst) * 1024, b_voff[q - kAInst]);
   };
   auto advance_load_cursor = [&]() {
@@ -241,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
     ld_stage = ld_stage == kStages - 1 ? 0 : ld_stage + 1;
     ld_a += a_step;
     ld_b += b_step;
-    a_range -= a_step;
+    a_range -= a_step;   // stays positive: the last step starts before the end of K
     if (++ld_kt == nk) {
       ld_kt = 0;
       ld_t += P;
@@ -331,6 +343,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const size_t col = static_cast<size_t>(tile_n) * BN + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;   // N % 8 == 0
           if constexpr (kF32Out) {
             float* C = static_cast<float*>(Cv);
             *reinterpret_cast<float4*>(C + row * N + col) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
