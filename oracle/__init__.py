@@ -24,4 +24,4 @@ Modules:
   l2_model    byte-granular LRU L2 model and Spearman rank check (page 1's offline predictor)
 """
 
-from . import tile_maps, gemm, transpose, lds  # noqa: F401
+from . import tile_maps, gemm, transpose, lds, l2_model  # noqa: F401
