@@ -2,20 +2,31 @@
 """Benchmark of the swizzled GEMM hot path on one MI355X.
 
 Workload: C = A * B at M = N = K = 4096, fp16 inputs uniform[-1, 1] (A seed 0, B seed 1), fp32
-accumulation, fp16 output, 256 x 256 x 64 tiles (a 16 x 16 tile grid), one workgroup per tile
-(non-persistent). One step runs the GEMM once in each tile order of the sweep -- row-major,
-grouped panel with groups 4, 8 and 16, Morton, XOR -- on the same HBM-resident inputs.
+accumulation, fp16 output, 256 x 256 x 32 tiles (a 16 x 16 tile grid), one workgroup per tile
+(non-persistent). One step runs the GEMM once in each variant of the sweep -- row-major, grouped
+panel with groups 4, 8 and 16, Morton, XOR, each without and with the XCD remap -- back to back on
+the same HBM-resident inputs.
 
 Printed: one JSON line with
-  value        whole-step throughput, TFLOP/s (6 GEMMs x 2*4096^3 flops / step time);
-  modes        per-order average kernel time (HIP events on the launch stream), TFLOP/s, % of the
-               2.5 PFLOP/s dense fp16 MFMA peak, and the L2 (TCC) hit rate with its gain over
-               row-major from a separate rocprofv3 --pmc pass (not timed);
+  value        whole-step throughput, TFLOP/s (12 GEMMs x 2*4096^3 flops / step wall time);
+  modes        per variant: warm kernel time (HIP events on the launch stream, inside the steps),
+               cold kernel time (median and min over launches that each follow a 512 MiB read that
+               evicts the L2s and the memory-side cache, as the page's timing clears L2 first),
+               TFLOP/s and % of the 2.5 PFLOP/s dense fp16 MFMA peak; the L2 (TCC) hit rate, its
+               gain over row-major, HBM fetch bytes, LDS bank conflicts and MFMA busy fraction from
+               rocprofv3 --pmc passes (cold launches, not timed); and the offline L2 prediction of
+               the library's tbl_predict_l2 for eight private L2s;
+  l2_model     Spearman rank correlations of the prediction with the measured hit rate, fetch bytes
+               and cold throughput;
   roofline     the GEMM kernel: average launch time -> TFLOP/s against the MFMA peak, and its HBM
                traffic per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size);
+  transpose    the int32 LDS transpose at 16384 x 16384 per layout: GB/s against 8 TB/s;
   cpu_baseline the fp64 CPU oracle on a sample of output rows of the same product.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-counters] [--no-cpu]
+       python bench.py --counter-pass      (one unmeasured GEMM, one cold GEMM per variant, then a
+                                            calibration copy)
+       python bench.py --transpose-pass    (each transpose layout at 1024x2048 and 16384x16384)
 """
 
 import argparse
@@ -24,6 +35,7 @@ import glob
 import json
 import os
 import shutil
+import statistics
 import subprocess
 import sys
 import tempfile
@@ -34,13 +46,24 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 M = N = K = 4096
-TILE = 256
+TILE, TILE_K = 256, 32
 PEAK_TFLOPS = 2500.0          # MI355X dense fp16/bf16 MFMA
 HBM_PEAK_GBS = 8000.0
-MODES = [("row", 0, 1), ("panel_g4", 2, 4), ("panel_g8", 2, 8), ("panel_g16", 2, 16),
-         ("morton", 3, 1), ("xor", 4, 1)]
+REMAP = 0x100
+ORDERS = [("row", 0, 1), ("panel_g4", 2, 4), ("panel_g8", 2, 8), ("panel_g16", 2, 16),
+          ("morton", 3, 1), ("xor", 4, 1)]
+MODES = [(name + suffix, mode | flag, g) for suffix, flag in (("", 0), ("+remap", REMAP))
+         for name, mode, g in ORDERS]
 FLOPS = 2.0 * M * N * K
 COPY_BYTES = 256 << 20        # calibration copy for the HBM traffic counters
+FLUSH_BYTES = 512 << 20       # > 8 x 4 MB L2 + 256 MB memory-side cache
+COLD_REPS = 10
+TR_SIZE = 16384
+TR_LAYOUTS = [("naive", 0), ("padded", 1), ("xor", 2)]
+PMC_PASSES = (("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("fetch", ["FETCH_SIZE"]),
+              ("write", ["WRITE_SIZE"]),
+              ("sq", ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
+                      "GRBM_GUI_ACTIVE"]))
 
 
 def _operands():
@@ -54,20 +77,51 @@ def _operands():
 
 
 def counter_pass():
-    """Run under rocprofv3 --pmc by the parent: a calibration copy, then one GEMM per order."""
+    """Run under rocprofv3 --pmc by the parent: per variant a cache-evicting read and one GEMM,
+    then the calibration copy as the last dispatch."""
     import torch
     import thread_block_lds_amd as tbl
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
     src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     _, _, ad, bd = _operands()
     c = torch.empty((M, N), dtype=torch.float16, device="cuda")
     torch.cuda.synchronize()
-    dst.copy_(src)
+    tbl.gemm(ad, bd, c)              # first launch of the kernel: not one of the measured ones
     torch.cuda.synchronize()
     for _, mode, g in MODES:
+        _evict(flush)
         tbl.gemm(ad, bd, c, mode=mode, group=g)
         torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
     print("counter pass done", flush=True)
+
+
+def _evict(buf):
+    """Read a buffer larger than every cache level: clean lines only, so the next kernel pays no
+    write-back of the eviction's data."""
+    buf.sum()
+
+
+def _transpose_input(rows, cols, seed):
+    import torch
+    from thread_block_lds_amd import synth
+    return torch.from_numpy(synth.i32_uniform((rows, cols), seed)).cuda()
+
+
+def transpose_pass():
+    """Each layout once at the correctness size and once at the throughput size (for profiling)."""
+    import torch
+    import thread_block_lds_amd as tbl
+    for rows, cols in ((1024, 2048), (TR_SIZE, TR_SIZE)):
+        x = _transpose_input(rows, cols, 0)
+        out = torch.empty((cols, rows), dtype=torch.int32, device="cuda")
+        for name, layout in TR_LAYOUTS:
+            tbl.transpose_i32(x, out, layout=layout)
+            torch.cuda.synchronize()
+            print(f"transpose {rows}x{cols} {name} done", flush=True)
+        del x, out
 
 
 def _run_pmc(counters, tag, tmp):
@@ -87,37 +141,74 @@ def _run_pmc(counters, tag, tmp):
 
 
 def counters():
-    """L2 hit rate per order and HBM traffic per GEMM launch, from three rocprofv3 --pmc passes."""
+    """Per-variant counters from the rocprofv3 --pmc passes (one child process each)."""
     if shutil.which("rocprofv3") is None:
         return None, "rocprofv3 not found"
     tmp = tempfile.mkdtemp(prefix="tbl_bench_", dir="/tmp")
     try:
         res = {}
-        for tag, ctrs in (("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("fetch", ["FETCH_SIZE"]),
-                          ("write", ["WRITE_SIZE"])):
+        for tag, ctrs in PMC_PASSES:
             rows = _run_pmc(ctrs, tag, tmp)
-            first = next(i for i, r in enumerate(rows) if "gemm_kernel" in r["kernel"])
-            gemm = [r for r in rows if "gemm_kernel" in r["kernel"]]
-            if len(gemm) != len(MODES) or first == 0:
-                raise RuntimeError(f"{tag}: expected the copy then {len(MODES)} GEMM dispatches")
-            # the calibration copy is the dispatch just before the first GEMM
-            res[tag] = (rows[first - 1], gemm)
-        l2 = {}
+            gemm = [r for r in rows if "gemm_kernel" in r["kernel"]][1:]   # the first is unmeasured
+            if len(gemm) != len(MODES) or "gemm_kernel" in rows[-1]["kernel"]:
+                raise RuntimeError(f"{tag}: expected 1 + {len(MODES)} GEMM dispatches, then the copy")
+            res[tag] = (rows[-1], gemm)     # the calibration copy is the last dispatch
+        per = {name: {} for name, _, _ in MODES}
         for (name, _, _), r in zip(MODES, res["l2"][1]):
             hit, miss = r["TCC_HIT_sum"], r["TCC_MISS_sum"]
-            l2[name] = 100.0 * hit / (hit + miss) if hit + miss > 0 else None
-        traffic = {}
-        for tag, key, true_kib in (("fetch", "FETCH_SIZE", COPY_BYTES / 1024.0),
-                                   ("write", "WRITE_SIZE", COPY_BYTES / 1024.0)):
+            per[name]["l2_hit_pct"] = 100.0 * hit / (hit + miss) if hit + miss > 0 else None
+        factors = {}
+        for tag, key in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
             copy, gemm = res[tag]
-            factor = (copy[key] / true_kib) if copy and copy.get(key) else None
-            traffic[tag] = {"factor": factor,
-                            "kib": {name: r[key] for (name, _, _), r in zip(MODES, gemm)}}
-        return {"l2": l2, "traffic": traffic}, None
+            factors[tag] = copy[key] / (COPY_BYTES / 1024.0) if copy.get(key) else None
+            for (name, _, _), r in zip(MODES, gemm):
+                per[name][tag + "_kib"] = r[key]
+        for (name, _, _), r in zip(MODES, res["sq"][1]):
+            per[name]["lds_bank_conflict_cycles"] = r["SQ_LDS_BANK_CONFLICT"]
+            per[name]["lds_conflict_frac"] = r["SQ_LDS_BANK_CONFLICT"] / max(r["SQ_LDS_IDX_ACTIVE"], 1.0)
+            # MFMA-busy SIMD cycles over (busy clocks per XCD x 256 CUs x 4 SIMDs); GRBM_GUI_ACTIVE
+            # sums the eight XCDs' busy clocks
+            per[name]["mfma_busy_frac"] = r["SQ_VALU_MFMA_BUSY_CYCLES"] / max(
+                r["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0, 1.0)
+        return {"per": per, "factors": factors}, None
     except Exception as e:  # counters are reported as null with the reason
         return None, f"{type(e).__name__}: {e}"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+def rank_corr(x, y):
+    """Spearman coefficient with ties ranked in index order (as the page's harness ranks them)."""
+    def ranks(v):
+        r = [0] * len(v)
+        for pos, i in enumerate(sorted(range(len(v)), key=lambda i: v[i])):
+            r[i] = pos
+        return r
+    rx, ry = ranks(list(x)), ranks(list(y))
+    n = len(rx)
+    mx, my = sum(rx) / n, sum(ry) / n
+    cov = sum((a - mx) * (b - my) for a, b in zip(rx, ry))
+    vx = sum((a - mx) ** 2 for a in rx)
+    vy = sum((b - my) ** 2 for b in ry)
+    return cov / (vx * vy) ** 0.5 if vx and vy else 0.0
+
+
+def predictions(tbl):
+    """tbl_predict_l2 per variant: eight private L2s of the reported size, workgroup w on XCD w % 8,
+    every resident workgroup of an XCD running together (one wave at one workgroup per CU)."""
+    info = tbl.device_info()
+    xcds, l2 = info["num_xcds"], info["l2_bytes"]
+    gm, gn, gk = M // TILE, N // TILE, K // TILE_K
+    block = TILE * TILE_K * 2
+    resident = max(1, tbl.default_num_programs(M, N, K, tbl.F16, persistent=True) // xcds)
+    out = {}
+    for name, mode, g in MODES:
+        hits, acc, _ = tbl.predict_l2(mode, gm, gn, gk, g, block, block, l2, num_caches=xcds,
+                                      num_programs=0, resident=resident)
+        out[name] = {"hit_pct": 100.0 * hits / acc,
+                     "fetch_mb": ((acc - hits) * block + 2 * M * N) / 1e6}
+    return out, {"caches": xcds, "capacity_bytes": l2, "resident_per_cache": resident,
+                 "block_bytes": block, "grid": [gm, gn, gk]}
 
 
 def cpu_baseline(a, b, budget_s=10.0):
@@ -145,6 +236,29 @@ def cpu_baseline(a, b, budget_s=10.0):
                       f"of the 4096^3 product, {total_t:.1f} s wall"}
 
 
+def time_transpose(tbl, torch, stream, reps=10):
+    x = _transpose_input(TR_SIZE, TR_SIZE, 0)
+    out = torch.empty((TR_SIZE, TR_SIZE), dtype=torch.int32, device="cuda")
+    res = {}
+    for name, layout in TR_LAYOUTS:
+        for _ in range(2):
+            tbl.transpose_i32(x, out, layout=layout, stream=stream.cuda_stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            tbl.transpose_i32(x, out, layout=layout, stream=stream.cuda_stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
+        gbs = 8.0 * TR_SIZE * TR_SIZE / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del x, out
+    return {"workload": f"int32 {TR_SIZE}x{TR_SIZE} transpose through 64x64 LDS tiles",
+            "algorithmic_bytes_per_launch": 8 * TR_SIZE * TR_SIZE, "peak_GB/s": HBM_PEAK_GBS,
+            "layouts": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,10 +267,14 @@ def main():
     ap.add_argument("--no-counters", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counter-pass", action="store_true")
+    ap.add_argument("--transpose-pass", action="store_true")
     args = ap.parse_args()
 
     if args.counter_pass:
         counter_pass()
+        return
+    if args.transpose_pass:
+        transpose_pass()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -174,6 +292,7 @@ def main():
     torch.cuda.set_device(0)
     a, b, ad, bd = _operands()
     c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -196,6 +315,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # cold launches: each after a fill that evicts every cache level, outside the events
+    cold = {}
+    for name, mode, g in MODES:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(COLD_REPS)]
+        for e0, e1 in ev:
+            _evict(flush)
+            e0.record(stream)
+            tbl.gemm(ad, bd, c, mode=mode, group=g, stream=stream.cuda_stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        cold[name] = [e0.elapsed_time(e1) for e0, e1 in ev]
+    del flush
+
+    pred, pred_cfg = predictions(tbl)
+    transpose = time_transpose(tbl, torch, stream)
+
     ms_step = wall * 1e3 / args.steps
     per_mode = {}
     all_ms = []
@@ -204,24 +340,44 @@ def main():
         all_ms += ms
         avg = sum(ms) / len(ms)
         tf = FLOPS / (avg * 1e-3) / 1e12
+        cmed, cmin = statistics.median(cold[name]), min(cold[name])
         per_mode[name] = {"mode": mode, "group": g, "ms": round(avg, 5), "tflops": round(tf, 1),
-                          "pct_peak": round(100 * tf / PEAK_TFLOPS, 2)}
-    if ctr:
-        row_hit = ctr["l2"].get("row")
-        for name in per_mode:
-            h = ctr["l2"].get(name)
-            per_mode[name]["l2_hit_pct"] = round(h, 2) if h is not None else None
-            per_mode[name]["l2_gain_pp_vs_row"] = round(h - row_hit, 2) if h is not None and row_hit is not None else None
-    kernel_ms = sum(all_ms) / len(all_ms)
-    achieved = FLOPS / (kernel_ms * 1e-3) / 1e12
+                          "pct_peak": round(100 * tf / PEAK_TFLOPS, 2),
+                          "cold_ms_median": round(cmed, 5), "cold_ms_min": round(cmin, 5),
+                          "cold_tflops": round(FLOPS / (cmed * 1e-3) / 1e12, 1),
+                          "pred_l2_hit_pct": round(pred[name]["hit_pct"], 2),
+                          "pred_fetch_mb": round(pred[name]["fetch_mb"], 1)}
+    l2_model = {"model": "tbl_predict_l2: byte-LRU replay per XCD (page's offline model, one cache per XCD)",
+                **pred_cfg,
+                "spearman_pred_vs_cold_tflops": round(rank_corr(
+                    [pred[n]["hit_pct"] for n, _, _ in MODES],
+                    [per_mode[n]["cold_tflops"] for n, _, _ in MODES]), 3)}
     traffic = None
     if ctr:
-        fac_f = ctr["traffic"]["fetch"]["factor"]
-        fac_w = ctr["traffic"]["write"]["factor"]
+        per = ctr["per"]
+        fac_f, fac_w = ctr["factors"]["fetch"], ctr["factors"]["write"]
+        row_hit = per["row"]["l2_hit_pct"]
+        for name in per_mode:
+            h = per[name]["l2_hit_pct"]
+            per_mode[name]["l2_hit_pct"] = round(h, 2) if h is not None else None
+            per_mode[name]["l2_gain_pp_vs_row"] = (round(h - row_hit, 2)
+                                                   if h is not None and row_hit is not None else None)
+            per_mode[name]["fetch_mb"] = round(per[name]["fetch_kib"] * 1024 / fac_f / 1e6, 1) if fac_f else None
+            per_mode[name]["write_mb"] = round(per[name]["write_kib"] * 1024 / fac_w / 1e6, 1) if fac_w else None
+            per_mode[name]["lds_conflict_frac"] = round(per[name]["lds_conflict_frac"], 5)
+            per_mode[name]["mfma_busy_frac"] = round(per[name]["mfma_busy_frac"], 4)
         if fac_f and fac_w:
-            kib = [ctr["traffic"]["fetch"]["kib"][n] / fac_f + ctr["traffic"]["write"]["kib"][n] / fac_w
-                   for n, _, _ in MODES]
-            traffic = round(1024.0 * sum(kib) / len(kib))
+            mb = [per_mode[n]["fetch_mb"] + per_mode[n]["write_mb"] for n, _, _ in MODES]
+            traffic = round(1e6 * sum(mb) / len(mb))
+        names = [n for n, _, _ in MODES]
+        if all(per_mode[n]["l2_hit_pct"] is not None for n in names):
+            l2_model["spearman_pred_vs_measured_hit"] = round(rank_corr(
+                [pred[n]["hit_pct"] for n in names], [per_mode[n]["l2_hit_pct"] for n in names]), 3)
+        if fac_f:
+            l2_model["spearman_pred_vs_measured_fetch"] = round(rank_corr(
+                [pred[n]["fetch_mb"] for n in names], [per_mode[n]["fetch_mb"] for n in names]), 3)
+    kernel_ms = sum(all_ms) / len(all_ms)
+    achieved = FLOPS / (kernel_ms * 1e-3) / 1e12
     best = max(per_mode, key=lambda n: per_mode[n]["tflops"])
     value = len(MODES) * FLOPS / (ms_step * 1e-3) / 1e12
 
@@ -239,18 +395,20 @@ def main():
         "dtype": "f16",
         "data": "synthetic: fp16 uniform[-1,1], A seed 0, B seed 1",
         "config": {"workload": "gemm 4096x4096x4096 fp16->fp16 (fp32 accumulate), 256x256x32 tiles "
-                               "(16x16 grid), non-persistent, one GEMM per order per step: row, panel "
-                               "g4/g8/g16, morton, xor",
-                   "M": M, "N": N, "K": K, "tile": [TILE, TILE, 32], "orders": [n for n, _, _ in MODES],
-                   "parallelism": "single GPU"},
+                               "(16x16 grid), non-persistent, one GEMM per variant per step: row, panel "
+                               "g4/g8/g16, morton, xor, each without and with the XCD remap",
+                   "M": M, "N": N, "K": K, "tile": [TILE, TILE, TILE_K],
+                   "variants": [n for n, _, _ in MODES], "parallelism": "single GPU"},
         "pct_peak": round(100 * value / PEAK_TFLOPS, 2),
         "best_mode": best,
         "modes": per_mode,
+        "l2_model": l2_model,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": "gemm_kernel<256,256,f16,f16-out>", "kernel_avg_ms": round(kernel_ms, 5),
                      "algorithmic_flops_per_launch": FLOPS,
                      "algorithmic_bytes_per_launch": 2 * (M * K + K * N + M * N)},
+        "transpose": transpose,
         "counters_note": ctr_err,
     }
     if not args.no_cpu:

@@ -13,6 +13,9 @@
  *   - tbl_transpose_i32: the int32 shared-memory transpose with naive, padded and XOR-swizzled LDS
  *     layouts ("CUDA Swizzle & bank conflict", whc-imageprocess.github.io: section
  *     "Case Study / Matrix Transpose").
+ *   - tbl_predict_l2: the offline LRU prediction of an order's L2 hit rate ("CUDA Thread Block
+ *     Swizzle", section "CUDA Thread Block Swizzle Benchmark"), generalised to several private
+ *     caches; host code only.
  *
  * Conventions shared by every entry point:
  *   - Matrices are dense and row-major with no padding: A is M x K, B is K x N, C is M x N.
@@ -127,7 +130,9 @@ int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_
  *                 (TBL_ERR_SHAPE otherwise).
  *   trace         NULL, or device int32[8 * T]: for every tile id t the workgroup that ran it writes
  *                 {program id, iteration of its tile loop, m, n, XCC id, core-clock cycles and
- *                 100 MHz real-time ticks from the tile's first k step to its epilogue, 0}.
+ *                 100 MHz real-time ticks from the tile's start to its epilogue, the start as the
+ *                 low 32 bits of the 100 MHz real-time counter}. A program's first tile starts
+ *                 before its prologue loads, a later tile where the previous tile's k loop ends.
  *                 Caller-owned. Tracing adds a few instructions per tile.
  *   All other arguments as tbl_gemm.
  */
@@ -156,6 +161,33 @@ int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32
  */
 int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t cols, int layout,
                       void* stream);
+
+/*
+ * tbl_predict_l2 -- offline L2 hit-rate prediction for an order (host only, no HIP call; runs on a
+ * machine without a GPU). "CUDA Thread Block Swizzle", section "CUDA Thread Block Swizzle
+ * Benchmark": operand blocks are replayed through a byte-capacity LRU cache. Running tiles are
+ * taken together, and k block by k block each reads its A block (m, k) then its B block (k, n); a
+ * miss inserts the block, then least-recently-used blocks are evicted while the cache holds more
+ * than capacity_bytes and more than one block. Generalised to private caches: program p (tile ids
+ * p, p + P, ..., as the persistent GEMM runs them; one id each when P >= T) replays on cache
+ * p mod num_caches, `resident` programs of a cache at a time, in program order. The page's own
+ * model is num_caches = 1, num_programs = T, resident = its wave size; gfx950's XCD L2s are
+ * num_caches = 8, resident = CUs per XCD x workgroups per CU.
+ *   swizzle_mode, grid_m, grid_n, group_size  as tbl_tile_map (the GEMM's executed order).
+ *   grid_k          k blocks per tile, in [1, 2^20].
+ *   a_block_bytes   bytes of one A block (block_m x block_k elements), >= 1; b_block_bytes likewise.
+ *   capacity_bytes  per cache, >= 0.
+ *   num_caches      in [1, 64].  num_programs  >= 0 (0 = T).  resident  >= 1.
+ *   hits, accesses  host int64 outputs: hits and block reads summed over the caches
+ *                   (accesses = 2 x T x grid_k).
+ * TBL_ERR_SHAPE when 2 x T x grid_k > 2^33 or (grid_m + grid_n) x grid_k > 2^26 (work and host
+ * memory bounds; the call allocates and frees 16 bytes per distinct block). Returns
+ * TBL_WARN_NOT_BIJECTIVE, with results, where tbl_tile_map would.
+ */
+int tbl_predict_l2(int swizzle_mode, int grid_m, int grid_n, int grid_k, int group_size,
+                   int64_t a_block_bytes, int64_t b_block_bytes, int64_t capacity_bytes,
+                   int num_caches, int num_programs, int resident, int64_t* hits,
+                   int64_t* accesses);
 
 /* tbl_gemm_tile_shape -- the tile shape tbl_gemm uses for these sizes (host only, no HIP call). */
 int tbl_gemm_tile_shape(int64_t M, int64_t N, int64_t K, int* block_m, int* block_n, int* block_k);

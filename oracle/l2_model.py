@@ -54,24 +54,34 @@ def _replay(cache, tiles, grid_k, a_bytes, b_bytes):
             cache.access(("B", k, n), b_bytes)
 
 
-def predict_hit_rate(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_bytes, concurrency):
-    """Page 1's model. tile_m / tile_n: the forward table (tile id -> m, n)."""
+def predict_counts(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_bytes, concurrency):
+    """Page 1's model as (hits, accesses). tile_m / tile_n: the forward table (tile id -> m, n)."""
     cache = ByteLRU(capacity_bytes)
     T = len(tile_m)
     for w0 in range(0, T, concurrency):
         wave = list(zip(tile_m[w0:w0 + concurrency].tolist(), tile_n[w0:w0 + concurrency].tolist()))
         _replay(cache, wave, grid_k, a_bytes, b_bytes)
-    return cache.hit_rate_pct()
+    return cache.hits, cache.hits + cache.misses
 
 
-def predict_hit_rate_xcd(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_per_xcd, num_programs,
-                         resident_per_xcd, num_xcds=8):
-    """XCD-aware variant (a reading; see the module docstring).
+def predict_hit_rate(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_bytes, concurrency):
+    """Page 1's model: the predicted hit rate in percent."""
+    return _pct(*predict_counts(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_bytes,
+                                concurrency))
+
+
+def _pct(hits, accesses):
+    return 100.0 * hits / accesses if accesses else 0.0
+
+
+def predict_counts_xcd(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_per_xcd, num_programs,
+                       resident_per_xcd, num_xcds=8):
+    """XCD-aware variant (a reading; see the module docstring), as (hits, accesses) over all XCDs.
 
     Programs p = 0 .. num_programs-1 run tile ids p, p + P, ... (the stride schedule); program p
     runs on XCD p mod num_xcds. Each XCD runs its programs ``resident_per_xcd`` at a time, in
     program order, and its cache sees, for each group of concurrently running programs, the tiles
-    of one loop iteration, k block by k block. Returns the hit rate over all XCDs' accesses.
+    of one loop iteration, k block by k block.
     """
     T = len(tile_m)
     P = num_programs
@@ -90,9 +100,14 @@ def predict_hit_rate_xcd(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_per_
                 _replay(caches[x], [(int(tile_m[t]), int(tile_n[t])) for t in ids], grid_k,
                         a_bytes, b_bytes)
                 it += 1
-    hits = sum(c.hits for c in caches)
-    total = sum(c.hits + c.misses for c in caches)
-    return 100.0 * hits / total if total else 0.0
+    return sum(c.hits for c in caches), sum(c.hits + c.misses for c in caches)
+
+
+def predict_hit_rate_xcd(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_per_xcd, num_programs,
+                         resident_per_xcd, num_xcds=8):
+    """The XCD-aware variant's hit rate in percent over all XCDs' accesses."""
+    return _pct(*predict_counts_xcd(tile_m, tile_n, grid_k, a_bytes, b_bytes, capacity_per_xcd,
+                                    num_programs, resident_per_xcd, num_xcds))
 
 
 def rank_correlation(x, y):

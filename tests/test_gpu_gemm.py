@@ -187,6 +187,13 @@ def test_trace_matches_oracle_schedule(mode, g, persistent, P):
         assert len(set(xcc[p::programs])) == 1, p           # a workgroup never changes XCD
     rr = np.mean(xcc[:min(programs, T)] == np.arange(min(programs, T)) % 8)
     print(f"workgroups on XCD (program mod 8): {rr:.3f}")
+    # timing fields: a program's tiles start in iteration order, each after the previous k loop
+    ticks = tr[:, 6] & 0xFFFFFFFF
+    start = tr[:, 7] & 0xFFFFFFFF
+    assert np.all(ticks > 0)
+    for t in range(T - programs):
+        gap = (start[t + programs] - start[t]) % (1 << 32)
+        assert ticks[t] <= gap < (1 << 31), t
 
 
 RAGGED = [  # (M, N, K, tile): partial tiles at every edge, K tails of 8 .. 24, tiny and single-tile

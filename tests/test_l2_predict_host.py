@@ -1,0 +1,98 @@
+"""tbl_predict_l2 (host code in libtbl.so, no GPU needed) against the oracle's L2 model.
+
+Hit and access counts are integers, so parity is exact. The page's printed predictions are checked
+through the library too, for every order of the printed sweep.
+"""
+
+import numpy as np
+import pytest
+
+import thread_block_lds_amd as tbl
+from conftest import golden_lines
+from oracle import l2_model, tile_maps as tm
+
+
+def _printed_rows():
+    out = []
+    for ln in golden_lines("p1_predicted_l2_hit_rates.txt"):
+        tok = ln.split()
+        if tok[0] != "spearman":
+            out.append((tok[0], int(tok[1]), int(tok[2]), float(tok[3])))
+    return out
+
+
+@pytest.mark.parametrize("name,mode,group,printed", _printed_rows())
+def test_library_reproduces_printed_predictions(name, mode, group, printed):
+    # 8192^3 fp16, 128x128x32 tiles: 64x64 tiles, 256 k blocks of 8 KiB, 64 MB, waves of 168
+    hits, acc, st = tbl.predict_l2(mode, 64, 64, 256, group, 8192, 8192, 64 * 1024 * 1024,
+                                   num_caches=1, num_programs=0, resident=168)
+    assert st == tbl.OK and acc == 2 * 4096 * 256
+    assert abs(100.0 * hits / acc - printed) <= 0.005, (name, 100.0 * hits / acc)
+
+
+@pytest.mark.parametrize("mode,group", [(tm.ROW, 1), (tm.PANEL, 8), (tm.MORTON, 1)])
+def test_library_counts_equal_oracle_on_printed_config(mode, group):
+    m, n = tm.tile_table(mode, 64, 64, group)
+    want = l2_model.predict_counts(m, n, 256, 8192, 8192, 64 * 1024 * 1024, 168)
+    got = tbl.predict_l2(mode, 64, 64, 256, group, 8192, 8192, 64 * 1024 * 1024, 1, 0, 168)[:2]
+    assert got == want
+
+
+def _cases():
+    rng = np.random.default_rng(7)
+    modes = [tm.ROW, tm.COL, tm.PANEL, tm.MORTON, tm.XOR, tm.SERPENTINE]
+    out = []
+    for i in range(24):
+        mode = modes[i % len(modes)] | (tm.XCD_REMAP if i % 4 == 3 else 0)
+        if mode & 0xFF in (tm.MORTON, tm.XOR):
+            gm = gn = int(2 ** rng.integers(1, 5))
+        else:
+            gm, gn = int(rng.integers(1, 19)), int(rng.integers(1, 19))
+        group = int(rng.integers(1, 24))
+        gk = int(rng.integers(1, 9))
+        a_b, b_b = int(rng.choice([16, 24, 64])), int(rng.choice([16, 32, 64]))
+        cap = int(rng.integers(0, 40)) * 16
+        caches = int(rng.choice([1, 2, 3, 8]))
+        programs = int(rng.choice([0, 1, 5, gm * gn, gm * gn + 3, max(1, gm * gn // 3)]))
+        resident = int(rng.integers(1, 9))
+        out.append((mode, gm, gn, gk, group, a_b, b_b, cap, caches, programs, resident))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases())
+def test_library_counts_equal_oracle_xcd_variant(case):
+    mode, gm, gn, gk, group, a_b, b_b, cap, caches, programs, resident = case
+    m, n = tm.tile_table(mode, gm, gn, group)
+    P = programs if programs else gm * gn
+    want = l2_model.predict_counts_xcd(m, n, gk, a_b, b_b, cap, P, resident, num_xcds=caches)
+    hits, acc, _ = tbl.predict_l2(mode, gm, gn, gk, group, a_b, b_b, cap, caches, programs, resident)
+    assert (hits, acc) == want
+    assert acc == 2 * gm * gn * gk
+
+
+def test_not_bijective_order_warns_and_still_predicts():
+    hits, acc, st = tbl.predict_l2(tm.XOR, 6, 6, 2, 1, 8, 8, 1 << 20, 1, 0, 4)
+    assert st == tbl.WARN_NOT_BIJECTIVE and acc == 2 * 36 * 2
+    m, n = tm.tile_table(tm.XOR, 6, 6, 1)
+    assert (hits, acc) == l2_model.predict_counts(m, n, 2, 8, 8, 1 << 20, 4)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(mode=7), tbl.ERR_INVALID_ARG), (dict(mode=tm.PANEL, group=0), tbl.ERR_INVALID_ARG),
+    (dict(grid_m=0), tbl.ERR_SHAPE), (dict(grid_k=0), tbl.ERR_SHAPE),
+    (dict(grid_k=(1 << 20) + 1), tbl.ERR_SHAPE), (dict(a_block_bytes=0), tbl.ERR_INVALID_ARG),
+    (dict(capacity_bytes=-1), tbl.ERR_INVALID_ARG), (dict(num_caches=0), tbl.ERR_INVALID_ARG),
+    (dict(num_caches=65), tbl.ERR_INVALID_ARG), (dict(num_programs=-1), tbl.ERR_INVALID_ARG),
+    (dict(resident=0), tbl.ERR_INVALID_ARG),
+    # work bound: 2 * T * grid_k > 2^33
+    (dict(grid_m=1 << 12, grid_n=1 << 12, grid_k=1 << 10), tbl.ERR_SHAPE),
+    # memory bound: (grid_m + grid_n) * grid_k > 2^26
+    (dict(grid_m=1 << 16, grid_n=1, grid_k=1 << 11), tbl.ERR_SHAPE),
+])
+def test_invalid_arguments(kwargs, status):
+    args = dict(mode=tm.ROW, grid_m=4, grid_n=4, grid_k=2, group=1, a_block_bytes=8, b_block_bytes=8,
+                capacity_bytes=64, num_caches=1, num_programs=0, resident=1)
+    args.update(kwargs)
+    with pytest.raises(tbl.TblError) as e:
+        tbl.predict_l2(**args)
+    assert e.value.status == status

@@ -40,6 +40,10 @@ _EXPORTS = {
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tbl_transpose_i32": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]),
+    "tbl_predict_l2": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
     "tbl_gemm_tile_shape": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                            ctypes.POINTER(ctypes.c_int)]),
@@ -182,6 +186,18 @@ def transpose_i32(x, out=None, layout=T_XOR, stream=None):
     st = lib().tbl_transpose_i32(_ptr(x), _ptr(out), rows, cols, int(layout), _stream(stream))
     _check(st, "tbl_transpose_i32")
     return out
+
+
+def predict_l2(mode, grid_m, grid_n, grid_k, group=1, a_block_bytes=1, b_block_bytes=1,
+               capacity_bytes=0, num_caches=1, num_programs=0, resident=1):
+    """(hits, accesses, status) of the offline L2 replay through tbl_predict_l2 (host only)."""
+    hits, acc = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().tbl_predict_l2(int(mode), int(grid_m), int(grid_n), int(grid_k), int(group),
+                              int(a_block_bytes), int(b_block_bytes), int(capacity_bytes),
+                              int(num_caches), int(num_programs), int(resident), ctypes.byref(hits),
+                              ctypes.byref(acc))
+    _check(st, "tbl_predict_l2", allow_warning=True)
+    return hits.value, acc.value, st
 
 
 def gemm_tile_shape(M, N, K):

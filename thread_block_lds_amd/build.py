@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtbl.so")
-SOURCES = ["api.hip", "gemm.hip", "transpose.hip", "tile_map.hip"]
+SOURCES = ["api.hip", "gemm.hip", "transpose.hip", "tile_map.hip", "l2_predict.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # packed-fp32-ops off: hipcc must not form packed fp32 instructions from scalar float code.
@@ -33,13 +33,14 @@ def _run(cmd, verbose):
 
 
 def build(verbose=False):
-    """Compile every HIP source and link libtbl.so. Always recompiles."""
+    """Compile every source (HIP kernels and host C++, all through hipcc) and link libtbl.so.
+    Always recompiles."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
     jobs = []
     with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         for src in SOURCES:
-            obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+            obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
             cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
             jobs.append(ex.submit(_run, cmd, verbose))

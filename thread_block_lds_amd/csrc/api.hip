@@ -129,7 +129,7 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
 
 extern "C" {
 
-int tbl_version(void) { return 100; }
+int tbl_version(void) { return 101; }
 
 const char* tbl_status_string(int status) {
   switch (status) {
@@ -208,6 +208,27 @@ int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32
   const tbl::TileOrder o = make_order(swizzle_mode, grid_m, grid_n, group_size);
   if (tbl::launch_tile_map(o, tile_m, tile_n, static_cast<hipStream_t>(stream)) != hipSuccess)
     return TBL_ERR_HIP;
+  return bijective_grid(swizzle_mode, grid_m, grid_n) ? TBL_OK : TBL_WARN_NOT_BIJECTIVE;
+}
+
+int tbl_predict_l2(int swizzle_mode, int grid_m, int grid_n, int grid_k, int group_size,
+                   int64_t a_block_bytes, int64_t b_block_bytes, int64_t capacity_bytes,
+                   int num_caches, int num_programs, int resident, int64_t* hits,
+                   int64_t* accesses) {
+  if (hits == nullptr || accesses == nullptr) return TBL_ERR_INVALID_ARG;
+  if (a_block_bytes < 1 || b_block_bytes < 1 || capacity_bytes < 0) return TBL_ERR_INVALID_ARG;
+  if (num_caches < 1 || num_caches > 64 || num_programs < 0 || resident < 1) return TBL_ERR_INVALID_ARG;
+  int rc = check_order(swizzle_mode, grid_m, grid_n, group_size);
+  if (rc != TBL_OK) return rc;
+  if (grid_k < 1 || grid_k > kMaxDim) return TBL_ERR_SHAPE;
+  const int64_t tiles = static_cast<int64_t>(grid_m) * grid_n;
+  // bounded work and memory: at most 2^33 block reads, 2^26 distinct blocks (16 bytes each)
+  if (2 * tiles * grid_k > (int64_t{1} << 33)) return TBL_ERR_SHAPE;
+  if ((static_cast<int64_t>(grid_m) + grid_n) * grid_k > (int64_t{1} << 26)) return TBL_ERR_SHAPE;
+  const tbl::TileOrder o = make_order(swizzle_mode, grid_m, grid_n, group_size);
+  tbl::predict_l2(o, grid_k, a_block_bytes, b_block_bytes, capacity_bytes, num_caches,
+                  num_programs == 0 ? static_cast<int>(tiles) : num_programs, resident, hits,
+                  accesses);
   return bijective_grid(swizzle_mode, grid_m, grid_n) ? TBL_OK : TBL_WARN_NOT_BIJECTIVE;
 }
 

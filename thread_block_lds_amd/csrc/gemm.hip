@@ -362,8 +362,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   // ---- compute cursor ----
   int c_t = blockIdx.x, c_iter = 0, c_m = 0, c_n = 0;
   order_tile(order, c_t, c_m, c_n);
-  // Schedule trace (optional): per tile id, the program, its loop iteration, (m, n), the XCD, and
-  // the core-clock cycles and 100 MHz real-time ticks from the tile's first step to its epilogue.
+  // Schedule trace (optional): per tile id, the program, its loop iteration, (m, n), the XCD, the
+  // core-clock cycles and 100 MHz real-time ticks from the tile's start to its epilogue, and the
+  // start itself (low 32 bits of the real-time counter). A program's first tile starts before its
+  // prologue; a later one when its predecessor's k loop ends.
   uint64_t clk0 = 0, rt0 = 0;
   auto record = [&]() {
     if (trace != nullptr) {
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
       int32_t* rec = trace + kTraceInts * static_cast<size_t>(c_t);
       rec[5] = static_cast<int32_t>(__builtin_readcyclecounter() - clk0);
       rec[6] = static_cast<int32_t>(__builtin_amdgcn_s_memrealtime() - rt0);
-      rec[7] = 0;
+      rec[7] = static_cast<int32_t>(rt0);
     }
   };
   record();

@@ -26,6 +26,11 @@ bool gemm_tile_supported(int bm, int bn, int bk);
 
 hipError_t launch_tile_map(const TileOrder& o, int32_t* tile_m, int32_t* tile_n, hipStream_t s);
 
+// Offline L2 replay of the order's operand-block reads (host only; arguments already validated):
+// writes the hits and accesses summed over num_caches byte-capacity LRU caches.
+void predict_l2(const TileOrder& o, int grid_k, int64_t a_bytes, int64_t b_bytes, int64_t capacity,
+                int num_caches, int num_programs, int resident, int64_t* hits, int64_t* accesses);
+
 hipError_t launch_transpose_i32(const int32_t* in, int32_t* out, int rows, int cols, int layout,
                                 hipStream_t s);
 

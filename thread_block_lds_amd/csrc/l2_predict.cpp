@@ -1,0 +1,126 @@
+// Offline L2 hit-rate prediction for a tile schedule (host code; no HIP call).
+//
+// "CUDA Thread Block Swizzle" (leimao.github.io), section "CUDA Thread Block Swizzle Benchmark",
+// predicts an order's L2 hit rate by replaying the operand blocks that concurrently running tiles
+// read through one byte-capacity LRU cache: tiles run in waves of consecutive tile ids, and within
+// a wave, k block by k block, each tile reads its A block (m, k), then its B block (k, n). A miss
+// inserts the block and evicts least-recently-used blocks while the cache holds more bytes than
+// its capacity and more than one block.
+//
+// gfx950 has eight XCDs with private L2s and dispatches workgroup p to XCD p mod 8, so this
+// generalises the replay: `num_caches` caches, program p on cache p mod num_caches, running tile
+// ids p, p + P, p + 2P, ... (the stride schedule of the persistent kernel; one id per program when
+// P >= T), `resident` programs of a cache at a time in program order. With one cache, P = T and
+// resident = the wave size, this is the page's model exactly. The tile order is the one the GEMM
+// executes (order_tile).
+#include <stdint.h>
+
+#include <vector>
+
+#include "internal.hpp"
+
+namespace tbl {
+namespace {
+
+// An LRU over dense block ids: A block (m, k) is m * grid_k + k, B block (k, n) is
+// (grid_m + n) * grid_k + k. Recency is a doubly linked list threaded through two arrays;
+// head_ is the least recently used block.
+class BlockLru {
+ public:
+  BlockLru(int64_t ids, int64_t a_ids, int64_t a_bytes, int64_t b_bytes, int64_t capacity)
+      : prev_(static_cast<size_t>(ids), kAbsent),
+        next_(static_cast<size_t>(ids), kNone),
+        a_ids_(a_ids),
+        a_bytes_(a_bytes),
+        b_bytes_(b_bytes),
+        capacity_(capacity) {}
+
+  void access(int64_t id) {
+    if (prev_[id] != kAbsent) {
+      ++hits;
+      unlink(id);
+      append(id);
+      return;
+    }
+    ++misses;
+    append(id);
+    ++held_;
+    used_ += bytes(id);
+    while (used_ > capacity_ && held_ > 1) {
+      const int64_t victim = head_;
+      unlink(victim);
+      prev_[victim] = kAbsent;
+      --held_;
+      used_ -= bytes(victim);
+    }
+  }
+
+  int64_t hits = 0;
+  int64_t misses = 0;
+
+ private:
+  static constexpr int64_t kAbsent = -2;  // in prev_: the block is not held
+  static constexpr int64_t kNone = -1;    // list end
+
+  int64_t bytes(int64_t id) const { return id < a_ids_ ? a_bytes_ : b_bytes_; }
+
+  void unlink(int64_t id) {
+    const int64_t p = prev_[id], n = next_[id];
+    if (p == kNone) head_ = n; else next_[p] = n;
+    if (n == kNone) tail_ = p; else prev_[n] = p;
+  }
+
+  void append(int64_t id) {
+    prev_[id] = tail_;
+    next_[id] = kNone;
+    if (tail_ == kNone) head_ = id; else next_[tail_] = id;
+    tail_ = id;
+  }
+
+  std::vector<int64_t> prev_, next_;
+  int64_t a_ids_, a_bytes_, b_bytes_, capacity_;
+  int64_t head_ = kNone, tail_ = kNone;
+  int64_t held_ = 0, used_ = 0;
+};
+
+}  // namespace
+
+void predict_l2(const TileOrder& o, int grid_k, int64_t a_bytes, int64_t b_bytes, int64_t capacity,
+                int num_caches, int num_programs, int resident, int64_t* hits, int64_t* accesses) {
+  const int64_t T = o.tiles, P = num_programs, gk = grid_k;
+  const int64_t a_ids = static_cast<int64_t>(o.grid_m) * gk;
+  const int64_t ids = a_ids + static_cast<int64_t>(o.grid_n) * gk;
+  std::vector<int64_t> am, bn;  // per running tile of a group: its A and B block ids at k = 0
+  *hits = 0;
+  *accesses = 0;
+  for (int c = 0; c < num_caches; ++c) {
+    BlockLru cache(ids, a_ids, a_bytes, b_bytes, capacity);
+    // programs of this cache, in order: c, c + num_caches, ... < P; `resident` of them at a time
+    const int64_t count = P > c ? (P - c + num_caches - 1) / num_caches : 0;
+    for (int64_t g0 = 0; g0 < count; g0 += resident) {
+      const int64_t g1 = g0 + resident < count ? g0 + resident : count;
+      for (int64_t it = 0;; ++it) {
+        am.clear();
+        bn.clear();
+        for (int64_t j = g0; j < g1; ++j) {
+          const int64_t t = c + j * num_caches + it * P;
+          if (t >= T) continue;
+          int m = 0, n = 0;
+          order_tile(o, static_cast<int>(t), m, n);
+          am.push_back(static_cast<int64_t>(m) * gk);
+          bn.push_back(a_ids + static_cast<int64_t>(n) * gk);
+        }
+        if (am.empty()) break;
+        for (int64_t k = 0; k < gk; ++k)
+          for (size_t i = 0; i < am.size(); ++i) {
+            cache.access(am[i] + k);
+            cache.access(bn[i] + k);
+          }
+      }
+    }
+    *hits += cache.hits;
+    *accesses += cache.hits + cache.misses;
+  }
+}
+
+}  // namespace tbl
