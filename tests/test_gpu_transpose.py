@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 LAYOUTS = [tbl.T_NAIVE, tbl.T_PADDED, tbl.T_XOR]
 
 
-@pytest.mark.parametrize("shape", [(64, 64), (64, 128), (192, 320), (1024, 2048), (2048, 1024)])
+@pytest.mark.parametrize("shape", [(64, 64), (64, 128), (192, 320), (128, 448), (1024, 2048), (2048, 1024)])
 def test_transpose_small_and_case_study(shape):
     x = synth.i32_uniform(shape, 11)
     want = oracle_transpose(x)
