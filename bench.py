@@ -21,12 +21,17 @@ Printed: one JSON line with
   roofline     the GEMM kernel: average launch time -> TFLOP/s against the MFMA peak, and its HBM
                traffic per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size);
   transpose    the int32 LDS transpose at 16384 x 16384 per layout: GB/s against 8 TB/s;
+  target_8192  the 8192^3 bf16 persistent GEMM (group-major g8 and serpentine s8, each with and
+               without the XCD remap): TFLOP/s and % of peak of each order (the 70 % target);
   cpu_baseline the fp64 CPU oracle on a sample of output rows of the same product.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-counters] [--no-cpu]
        python bench.py --counter-pass      (one unmeasured GEMM, one cold GEMM per variant, then a
                                             calibration copy)
        python bench.py --transpose-pass    (each transpose layout at 1024x2048 and 16384x16384)
+       python bench.py --page-sweep        (the swizzle page's own 8192^3 128x128x32 sweep: one
+                                            JSON line with TFLOP/s, TCC hit rates, both L2 models
+                                            and the Spearman coefficients)
 """
 
 import argparse
@@ -60,6 +65,13 @@ FLUSH_BYTES = 512 << 20       # > 8 x 4 MB L2 + 256 MB memory-side cache
 COLD_REPS = 10
 TR_SIZE = 16384
 TR_LAYOUTS = [("naive", 0), ("padded", 1), ("xor", 2)]
+C3 = 8192                     # the persistent bf16 workload of the 70 %-of-peak target
+C3_MODES = [("group_major_g8", 2, 8), ("serpentine_s8", 5, 8),
+            ("group_major_g8+remap", 2 | REMAP, 8), ("serpentine_s8+remap", 5 | REMAP, 8)]
+PS = 8192                     # the swizzle page's own sweep: 8192^3 fp16 N(0,1), 128x128x32 tiles
+PS_TILE = (128, 128, 32)
+PS_ORDERS = ([("row", 0, 1), ("col", 1, 1)] + [(f"panel_g{g}", 2, g) for g in (1, 2, 4, 8, 16, 32, 64)]
+             + [("morton", 3, 1), ("xor", 4, 1)])
 PMC_PASSES = (("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("fetch", ["FETCH_SIZE"]),
               ("write", ["WRITE_SIZE"]),
               ("sq", ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
@@ -124,10 +136,10 @@ def transpose_pass():
         del x, out
 
 
-def _run_pmc(counters, tag, tmp):
+def _run_pmc(counters, tag, tmp, pass_flag="--counter-pass"):
     out = os.path.join(tmp, tag)
     cmd = ["rocprofv3", "--pmc", *counters, "-d", out, "-o", tag, "--output-format", "csv", "--",
-           sys.executable, os.path.abspath(__file__), "--counter-pass"]
+           sys.executable, os.path.abspath(__file__), pass_flag]
     subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL, timeout=240,
                    cwd=tmp, env=dict(os.environ, TMPDIR=tmp))
     files = glob.glob(os.path.join(out, "**", "*counter_collection.csv"), recursive=True)
@@ -259,6 +271,165 @@ def time_transpose(tbl, torch, stream, reps=10):
             "layouts": res}
 
 
+def _dev16(bits, torch, dtype):
+    import numpy as np
+    return torch.from_numpy(bits.view(np.int16)).view(dtype).cuda()
+
+
+def _median_ms(torch, stream, launch, reps, evict=None):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        if evict is not None:
+            evict()
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return statistics.median(e0.elapsed_time(e1) for e0, e1 in ev)
+
+
+def target_check(tbl, torch, stream, reps=10):
+    """The 8192^3 bf16 persistent workload: median kernel time of back-to-back launches per order."""
+    from thread_block_lds_amd import synth
+    a, b = synth.gemm_operands(C3, C3, C3, "bf16", "normal", seed=0)
+    ad, bd = _dev16(a, torch, torch.bfloat16), _dev16(b, torch, torch.bfloat16)
+    del a, b
+    c = torch.empty((C3, C3), dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * C3 ** 3
+    res = {}
+    for name, mode, g in C3_MODES:
+        def launch():
+            tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=True, stream=stream.cuda_stream)
+        launch()
+        launch()
+        ms = _median_ms(torch, stream, launch, reps)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2)}
+    best = max(res, key=lambda n: res[n]["tflops"])
+    del ad, bd, c
+    return {"workload": "gemm 8192^3 bf16 N(0,1)/sqrt(K) -> bf16 (fp32 accumulate), 256x256x32 tiles, "
+                        "persistent stride schedule over CUs x occupancy programs",
+            "programs": tbl.default_num_programs(C3, C3, C3, tbl.BF16, persistent=True),
+            "orders": res, "best": best, "best_pct_peak": res[best]["pct_peak"], "target_pct_peak": 70.0}
+
+
+def _page_printed():
+    """The swizzle page's printed sweep (RTX 5080), from the golden fixture, for side-by-side context."""
+    path = os.path.join(ROOT, "tests", "golden", "p1_predicted_l2_hit_rates.txt")
+    out = {}
+    for ln in open(path):
+        tok = ln.split()
+        if not tok or tok[0].startswith("#") or tok[0] == "spearman":
+            continue
+        out[tok[0]] = {"pred_hit_pct": float(tok[3]), "tflops": float(tok[4]),
+                       "tflops_persistent": float(tok[5])}
+    return out
+
+
+def page_sweep_pass():
+    """Run under rocprofv3 --pmc by the parent: one unmeasured GEMM, then per order an eviction and
+    one GEMM, first non-persistent, then persistent."""
+    import torch
+    import thread_block_lds_amd as tbl
+    from thread_block_lds_amd import synth
+    a, b = synth.gemm_operands(PS, PS, PS, "f16", "randn", seed=0)
+    ad, bd = _dev16(a, torch, torch.float16), _dev16(b, torch, torch.float16)
+    c = torch.empty((PS, PS), dtype=torch.float16, device="cuda")
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    tbl.gemm(ad, bd, c, tile=PS_TILE)
+    torch.cuda.synchronize()
+    for pers in (False, True):
+        for _, mode, g in PS_ORDERS:
+            _evict(flush)
+            tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=pers, tile=PS_TILE)
+            torch.cuda.synchronize()
+    print("page sweep pass done", flush=True)
+
+
+def page_sweep(reps=10):
+    """The swizzle page's benchmark sweep on this GPU: 8192^3 fp16 N(0,1), 128x128x32 tiles, 11
+    orders, non-persistent and persistent, cold launches; measured TCC hit rates; the page's
+    one-cache model and the per-XCD model; Spearman coefficients as the page computes them."""
+    hits = None
+    note = None
+    if shutil.which("rocprofv3") is not None:
+        tmp = tempfile.mkdtemp(prefix="tbl_sweep_", dir="/tmp")
+        try:
+            rows = _run_pmc(["TCC_HIT_sum", "TCC_MISS_sum"], "ps", tmp, "--page-sweep-pass")
+            gemm = [r for r in rows if "gemm_kernel" in r["kernel"]][1:]
+            if len(gemm) != 2 * len(PS_ORDERS):
+                raise RuntimeError(f"expected {2 * len(PS_ORDERS)} GEMM dispatches, got {len(gemm)}")
+            hits = [100.0 * r["TCC_HIT_sum"] / max(r["TCC_HIT_sum"] + r["TCC_MISS_sum"], 1.0) for r in gemm]
+        except Exception as e:
+            note = f"{type(e).__name__}: {e}"
+        finally:
+            shutil.rmtree(tmp, ignore_errors=True)
+    else:
+        note = "rocprofv3 not found"
+
+    import torch
+    import thread_block_lds_amd as tbl
+    from thread_block_lds_amd import synth
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    a, b = synth.gemm_operands(PS, PS, PS, "f16", "randn", seed=0)
+    ad, bd = _dev16(a, torch, torch.float16), _dev16(b, torch, torch.float16)
+    del a, b
+    c = torch.empty((PS, PS), dtype=torch.float16, device="cuda")
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    gm = gn = PS // PS_TILE[0]
+    gk = PS // PS_TILE[2]
+    T = gm * gn
+    # measured concurrent capacity: the program count of a persistent launch, read from its trace
+    trace = torch.zeros(8 * T, dtype=torch.int32, device="cuda")
+    tbl.gemm(ad, bd, c, persistent=True, tile=PS_TILE, trace=trace)
+    torch.cuda.synchronize()
+    capacity = int(trace.view(T, 8)[:, 0].max().item()) + 1
+    info = tbl.device_info()
+    xcds, l2 = info["num_xcds"], info["l2_bytes"]
+    block = PS_TILE[0] * PS_TILE[2] * 2
+    flops = 2.0 * PS ** 3
+    printed = _page_printed()
+    out = {}
+    for pi, pers in enumerate((False, True)):
+        for oi, (name, mode, g) in enumerate(PS_ORDERS):
+            def launch():
+                tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=pers, tile=PS_TILE,
+                         stream=stream.cuda_stream)
+            launch()
+            ms = _median_ms(torch, stream, launch, reps, evict=lambda: _evict(flush))
+            key = "persistent" if pers else "nonpersistent"
+            rec = out.setdefault(name, {"mode": mode, "group": g})
+            rec[key] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+            if hits is not None:
+                rec[key]["l2_hit_pct"] = round(hits[pi * len(PS_ORDERS) + oi], 2)
+    for name, mode, g in PS_ORDERS:
+        h, acc, _ = tbl.predict_l2(mode, gm, gn, gk, g, block, block, xcds * l2, num_caches=1,
+                                   num_programs=0, resident=capacity)
+        out[name]["pred_page_model_pct"] = round(100.0 * h / acc, 2)
+        for key, programs in (("nonpersistent", 0), ("persistent", capacity)):
+            h, acc, _ = tbl.predict_l2(mode, gm, gn, gk, g, block, block, l2, num_caches=xcds,
+                                       num_programs=programs, resident=max(1, capacity // xcds))
+            out[name][key]["pred_xcd_model_pct"] = round(100.0 * h / acc, 2)
+        out[name]["page_rtx5080"] = printed.get(name)
+    names = [n for n, _, _ in PS_ORDERS]
+    spear = {}
+    for key in ("nonpersistent", "persistent"):
+        tf = [out[n][key]["tflops"] for n in names]
+        spear[f"page_model_vs_tflops_{key}"] = round(rank_corr([out[n]["pred_page_model_pct"] for n in names], tf), 3)
+        spear[f"xcd_model_vs_tflops_{key}"] = round(rank_corr([out[n][key]["pred_xcd_model_pct"] for n in names], tf), 3)
+        if hits is not None:
+            spear[f"xcd_model_vs_measured_hit_{key}"] = round(rank_corr(
+                [out[n][key]["pred_xcd_model_pct"] for n in names], [out[n][key]["l2_hit_pct"] for n in names]), 3)
+    print(json.dumps({"sweep": "swizzle page benchmark: 8192^3 fp16 N(0,1) -> fp16, 128x128x32 tiles, "
+                               "cold launches (512 MiB eviction read before each)",
+                      "measured_capacity": capacity, "page_model": {"caches": 1, "capacity_bytes": xcds * l2,
+                                                                     "wave": capacity},
+                      "xcd_model": {"caches": xcds, "capacity_bytes": l2, "resident_per_cache": max(1, capacity // xcds)},
+                      "orders": out, "spearman": spear, "counters_note": note}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,7 +439,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counter-pass", action="store_true")
     ap.add_argument("--transpose-pass", action="store_true")
+    ap.add_argument("--page-sweep", action="store_true")
+    ap.add_argument("--page-sweep-pass", action="store_true")
     args = ap.parse_args()
+
+    if args.page_sweep_pass:
+        page_sweep_pass()
+        return
 
     if args.counter_pass:
         counter_pass()
@@ -283,6 +460,9 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         sys.exit("--steps must be >= 1 and --warmup >= 0")
+    if args.page_sweep:
+        page_sweep()
+        return
 
     # counters first, in child processes, before this process touches the GPU
     ctr, ctr_err = (None, "skipped (--no-counters)") if args.no_counters else counters()
@@ -331,6 +511,7 @@ def main():
 
     pred, pred_cfg = predictions(tbl)
     transpose = time_transpose(tbl, torch, stream)
+    target = target_check(tbl, torch, stream)
 
     ms_step = wall * 1e3 / args.steps
     per_mode = {}
@@ -409,6 +590,7 @@ def main():
                      "algorithmic_flops_per_launch": FLOPS,
                      "algorithmic_bytes_per_launch": 2 * (M * K + K * N + M * N)},
         "transpose": transpose,
+        "target_8192": target,
         "counters_note": ctr_err,
     }
     if not args.no_cpu:

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
         for (int r = 0; r < 16; ++r) acc[i][j][r] = z;
   };
 
-  // One 16-deep phase: MFMA q of the phase, then (optionally) direct load q and two operand
+  // One 16-deep phase: MFMA q of the phase, then (on some slots) a direct load and two operand
   // reads for a later phase; the scheduling barrier after each group keeps this interleaving, so
   // the matrix pipe always has an MFMA queued while loads and reads issue, and the reads finish
   // well before the phase that consumes them starts.
@@ -305,6 +305,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   constexpr int kSlots = (TM * TN > kReadSlots ? (TM * TN > kLoads ? TM * TN : kLoads)
                                                : (kReadSlots > kLoads ? kReadSlots : kLoads));
   static_assert(kLoads % 2 == 0, "loads split evenly between the two phases");
+  constexpr int kLoadEvery = kSlots / (kLoads / 2);
   auto phase = [&](const uint4 (&ua)[TM], const uint4 (&ub)[TN], int load0, int rstage, int rs,
                    uint4 (&ra)[TM], uint4 (&rb)[TN]) {
 #pragma unroll
@@ -313,8 +314,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
         const int i = q / TN, j = q % TN;
         acc[i][j] = mfma32x32x16<kBf16>(ub[j], ua[i], acc[i][j]);
       }
-      // half of the step's direct loads, on every other MFMA slot
-      if ((q & 1) == 0 && q / 2 < kLoads / 2) issue_load(load0 + q / 2);
+      // half of the step's direct loads, spread evenly over the phase's MFMA slots so that the
+      // four waves, released together by the barrier, do not queue their loads in one burst
+      if (q % kLoadEvery == 0 && q / kLoadEvery < kLoads / 2) issue_load(load0 + q / kLoadEvery);
       if (2 * q < kReads) read_item(rstage, rs, 2 * q, ra, rb);
       if (2 * q + 1 < kReads) read_item(rstage, rs, 2 * q + 1, ra, rb);
       __builtin_amdgcn_sched_barrier(0);

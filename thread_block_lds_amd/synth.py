@@ -7,6 +7,8 @@ Recipe (per workload):
   * fp16 GEMM operands: uniform on [-1, 1] drawn in fp32, rounded to fp16 (round to nearest even).
   * bf16 GEMM operands: standard normal drawn in fp32, scaled by ``scale`` (1/sqrt(K) for the
     8192^3 workload), rounded to bf16 (round to nearest even on the fp32 bit pattern).
+  * fp16 standard-normal operands, unscaled (the 8192^3, 128 x 128 x 32 sweep of the swizzle
+    page, which draws its inputs from a standard normal): N(0, 1) in fp32, rounded to fp16.
   * int32 transpose input: uniform over the full int32 range.
   * small-integer operands (exactness tests): uniform integers in [lo, hi], exactly representable.
 A matrix's seed is given by the caller; the workloads use seed s for A and s + 1 for B.
@@ -57,7 +59,8 @@ def i32_uniform(shape, seed):
 def gemm_operands(M, N, K, dtype, dist, seed=0):
     """(A bits (M, K), B bits (K, N)) for a GEMM workload; A uses ``seed``, B uses ``seed + 1``.
 
-    dist "uniform": fp16 uniform[-1, 1]; dist "normal": bf16 N(0,1)/sqrt(K) (or fp16 if asked)."""
+    dist "uniform": fp16 uniform[-1, 1]; dist "normal": bf16 N(0,1)/sqrt(K) (or fp16 if asked);
+    dist "randn": fp16 N(0, 1), unscaled."""
     if dist == "uniform":
         if dtype != "f16":
             raise ValueError("uniform[-1,1] inputs are generated in fp16")
@@ -68,5 +71,11 @@ def gemm_operands(M, N, K, dtype, dist, seed=0):
             return bf16_normal((M, K), seed, s), bf16_normal((K, N), seed + 1, s)
         x = _rng(seed).standard_normal((M, K), dtype=np.float32) * np.float32(s)
         y = _rng(seed + 1).standard_normal((K, N), dtype=np.float32) * np.float32(s)
+        return x.astype(np.float16).view(np.uint16), y.astype(np.float16).view(np.uint16)
+    if dist == "randn":
+        if dtype != "f16":
+            raise ValueError("unscaled normal inputs are generated in fp16")
+        x = _rng(seed).standard_normal((M, K), dtype=np.float32)
+        y = _rng(seed + 1).standard_normal((K, N), dtype=np.float32)
         return x.astype(np.float16).view(np.uint16), y.astype(np.float16).view(np.uint16)
     raise ValueError(dist)
