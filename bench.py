@@ -588,7 +588,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": "gemm_kernel<256,256,f16,f16-out>", "kernel_avg_ms": round(kernel_ms, 5),
                      "algorithmic_flops_per_launch": FLOPS,
-                     "algorithmic_bytes_per_launch": 2 * (M * K + K * N + M * N)},
+                     "algorithmic_bytes_per_launch": 2 * (M * K + K * N + M * N),
+                     # counter KiB per true KiB on a 256 MiB device copy; traffic = counters / factor
+                     "traffic_calibration": ({k: round(v, 4) if v else None for k, v in ctr["factors"].items()}
+                                             if ctr else None)},
         "transpose": transpose,
         "target_8192": target,
         "counters_note": ctr_err,
