@@ -29,6 +29,8 @@ Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-counters] [--n
        python bench.py --counter-pass      (one unmeasured GEMM, one cold GEMM per variant, then a
                                             calibration copy)
        python bench.py --transpose-pass    (each transpose layout at 1024x2048 and 16384x16384)
+       python bench.py --lds-sweep         (every LDS operand-layout variant at 4096^3: measured
+                                            bank-conflict cycles against the oracle's prediction)
        python bench.py --page-sweep        (the swizzle page's own 8192^3 128x128x32 sweep: one
                                             JSON line with TFLOP/s, TCC hit rates, both L2 models
                                             and the Spearman coefficients)
@@ -430,6 +432,75 @@ def page_sweep(reps=10):
                       "orders": out, "spearman": spear, "counters_note": note}), flush=True)
 
 
+def _layout_predictions():
+    """The oracle's predicted conflict cycles per layout, from the committed fixture written by
+    tests/golden/make_gemm_lds_conflicts.py."""
+    path = os.path.join(ROOT, "tests", "golden", "gemm_lds_conflicts_4096.txt")
+    out = {}
+    for ln in open(path):
+        tok = ln.split()
+        if tok and not tok[0].startswith("#"):
+            out[tuple(int(x) for x in tok[:5])] = int(tok[7])
+    return out
+
+
+def lds_sweep_pass():
+    """Run under rocprofv3 --pmc by the parent: one unmeasured GEMM, then one 4096^3 GEMM per
+    operand-layout variant."""
+    import torch
+    import thread_block_lds_amd as tbl
+    _, _, ad, bd = _operands()
+    c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    tbl.gemm_lds_layout(ad, bd, tbl.LDS_LAYOUTS[0], c)
+    torch.cuda.synchronize()
+    for layout in tbl.LDS_LAYOUTS:
+        tbl.gemm_lds_layout(ad, bd, layout, c)
+        torch.cuda.synchronize()
+    print("lds sweep pass done", flush=True)
+
+
+def lds_sweep(reps=10):
+    """Every compiled LDS-layout variant at 4096^3 (row order): measured SQ_LDS_BANK_CONFLICT per
+    launch against the oracle's prediction, and the median kernel time."""
+    measured, note = None, None
+    if shutil.which("rocprofv3") is not None:
+        tmp = tempfile.mkdtemp(prefix="tbl_lds_", dir="/tmp")
+        try:
+            rows = _run_pmc(["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS"], "lds", tmp,
+                            "--lds-sweep-pass")
+            gemm = [r for r in rows if "gemm_kernel" in r["kernel"]][1:]
+            measured = [(r["SQ_LDS_BANK_CONFLICT"], r["SQ_LDS_IDX_ACTIVE"], r["SQ_INSTS_LDS"]) for r in gemm]
+        except Exception as e:
+            note = f"{type(e).__name__}: {e}"
+        finally:
+            shutil.rmtree(tmp, ignore_errors=True)
+    else:
+        note = "rocprofv3 not found"
+    import torch
+    import thread_block_lds_amd as tbl
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    _, _, ad, bd = _operands()
+    c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    pred = _layout_predictions()
+    res = []
+    for i, layout in enumerate(tbl.LDS_LAYOUTS):
+        def launch():
+            tbl.gemm_lds_layout(ad, bd, layout, c, stream=stream.cuda_stream)
+        launch()
+        ms = _median_ms(torch, stream, launch, reps)
+        rec = {"layout": dict(zip(("a_per_phase", "a_max_phase", "b_vec", "b_per_phase", "b_max_phase"), layout)),
+               "ms": round(ms, 5), "tflops": round(FLOPS / (ms * 1e-3) / 1e12, 1),
+               "predicted_conflict_cycles": pred.get(tuple(layout))}
+        if measured is not None and len(measured) == len(tbl.LDS_LAYOUTS):
+            conf, active, insts = measured[i]
+            rec.update({"measured_conflict_cycles": int(conf), "lds_active_cycles": int(active),
+                        "lds_instructions": int(insts)})
+        res.append(rec)
+    print(json.dumps({"sweep": "LDS operand layouts of the 256x256x32 fp16 GEMM, 4096^3, row order",
+                      "layouts": res, "counters_note": note}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -441,7 +512,13 @@ def main():
     ap.add_argument("--transpose-pass", action="store_true")
     ap.add_argument("--page-sweep", action="store_true")
     ap.add_argument("--page-sweep-pass", action="store_true")
+    ap.add_argument("--lds-sweep", action="store_true")
+    ap.add_argument("--lds-sweep-pass", action="store_true")
     args = ap.parse_args()
+
+    if args.lds_sweep_pass:
+        lds_sweep_pass()
+        return
 
     if args.page_sweep_pass:
         page_sweep_pass()
@@ -462,6 +539,9 @@ def main():
         sys.exit("--steps must be >= 1 and --warmup >= 0")
     if args.page_sweep:
         page_sweep()
+        return
+    if args.lds_sweep:
+        lds_sweep()
         return
 
     # counters first, in child processes, before this process touches the GPU

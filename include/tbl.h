@@ -8,6 +8,8 @@
  *     kernel with its persistent tile loop in section "CUDA Thread Block Swizzle Benchmark"), plus the
  *     group-major and serpentine orders of the tvm_tirx ClusterPersistentScheduler2D page
  *     (tvm.apache.org: "Tile Ordering", "Serpentine Mode", "Example 1").
+ *   - tbl_gemm_lds_layout: the same GEMM with the operands' LDS swizzles taken from the chunk-XOR
+ *     family of "CUDA Swizzle & bank conflict" (section "Triton - Shared Layout swizzling").
  *   - tbl_tile_map: the program-id -> (m, n) table of any order, computed by the same device code
  *     the GEMM uses.
  *   - tbl_transpose_i32: the int32 shared-memory transpose with naive, padded and XOR-swizzled LDS
@@ -139,6 +141,27 @@ int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_
 int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
                    int swizzle_mode, int group_size, int persistent, int num_programs, int block_m,
                    int block_n, int block_k, int32_t* trace, void* stream);
+
+/*
+ * tbl_gemm_lds_layout -- tbl_gemm on 256x256x32 tiles with chosen LDS swizzles for the operands,
+ * members of the chunk-XOR family of "CUDA Swizzle & bank conflict" (section "Triton - Shared
+ * Layout swizzling"), on 16-byte chunks. A sits in LDS as rows of 32 k (4 chunks): row r stores
+ * logical chunk c at c XOR ((r / a_per_phase) mod a_max_phase). B sits k-major as rows of 256 n
+ * (32 chunks): row k stores chunk c at c XOR ((((k / b_per_phase) mod b_max_phase) * b_vec) mod 32).
+ * The layout changes which LDS banks the operand reads hit, never the result: every variant
+ * returns the same bits as tbl_gemm_tiled with 256x256x32 tiles.
+ *   dtype         TBL_F16 only (TBL_ERR_DTYPE otherwise).
+ *   (a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase) one of the compiled variants:
+ *                 (4,4,4,1,4) the tbl_gemm layouts; A varied with B at its default:
+ *                 (1,1,...) no swizzle, (1,4), (2,4), (4,2), (8,4); B varied with A at its default:
+ *                 (...,1,1,1) no swizzle, (1,1,4), (2,1,4), (4,1,2), (4,2,2), (8,1,4).
+ *                 TBL_ERR_INVALID_ARG for any other combination.
+ *   All other arguments as tbl_gemm (num_programs = 0 resolves as for the 256x256 kernel).
+ */
+int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                        int dtype, int swizzle_mode, int group_size, int persistent, int num_programs,
+                        int a_per_phase, int a_max_phase, int b_vec, int b_per_phase,
+                        int b_max_phase, void* stream);
 
 /*
  * tbl_tile_map -- write the forward table of an order: tile_m[t], tile_n[t] for t in [0, T).

@@ -134,3 +134,65 @@ def transpose_store_passes(M, N, tile, layout, elem_bytes=4, num_banks=32, bank_
         passes += p
         extra += p - ph
     return passes * blocks, extra * blocks
+
+
+# ----------------------------------------------------------------------------- the GEMM's operand reads
+
+def gemm_operand_read_passes(a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase,
+                             tile=256, waves=(2, 2), num_banks=64, bank_bytes=4):
+    """Extra LDS passes of one workgroup's operand reads in one 32-deep k step of the GEMM.
+
+    Layouts: the Triton chunk-XOR family of "CUDA Swizzle & bank conflict" (section "Triton -
+    Shared Layout swizzling") on fp16 data. A is held as rows of 32 k (one per m), swizzled with
+    vec = 8 elements (16 bytes) and (a_per_phase, a_max_phase); B is held k-major as rows of
+    ``tile`` n values, swizzled with vec = 8 * b_vec elements and (b_per_phase, b_max_phase).
+
+    Read instructions (a reading of the hardware, not of the pages; see the bank geometry below):
+      * A: a 16-byte read per lane; for MFMA block q of a wave's 128 rows and k half s, lane l
+        reads row 128 wm + 32 q + (l mod 32) at k = 16 s + 8 (l div 32), the operand layout of the
+        32x32x16 MFMA;
+      * B: a transposing 8-byte read per lane; for block j of a wave's 128 columns, k half s and
+        quarter t, lane r of 16-lane group g reads row k = 16 s + 4 t + 8 (g div 2) + r div 4 at
+        columns 128 wn + 32 j + 16 (g mod 2) + 4 (r mod 4) .. + 3.
+    Bank geometry (gfx950, measured): 64 banks of 4 bytes seen by 8- and 16-byte accesses, which are
+    served in phases of 32 and 16 lanes (the page's model with those constants).
+    Returns (extra passes of all A reads, extra passes of all B reads) per workgroup and k step.
+    """
+    per_wave = tile // 2 if waves == (2, 2) else None
+    if per_wave is None:
+        raise ValueError("2 x 2 waves")
+    b_stage = tile * 32 * 2            # bytes of A in a stage, where B starts
+    extra_a = extra_b = 0
+    for wm in range(waves[0]):
+        for s in range(2):
+            for q in range(per_wave // 32):
+                addrs = []
+                for l in range(64):
+                    row = per_wave * wm + 32 * q + (l % 32)
+                    k0 = 16 * s + 8 * (l // 32)
+                    addrs.append(2 * chunk_xor(row, k0, 32, 8, a_per_phase, a_max_phase))
+                p, ph = instruction_passes(addrs, 16, num_banks, bank_bytes)
+                extra_a += (p - ph) * waves[1]        # every wave of this row reads the same A
+    for wn in range(waves[1]):
+        for s in range(2):
+            for j in range(per_wave // 32):
+                for t in range(2):
+                    addrs = []
+                    for l in range(64):
+                        g, r = l // 16, l % 16
+                        k = 16 * s + 4 * t + 8 * (g // 2) + r // 4
+                        n = per_wave * wn + 32 * j + 16 * (g % 2) + 4 * (r % 4)
+                        addrs.append(b_stage + 2 * chunk_xor(k, n, tile, 8 * b_vec, b_per_phase,
+                                                             b_max_phase))
+                    p, ph = instruction_passes(addrs, 8, num_banks, bank_bytes)
+                    extra_b += (p - ph) * waves[0]
+    return extra_a, extra_b
+
+
+def gemm_lds_conflicts(M, N, K, layout, tile=256):
+    """Predicted LDS bank-conflict cycles (extra passes) of one GEMM launch: every workgroup runs
+    every 32-deep k step of its tiles, with the per-step extra passes of gemm_operand_read_passes."""
+    tiles = -(-M // tile) * -(-N // tile)
+    steps = -(-K // 32)
+    a, b = gemm_operand_read_passes(*layout, tile=tile)
+    return tiles * steps * (a + b)

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(tbl.exported_names()) == declared
-    assert tbl.version() == 101
+    assert tbl.version() == 102
 
 
 def test_status_strings():
@@ -113,3 +113,19 @@ def test_tile_shape_rule_and_default_programs():
     assert tbl.default_num_programs(1, 8, 8, persistent=False) == 1
     with pytest.raises(tbl.TblError):
         tbl.default_num_programs(520, 516, 512)
+
+
+def _layout(layout=(4, 4, 4, 1, 4), dtype=0, M=512, N=512, K=512, A=FAKE, mode=0):
+    return tbl.lib().tbl_gemm_lds_layout(A, FAKE, FAKE, M, N, K, dtype, mode, 1, 0, 0, *layout, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(layout=(3, 4, 4, 1, 4)), tbl.ERR_INVALID_ARG), (dict(layout=(4, 4, 4, 1, 8)), tbl.ERR_INVALID_ARG),
+    (dict(layout=(4, 4, 16, 1, 4)), tbl.ERR_INVALID_ARG), (dict(layout=(0, 0, 0, 0, 0)), tbl.ERR_INVALID_ARG),
+    (dict(dtype=tbl.BF16), tbl.ERR_DTYPE), (dict(dtype=tbl.F16_F32OUT), tbl.ERR_DTYPE), (dict(dtype=7), tbl.ERR_DTYPE),
+    (dict(A=NULL), tbl.ERR_INVALID_ARG), (dict(N=500), tbl.ERR_SHAPE), (dict(A=MISALIGNED), tbl.ERR_ALIGN),
+    (dict(M=768, N=512, mode=tbl.XOR), tbl.ERR_NOT_BIJECTIVE),
+])
+def test_gemm_lds_layout_rejects(kw, want):
+    assert _layout(**kw) == want
+

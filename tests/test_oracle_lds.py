@@ -92,3 +92,38 @@ def test_page_closed_form_naive_transpose():
     assert extra == want["store_conflicts_naive"]
     assert lds.transpose_store_passes(1024, 2048, 32, "padded")[1] == want["store_conflicts_padded"]
     assert lds.transpose_store_passes(1024, 2048, 32, "xor")[1] == want["store_conflicts_xor"]
+
+
+# ---- the GEMM's operand reads under the chunk-XOR family (gfx950 geometry: 64 banks x 4 bytes,
+# 16-byte reads in phases of 16 lanes, 8-byte reads in phases of 32 lanes) ----
+#
+# Hand counts per read instruction, derived from the row pitches alone:
+#   A rows are 64 bytes, so rows r, r+4, r+8, r+12 share one 256-byte bank window. A 16-lane phase
+#   reads 16 consecutive rows at the same logical chunk: unswizzled, 4 rows per window -> 4 passes
+#   instead of 1, i.e. 3 extra per phase, 12 per instruction (4 phases). A phase value that takes
+#   only 2 distinct values among those 4 rows leaves 2 rows per window: 1 extra per phase, 4 per
+#   instruction. Four distinct values: conflict-free.
+#   B rows are 512 bytes, all in the same window position. A 32-lane phase of the transposing read
+#   covers 4 k rows x 64 contiguous bytes: unswizzled, 4 rows on the same 16 banks -> 4 passes per
+#   phase, 3 extra, 6 per instruction (2 phases); 2 distinct 64-byte positions -> 2 per instruction.
+# A workgroup issues 32 A reads and 64 B reads per k step (4 waves x 2 k halves x 4 blocks, B
+# twice: two 4-row quarters per block).
+@pytest.mark.parametrize("layout,want", [
+    ((4, 4, 4, 1, 4), (0, 0)),
+    ((1, 1, 4, 1, 4), (32 * 12, 0)), ((1, 4, 4, 1, 4), (32 * 12, 0)),
+    ((2, 4, 4, 1, 4), (32 * 4, 0)), ((4, 2, 4, 1, 4), (32 * 4, 0)), ((8, 4, 4, 1, 4), (32 * 4, 0)),
+    ((4, 4, 1, 1, 1), (0, 64 * 6)), ((4, 4, 1, 1, 4), (0, 64 * 6)),
+    ((4, 4, 2, 1, 4), (0, 64 * 2)), ((4, 4, 4, 1, 2), (0, 64 * 2)), ((4, 4, 4, 2, 2), (0, 64 * 2)),
+    ((4, 4, 8, 1, 4), (0, 64 * 2)),
+])
+def test_gemm_operand_read_passes_hand_counts(layout, want):
+    assert lds.gemm_operand_read_passes(*layout) == want
+
+
+def test_gemm_lds_conflicts_scales_with_tiles_and_steps():
+    per_step = sum(lds.gemm_operand_read_passes(1, 1, 1, 1, 1))
+    assert per_step == 32 * 12 + 64 * 6
+    assert lds.gemm_lds_conflicts(4096, 4096, 4096, (1, 1, 1, 1, 1)) == 256 * 128 * per_step
+    # partial tiles and a partial k step count as whole ones
+    assert lds.gemm_lds_conflicts(300, 520, 40, (1, 1, 1, 1, 1)) == 2 * 3 * 2 * per_step
+    assert lds.gemm_lds_conflicts(4096, 4096, 4096, (4, 4, 4, 1, 4)) == 0

@@ -36,6 +36,11 @@ _EXPORTS = {
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_void_p]),
+    "tbl_gemm_lds_layout": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "tbl_tile_map": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tbl_transpose_i32": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -155,6 +160,37 @@ def gemm(a, b, c=None, mode=ROW, group=1, persistent=False, num_programs=0, out_
                                   int(bool(persistent)), int(num_programs), int(bm), int(bn), int(bk),
                                   _ptr(trace), s)
         _check(st, "tbl_gemm_tiled")
+    return c
+
+
+# (a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase) of every compiled LDS-layout variant
+LDS_LAYOUTS = [(4, 4, 4, 1, 4), (1, 1, 4, 1, 4), (1, 4, 4, 1, 4), (2, 4, 4, 1, 4), (4, 2, 4, 1, 4),
+               (8, 4, 4, 1, 4), (4, 4, 1, 1, 1), (4, 4, 1, 1, 4), (4, 4, 2, 1, 4), (4, 4, 4, 1, 2),
+               (4, 4, 4, 2, 2), (4, 4, 8, 1, 4)]
+
+
+def gemm_lds_layout(a, b, layout, c=None, mode=ROW, group=1, persistent=False, num_programs=0,
+                    stream=None):
+    """C = A @ B (fp16 in, fp16 out, 256x256x32 tiles) with the LDS swizzles ``layout`` =
+    (a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase) through tbl_gemm_lds_layout."""
+    import torch
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shape mismatch {tuple(a.shape)} x {tuple(b.shape)}")
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("the LDS-layout variants take fp16 A and B")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("A and B must be contiguous row-major")
+    M, K = a.shape
+    N = b.shape[1]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    if c.shape != (M, N) or not c.is_contiguous() or c.dtype != torch.float16:
+        raise ValueError("C must be a contiguous (M, N) fp16 tensor")
+    app, amp, bv, bpp, bmp = (int(x) for x in layout)
+    st = lib().tbl_gemm_lds_layout(_ptr(a), _ptr(b), _ptr(c), M, N, K, F16, int(mode), int(group),
+                                   int(bool(persistent)), int(num_programs), app, amp, bv, bpp, bmp,
+                                   _stream(stream))
+    _check(st, "tbl_gemm_lds_layout")
     return c
 
 

@@ -129,7 +129,7 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
 
 extern "C" {
 
-int tbl_version(void) { return 101; }
+int tbl_version(void) { return 102; }
 
 const char* tbl_status_string(int status) {
   switch (status) {
@@ -175,6 +175,37 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
   a.num_programs = programs;
   a.trace = trace;
   if (tbl::launch_gemm(dtype, block_m, block_n, block_k, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TBL_ERR_HIP;
+  return TBL_OK;
+}
+
+int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                        int dtype, int swizzle_mode, int group_size, int persistent, int num_programs,
+                        int a_per_phase, int a_max_phase, int b_vec, int b_per_phase,
+                        int b_max_phase, void* stream) {
+  int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent, num_programs,
+                         256, 256, 32);
+  if (rc != TBL_OK) return rc;
+  if (dtype != TBL_F16) return TBL_ERR_DTYPE;
+  if (!tbl::gemm_layout_supported(a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase))
+    return TBL_ERR_INVALID_ARG;
+  const int gm = static_cast<int>((M + 255) / 256), gn = static_cast<int>((N + 255) / 256);
+  int programs = 0;
+  rc = resolve_programs(dtype, 256, 256, 32, static_cast<int64_t>(gm) * gn, persistent, num_programs,
+                        &programs);
+  if (rc != TBL_OK) return rc;
+  tbl::GemmLaunch a;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.order = make_order(swizzle_mode, gm, gn, group_size);
+  a.num_programs = programs;
+  a.trace = nullptr;
+  if (tbl::launch_gemm_layout(a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase, a,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
     return TBL_ERR_HIP;
   return TBL_OK;
 }

@@ -1,506 +1,8 @@
-// Tiled GEMM C = A * B for gfx950 with a swizzled, optionally persistent tile schedule.
-//
-// What is computed follows the GEMM kernel of "CUDA Thread Block Swizzle" (leimao.github.io),
-// section "CUDA Thread Block Swizzle Benchmark": workgroup p walks tile ids p, p + P, p + 2P, ...
-// (P = workgroups launched), maps each id to an output tile (m, n) through the selected order, and
-// accumulates that tile in fp32 over k before casting to the output type. The order decides only
-// when a tile is computed, never its value.
-//
-// How it is computed on CDNA4:
-//   * 256 threads = 4 wave64s arranged 2 x 2; each wave owns a (BM/2) x (BN/2) sub-tile made of
-//     32 x 32 MFMA blocks (v_mfma_f32_32x32x16_{f16,bf16}) with fp32 accumulators.
-//   * A workgroup's tiles form one stream of 32-deep k steps (tile after tile). Operands move
-//     global -> LDS with direct-to-LDS 16-byte buffer loads (no registers in between) into five
-//     LDS stages of (BM + BN) x 32 sixteen-bit values, issued three steps ahead of their use, also
-//     across tile boundaries, so the next tile's first steps load during the current epilogue.
-//   * A sits in LDS row-major (one 64-byte row of k per m); B sits k-major as loaded (one row of
-//     BN values per k) and is read transposed by ds_read_b64_tr_b16, which hands each lane the
-//     8 consecutive k of one column that the MFMA B operand wants; no register transposes.
-//   * LDS swizzles (the chunk-XOR idea of "CUDA Swizzle & bank conflict", sections "Hopper TMA 的
-//     swizzling" and "Triton - Shared Layout swizzling", applied to 16-byte chunks and sized to
-//     gfx950's 64 x 4-byte banks): A chunk c of row r is stored at chunk c XOR ((r >> 2) mod 4);
-//     B chunk c of row k at chunk c XOR 4 (k mod 4). The XOR is applied on the global-address side
-//     of the direct loads, whose LDS destinations are fixed (lane l writes bytes 16 l .. 16 l + 15
-//     of its 1 KiB block). Both operand reads then hit 16 (A) or 32 (B) distinct 16-byte bank
-//     groups per service cycle.
-//   * One barrier per step, between its two 16-deep phases; operand reads run one phase ahead of
-//     the MFMAs that consume them.
-//   * The MFMA is issued with B as its first operand, so each lane ends up holding 4 consecutive
-//     output columns of one row and stores them with one 8-byte (16-bit output) or 16-byte (fp32
-//     output) store.
-#include <stdint.h>
-
-#include "internal.hpp"
+// Default-layout GEMM launches (the kernel is in gemm_kernel.hpp): tile shapes 64, 128 and 256,
+// four input/output type combinations, and the occupancy query.
+#include "gemm_kernel.hpp"
 
 namespace tbl {
-namespace {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-constexpr int kThreads = 256;
-constexpr int kBK = 32;          // k depth of one step / LDS stage
-constexpr int kStages = 5;       // LDS stages in flight
-constexpr int kARow = kBK * 2;   // bytes of one A row in LDS: 32 sixteen-bit values = 4 chunks
-constexpr int kTraceInts = 8;    // int32 per tile in the optional schedule trace
-
-template <bool kBf16>
-__device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c) {
-  if constexpr (kBf16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
-                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ uint16_t to_out16(float v, bool bf16) {
-  if (bf16) return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-}
-
-__device__ __forceinline__ int xcc_id() {
-  // HW_REG_XCC_ID (hardware register 20), bits [3:0]: the XCD this wave runs on.
-  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xF;
-}
-
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char_t;
-
-// Raw buffer descriptor over [base, base + bytes): loads past ``bytes`` return zero.
-__device__ __forceinline__ i32x4_t make_desc(const void* base, size_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const unsigned n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<unsigned>(bytes);
-  // The values are wave-uniform; readfirstlane makes that explicit so they live in SGPRs.
-  return i32x4_t{__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<unsigned>(b))),
-                 __builtin_amdgcn_readfirstlane(static_cast<int>((b >> 32) & 0xFFFFu)),
-                 __builtin_amdgcn_readfirstlane(static_cast<int>(n)), 0x00020000};
-}
-
-// 16 bytes per lane from desc + voffset straight into LDS: lane l writes lds_addr + 16 l.
-// Issued as inline asm so that the compiler's wait-count pass, which would otherwise make every
-// later LDS read wait for all direct loads in flight, leaves the waits to the explicit ones below.
-// M0 carries the LDS address; nothing else in this kernel keeps a value in M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void load_to_lds(i32x4_t desc, unsigned lds_addr, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voffset), "s"(desc) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-#define TBL_WAIT_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
-
-// s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this wave are in flight.
-// They retire in issue order on this architecture, so every older one has then completed.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  if constexpr (N == 0) TBL_WAIT_VMCNT(0);
-  else if constexpr (N == 1) TBL_WAIT_VMCNT(1);
-  else if constexpr (N == 2) TBL_WAIT_VMCNT(2);
-  else if constexpr (N == 3) TBL_WAIT_VMCNT(3);
-  else if constexpr (N == 4) TBL_WAIT_VMCNT(4);
-  else if constexpr (N == 5) TBL_WAIT_VMCNT(5);
-  else if constexpr (N == 6) TBL_WAIT_VMCNT(6);
-  else if constexpr (N == 10) TBL_WAIT_VMCNT(10);
-  else if constexpr (N == 12) TBL_WAIT_VMCNT(12);
-  else if constexpr (N == 20) TBL_WAIT_VMCNT(20);
-  else if constexpr (N == 24) TBL_WAIT_VMCNT(24);
-  else static_assert(N < 0, "add this count");
-}
-
-// Workgroup barrier that is also a compiler memory barrier. It first waits for this wave's LDS
-// reads (so no wave reads a stage that another wave refills after the barrier), but not for the
-// direct loads in flight, which __syncthreads() would drain.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ unsigned lds_address(const char* p) {
-  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_char_t*)p));   // generic -> LDS offset
-}
-
-template <int BM, int BN, bool kBf16, bool kF32Out>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restrict__ A,
-                                                        const uint16_t* __restrict__ B,
-                                                        void* __restrict__ Cv, int M, int N, int K,
-                                                        TileOrder order, int num_programs,
-                                                        int32_t* __restrict__ trace) {
-  constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile
-  constexpr int TM = WM / 32, TN = WN / 32;        // 32 x 32 MFMA blocks per wave
-  constexpr int kBRow = BN * 2;                    // bytes of one B row (one k) in LDS
-  constexpr int kAStage = BM * kARow;
-  constexpr int kBStage = kBK * kBRow;
-  constexpr int kStage = kAStage + kBStage;
-  constexpr int kAInst = kAStage / 1024 / 4;       // 1 KiB direct loads per wave per step
-  constexpr int kBInst = kBStage / 1024 / 4;
-  constexpr int kLoads = kAInst + kBInst;
-  constexpr int kBChunks = BN / 8;                 // 16-byte chunks per B row
-  static_assert(kAInst >= 1 && kBInst >= 1, "each wave loads at least one block of A and B");
-  static_assert(kStages == 5, "the wait counts assume four steps in flight");
-
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int nk = (K + kBK - 1) / kBK;
-  const int P = num_programs;
-  if (static_cast<int>(blockIdx.x) >= order.tiles) return;
-  const int my_tiles = (order.tiles - 1 - static_cast<int>(blockIdx.x)) / P + 1;
-  const int total = my_tiles * nk;
-
-  // ---- per-lane constants ----
-  // Direct loads. A block (16 rows of 64 bytes): lane l fills physical chunk l mod 4 of row l / 4,
-  // which holds logical chunk (l mod 4) XOR ((row >> 2) mod 4) = (l mod 4) XOR ((l >> 4) mod 4).
-  // In the last k step of a K that is not a multiple of 32, chunks at k >= K belong to the next
-  // row of A; a_voff_tail points those lanes past the buffer range, so they read zero.
-  constexpr int kOutOfRange = 0x7FFFFFF0;
-  int a_voff[kAInst], a_voff_tail[kAInst];
-  const int a_lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const bool a_tail_ok = a_lane_chunk * 8 + 8 <= K % kBK;
-#pragma unroll
-  for (int j = 0; j < kAInst; ++j) {
-    const int row = (wave * kAInst + j) * 16 + (lane >> 2);
-    a_voff[j] = (row * K + a_lane_chunk * 8) * 2;
-    a_voff_tail[j] = a_tail_ok ? a_voff[j] : kOutOfRange;
-  }
-  // B block (1 KiB of k-major rows of BN values): lane l fills bytes 16 l of the block.
-  int b_voff[kBInst];
-#pragma unroll
-  for (int j = 0; j < kBInst; ++j) {
-    const int o = (wave * kBInst + j) * 1024 + 16 * lane;
-    const int k = o / kBRow;
-    const int chunk = ((o % kBRow) >> 4) ^ ((4 * (k & 3)) & (kBChunks - 1));
-    b_voff[j] = (k * N + chunk * 8) * 2;
-  }
-  // MFMA operand reads. A: lane reads row (lane mod 32) of a 32-row block, logical chunk
-  // 2s + lane / 32 of phase s.
-  int a_rd[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int row = wm * WM + (lane & 31);
-    const int chunk = (2 * s + (lane >> 5)) ^ ((row >> 2) & 3);
-    a_rd[s] = row * kARow + chunk * 16;
-  }
-  // B: within each 16-lane group, lane r points at row k0 + r/4, columns n0 + 4 (r mod 4) .. +3;
-  // the transposing read then gives lane i column n0 + i at rows k0 .. k0 + 3.
-  int b_rd[TN];
-  {
-    const int g = lane >> 4, r = lane & 15;
-    const int k = 8 * (g >> 1) + (r >> 2);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = wn * WN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
-      const int chunk = (n >> 3) ^ ((4 * (k & 3)) & (kBChunks - 1));
-      b_rd[j] = kAStage + k * kBRow + chunk * 16 + (n & 7) * 2;
-    }
-  }
-
-  // ---- load cursor: the next step whose operands go to LDS ----
-  // Every step issues exactly kLoads direct loads; past the end of this workgroup's stream they
-  // read a zero-length buffer (no memory access) into a stage nobody reads again, which keeps the
-  // number of loads in flight, and so every wait count, the same at each step.
-  int ld_t = blockIdx.x, ld_kt = 0, ld_issued = 0, ld_stage = 0;
-  // Running (wave-uniform) positions of the next step's A and B blocks; set with multiplies only
-  // when the cursor enters a new tile, then advanced by additions. Each step's buffer ranges end
-  // at this tile's last row of A that exists (from k0 on) and at B's last row of this step that
-  // exists (k < K); loads past them read zero instead of touching memory. Tile rows past M and
-  // columns past N read values that only reach C elements that are never stored.
-  uint64_t ld_a = 0, ld_b = 0;
-  const unsigned a_step = kBK * 2;                                        // bytes per k step in A
-  const uint64_t b_step = static_cast<uint64_t>(kBK) * static_cast<unsigned>(N) * 2;
-  const unsigned b_row = static_cast<unsigned>(N) * 2;
-  unsigned a_range = 0, b_lead = 0;   // b_lead: n0 * 2, the base's offset into its row
-  auto enter_tile = [&]() {
-    int m, n;
-    order_tile(order, ld_t, m, n);
-    m = __builtin_amdgcn_readfirstlane(m);
-    n = __builtin_amdgcn_readfirstlane(n);
-    const int rows = min(BM, M - m * BM);
-    ld_a = reinterpret_cast<uint64_t>(A) +
-           static_cast<uint64_t>(static_cast<unsigned>(m)) * BM * static_cast<unsigned>(K) * 2;
-    ld_b = reinterpret_cast<uint64_t>(B) + static_cast<uint64_t>(static_cast<unsigned>(n)) * (BN * 2);
-    a_range = static_cast<unsigned>(rows) * static_cast<unsigned>(K) * 2;
-    b_lead = static_cast<unsigned>(n) * (BN * 2);
-  };
-  enter_tile();
-  i32x4_t ld_da, ld_db;
-  unsigned ld_lds = 0;
-  bool ld_tail = false;   // the step being issued is a partial last k step
-  auto prepare_step = [&]() {
-    const bool real = ld_issued < total;
-    const int k_left = K - ld_kt * kBK;
-    const unsigned b_rows = static_cast<unsigned>(k_left < kBK ? k_left : kBK);
-    ld_tail = k_left < kBK;
-    ld_da = make_desc(reinterpret_cast<const void*>(ld_a), real ? a_range : 0u);
-    ld_db = make_desc(reinterpret_cast<const void*>(ld_b), real ? b_rows * b_row - b_lead : 0u);
-    ld_lds = lds_address(lds + ld_stage * kStage);
-  };
-  auto issue_load = [&](int q) {   // q-th of this wave's kLoads loads of the prepared step
-    if (q < kAInst) load_to_lds(ld_da, ld_lds + (wave * kAInst + q) * 1024, ld_tail ? a_voff_tail[q] : a_voff[q]);
-    else load_to_lds(ld_db, ld_lds + kAStage + (wave * kBInst + q - kAInst) * 1024, b_voff[q - kAInst]);
-  };
-  auto advance_load_cursor = [&]() {
-    ++ld_issued;
-    ld_stage = ld_stage == kStages - 1 ? 0 : ld_stage + 1;
-    ld_a += a_step;
-    ld_b += b_step;
-    a_range -= a_step;   // stays positive: the last step starts before the end of K
-    if (++ld_kt == nk) {
-      ld_kt = 0;
-      ld_t += P;
-      if (ld_t < order.tiles) enter_tile();
-    }
-  };
-
-  // ---- operand fragments ----
-  // Read item q of phase s from a stage: items 0 .. TM-1 are A blocks (one 16-byte read each),
-  // items TM .. TM + 2 TN - 1 are halves of B blocks (one transposing 8-byte read each).
-  constexpr int kReads = TM + 2 * TN;
-  auto read_item = [&](int stage, int s, int q, uint4 (&af)[TM], uint4 (&bf)[TN]) {
-    if (q < TM) {
-      af[q] = *reinterpret_cast<const uint4*>(lds + stage * kStage + a_rd[s] + q * 32 * kARow);
-    } else {
-      const int j = (q - TM) >> 1, t = (q - TM) & 1;
-      const char* p = lds + stage * kStage + b_rd[j] + s * 16 * kBRow + t * 4 * kBRow;
-      const uint2 h = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
-      if (t == 0) {
-        bf[j].x = h.x;
-        bf[j].y = h.y;
-      } else {
-        bf[j].z = h.x;
-        bf[j].w = h.y;
-      }
-    }
-  };
-
-  // Accumulators start from a zero the compiler cannot see through: a visible constant zero lets
-  // it peel the first k step (MFMA with a zero addend) and then shuffle accumulators between
-  // register tuples to join the peeled step and the loop.
-  f32x16_t acc[TM][TN];
-  auto zero_acc = [&]() {
-    float z;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = z;
-  };
-
-  // One 16-deep phase: MFMA q of the phase, then (on some slots) a direct load and two operand
-  // reads for a later phase; the scheduling barrier after each group keeps this interleaving, so
-  // the matrix pipe always has an MFMA queued while loads and reads issue, and the reads finish
-  // well before the phase that consumes them starts.
-  constexpr int kReadSlots = (kReads + 1) / 2;
-  constexpr int kSlots = (TM * TN > kReadSlots ? (TM * TN > kLoads ? TM * TN : kLoads)
-                                               : (kReadSlots > kLoads ? kReadSlots : kLoads));
-  static_assert(kLoads % 2 == 0, "loads split evenly between the two phases");
-  constexpr int kLoadEvery = kSlots / (kLoads / 2);
-  auto phase = [&](const uint4 (&ua)[TM], const uint4 (&ub)[TN], int load0, int rstage, int rs,
-                   uint4 (&ra)[TM], uint4 (&rb)[TN]) {
-#pragma unroll
-    for (int q = 0; q < kSlots; ++q) {
-      if (q < TM * TN) {
-        const int i = q / TN, j = q % TN;
-        acc[i][j] = mfma32x32x16<kBf16>(ub[j], ua[i], acc[i][j]);
-      }
-      // half of the step's direct loads, spread evenly over the phase's MFMA slots so that the
-      // four waves, released together by the barrier, do not queue their loads in one burst
-      if (q % kLoadEvery == 0 && q / kLoadEvery < kLoads / 2) issue_load(load0 + q / kLoadEvery);
-      if (2 * q < kReads) read_item(rstage, rs, 2 * q, ra, rb);
-      if (2 * q + 1 < kReads) read_item(rstage, rs, 2 * q + 1, ra, rb);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Lane l holds, for MFMA block (i, j) and group g, row (l mod 32) and columns
-  // 8g + 4*(l div 32) .. +3 of that 32 x 32 block. Accumulators stay in AGPRs until their block is
-  // stored: fp32 stores take AGPR data directly (16 bytes per lane, 32 contiguous bytes per row and
-  // store). The 16-bit path copies one block at a time to VGPRs (an explicit v_accvgpr_read keeps
-  // the compiler from copying all of them up front), packs each group's four values into 8 bytes,
-  // and swaps halves of the wave between groups g and g + 1 (v_permlane32_swap: lanes 32..63 of
-  // the first operand trade places with lanes 0..31 of the second), after which lane l < 32 holds
-  // columns 16p .. 16p + 7 of its row and lane l + 32 columns 16p + 8 .. 16p + 15, for p = g / 2.
-  // Each store then writes 16 bytes per lane and 32 contiguous bytes per row, half as many
-  // stores of twice the width, which the memory system drains several times faster than 8-byte
-  // pieces when every workgroup stores its tile at once.
-  auto epilogue = [&](int tile_m, int tile_n) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const size_t row = static_cast<size_t>(tile_m) * BM + wm * WM + i * 32 + (lane & 31);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const size_t col0 = static_cast<size_t>(tile_n) * BN + wn * WN + j * 32;
-        if constexpr (kF32Out) {
-          float* C = static_cast<float*>(Cv);
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const size_t col = col0 + 8 * g + 4 * (lane >> 5);
-            if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
-            *reinterpret_cast<float4*>(C + row * N + col) =
-                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          }
-        } else {
-          float v[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]) : "memory");
-          uint32_t pk[4][2];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            pk[g][0] = to_out16(v[4 * g], kBf16) | (static_cast<uint32_t>(to_out16(v[4 * g + 1], kBf16)) << 16);
-            pk[g][1] = to_out16(v[4 * g + 2], kBf16) | (static_cast<uint32_t>(to_out16(v[4 * g + 3], kBf16)) << 16);
-          }
-          uint16_t* C = static_cast<uint16_t*>(Cv);
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const auto lo = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
-            const auto hi = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
-            const size_t col = col0 + 16 * p + 8 * (lane >> 5);
-            if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
-            *reinterpret_cast<uint4*>(C + row * N + col) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 block at a time
-      }
-    }
-  };
-
-  // ---- compute cursor ----
-  int c_t = blockIdx.x, c_iter = 0, c_m = 0, c_n = 0;
-  order_tile(order, c_t, c_m, c_n);
-  // Schedule trace (optional): per tile id, the program, its loop iteration, (m, n), the XCD, the
-  // core-clock cycles and 100 MHz real-time ticks from the tile's start to its epilogue, and the
-  // start itself (low 32 bits of the real-time counter). A program's first tile starts before its
-  // prologue; a later one when its predecessor's k loop ends.
-  uint64_t clk0 = 0, rt0 = 0;
-  auto record = [&]() {
-    if (trace != nullptr) {
-      if (tid == 0) {
-        int32_t* rec = trace + kTraceInts * static_cast<size_t>(c_t);
-        rec[0] = blockIdx.x;
-        rec[1] = c_iter;
-        rec[2] = c_m;
-        rec[3] = c_n;
-        rec[4] = xcc_id();
-      }
-      clk0 = __builtin_readcyclecounter();
-      rt0 = __builtin_amdgcn_s_memrealtime();
-    }
-  };
-  auto record_time = [&]() {
-    if (trace != nullptr && tid == 0) {
-      int32_t* rec = trace + kTraceInts * static_cast<size_t>(c_t);
-      rec[5] = static_cast<int32_t>(__builtin_readcyclecounter() - clk0);
-      rec[6] = static_cast<int32_t>(__builtin_amdgcn_s_memrealtime() - rt0);
-      rec[7] = static_cast<int32_t>(rt0);
-    }
-  };
-  record();
-
-  // prologue: kStages - 1 steps in flight; step 0 must have landed everywhere
-#pragma unroll
-  for (int i = 0; i < kStages - 1; ++i) {
-    prepare_step();
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) issue_load(q);
-    advance_load_cursor();
-  }
-  wait_vm<3 * kLoads>();   // step 0 landed; steps 1..3 may still be in flight
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-
-  uint4 af0[TM], bf0[TN], af1[TM], bf1[TN];
-#pragma unroll
-  for (int q = 0; q < kReads; ++q) read_item(0, 0, q, af0, bf0);
-  bool drained = false;   // an epilogue's stores are in flight: the next wait waits for everything
-  int c_stage = 0;
-
-  // Step g: phase 0 multiplies with the operands read during the previous phase, reads phase 1's,
-  // and issues the first half of the loads of step g + 4 into the stage of step g - 1 (free since
-  // the previous barrier: its last reads were issued before it). The barrier certifies step g + 1
-  // in every wave's LDS blocks. Phase 1 multiplies, reads step g + 1's first operands and issues
-  // the second half of step g + 4's loads.
-  for (int tile = 0; tile < my_tiles; ++tile) {
-    zero_acc();
-    for (int kt = 0; kt < nk; ++kt) {
-      prepare_step();
-      phase(af0, bf0, 0, c_stage, 1, af1, bf1);
-      // newer than step g + 1's loads: steps g + 2 and g + 3, and half of step g + 4; after an
-      // epilogue its stores come first, so only the half step just issued may remain
-      if (drained) wait_vm<kLoads / 2>();
-      else wait_vm<2 * kLoads + kLoads / 2>();
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      drained = false;
-      const int next_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
-      phase(af1, bf1, kLoads / 2, next_stage, 0, af0, bf0);
-      advance_load_cursor();
-      c_stage = next_stage;
-    }
-    record_time();
-    epilogue(c_m, c_n);
-    drained = true;
-    c_t += P;
-    ++c_iter;
-    if (c_t < order.tiles) {
-      order_tile(order, c_t, c_m, c_n);
-      record();
-    }
-  }
-}
-
-template <int BM, int BN>
-const void* kernel_for(int dtype) {
-  switch (dtype) {
-    case 0: return reinterpret_cast<const void*>(&gemm_kernel<BM, BN, false, false>);
-    case 1: return reinterpret_cast<const void*>(&gemm_kernel<BM, BN, true, false>);
-    case 2: return reinterpret_cast<const void*>(&gemm_kernel<BM, BN, false, true>);
-    case 3: return reinterpret_cast<const void*>(&gemm_kernel<BM, BN, true, true>);
-    default: return nullptr;
-  }
-}
-
-template <int BM, int BN>
-hipError_t launch(int dtype, const GemmLaunch& a, hipStream_t s) {
-  const dim3 grid(a.num_programs), block(kThreads);
-  const uint16_t* A = static_cast<const uint16_t*>(a.A);
-  const uint16_t* B = static_cast<const uint16_t*>(a.B);
-  switch (dtype) {
-    case 0:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false>), grid, block, 0, s, A, B, a.C, a.M, a.N,
-                         a.K, a.order, a.num_programs, a.trace);
-      break;
-    case 1:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false>), grid, block, 0, s, A, B, a.C, a.M, a.N,
-                         a.K, a.order, a.num_programs, a.trace);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, false, true>), grid, block, 0, s, A, B, a.C, a.M, a.N,
-                         a.K, a.order, a.num_programs, a.trace);
-      break;
-    case 3:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true>), grid, block, 0, s, A, B, a.C, a.M, a.N,
-                         a.K, a.order, a.num_programs, a.trace);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-}  // namespace
-
 bool gemm_tile_supported(int bm, int bn, int bk) {
   return bk == kBK && bm == bn && (bm == 64 || bm == 128 || bm == 256);
 }

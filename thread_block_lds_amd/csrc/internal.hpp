@@ -24,6 +24,12 @@ hipError_t launch_gemm(int dtype, int bm, int bn, int bk, const GemmLaunch& a, h
 hipError_t gemm_blocks_per_cu(int dtype, int bm, int bn, int bk, int* out);
 bool gemm_tile_supported(int bm, int bn, int bk);
 
+// The 256 x 256 x 32 fp16 -> fp16 kernel with the LDS swizzles (A: perPhase, maxPhase; B: vec in
+// 16-byte chunks, perPhase, maxPhase) of one compiled variant; gemm_layout_supported lists them.
+bool gemm_layout_supported(int a_pp, int a_mp, int b_vec, int b_pp, int b_mp);
+hipError_t launch_gemm_layout(int a_pp, int a_mp, int b_vec, int b_pp, int b_mp, const GemmLaunch& a,
+                              hipStream_t s);
+
 hipError_t launch_tile_map(const TileOrder& o, int32_t* tile_m, int32_t* tile_n, hipStream_t s);
 
 // Offline L2 replay of the order's operand-block reads (host only; arguments already validated):
