@@ -68,24 +68,29 @@ def tma_swizzle(y, x, NX, elem_bytes, swizzle_bytes=128):
 
 # ----------------------------------------------------------------------------- bank model
 
-def instruction_passes(byte_addrs, access_bytes, num_banks=32, bank_bytes=4, lanes=None):
+def instruction_passes(byte_addrs, access_bytes, num_banks=32, bank_bytes=4, lanes=None,
+                       lanes_per_phase=None):
     """Passes (wavefronts) one shared-memory instruction needs under the page's bank model.
 
     ``byte_addrs``: start byte address of each active lane, in lane order. Every lane touches
     ``access_bytes`` consecutive bytes, i.e. access_bytes/bank_bytes consecutive words; word w sits
     in bank w mod num_banks. The lanes are served in phases of as many lanes as fill the banks once
-    (num_banks*bank_bytes/access_bytes lanes, at most the lane count). Within a phase, each bank
-    delivers one distinct word per pass and lanes asking for the same word share it, so the phase
-    needs as many passes as the busiest bank has distinct words.
-    Returns (passes, phases); passes - phases is the number of extra (conflict) passes.
+    (num_banks*bank_bytes/access_bytes lanes, at most the lane count), or of ``lanes_per_phase``
+    lanes when given. Within a phase, each bank delivers one distinct word per pass and lanes asking
+    for the same word share it, so the phase needs as many passes as the busiest bank has distinct
+    words; without conflicts a phase needs ceil(lanes x words per lane / num_banks) passes (one,
+    when the phase fills the banks once).
+    Returns (passes, ideal passes); their difference is the number of extra (conflict) passes.
     """
     addrs = np.asarray(byte_addrs, dtype=np.int64)
     if lanes is None:
         lanes = len(addrs)
     words_per_lane = max(1, access_bytes // bank_bytes)
-    lanes_per_phase = max(1, min(lanes, (num_banks * bank_bytes) // access_bytes))
+    if lanes_per_phase is None:
+        lanes_per_phase = (num_banks * bank_bytes) // access_bytes
+    lanes_per_phase = max(1, min(lanes, lanes_per_phase))
     passes = 0
-    phases = 0
+    ideal = 0
     for start in range(0, len(addrs), lanes_per_phase):
         phase = addrs[start:start + lanes_per_phase]
         words = set()
@@ -97,8 +102,8 @@ def instruction_passes(byte_addrs, access_bytes, num_banks=32, bank_bytes=4, lan
         for w in words:
             per_bank[w % num_banks] = per_bank.get(w % num_banks, 0) + 1
         passes += max(per_bank.values())
-        phases += 1
-    return passes, phases
+        ideal += max(1, -(-len(phase) * words_per_lane // num_banks))
+    return passes, ideal
 
 
 def transpose_store_passes(M, N, tile, layout, elem_bytes=4, num_banks=32, bank_bytes=4,
@@ -139,7 +144,7 @@ def transpose_store_passes(M, N, tile, layout, elem_bytes=4, num_banks=32, bank_
 # ----------------------------------------------------------------------------- the GEMM's operand reads
 
 def gemm_operand_read_passes(a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase,
-                             tile=256, waves=(2, 2), num_banks=64, bank_bytes=4):
+                             tile=256, waves=(2, 4), num_banks=64, bank_bytes=4):
     """Extra LDS passes of one workgroup's operand reads in one 32-deep k step of the GEMM.
 
     Layouts: the Triton chunk-XOR family of "CUDA Swizzle & bank conflict" (section "Triton -
@@ -147,52 +152,55 @@ def gemm_operand_read_passes(a_per_phase, a_max_phase, b_vec, b_per_phase, b_max
     vec = 8 elements (16 bytes) and (a_per_phase, a_max_phase); B is held k-major as rows of
     ``tile`` n values, swizzled with vec = 8 * b_vec elements and (b_per_phase, b_max_phase).
 
+    The workgroup's waves form a waves[0] x waves[1] grid over the tile; wave (wm, wn) owns rows
+    wm * tile / waves[0] .. and columns wn * tile / waves[1] .. of it.
     Read instructions (a reading of the hardware, not of the pages; see the bank geometry below):
-      * A: a 16-byte read per lane; for MFMA block q of a wave's 128 rows and k half s, lane l
-        reads row 128 wm + 32 q + (l mod 32) at k = 16 s + 8 (l div 32), the operand layout of the
-        32x32x16 MFMA;
-      * B: a transposing 8-byte read per lane; for block j of a wave's 128 columns, k half s and
+      * A: a 16-byte read per lane; for MFMA block q of a wave's rows and k half s, lane l reads
+        row r0 + 32 q + (l mod 32) at k = 16 s + 8 (l div 32), the operand layout of the 32x32x16
+        MFMA;
+      * B: a transposing 8-byte read per lane; for block j of a wave's columns, k half s and
         quarter t, lane r of 16-lane group g reads row k = 16 s + 4 t + 8 (g div 2) + r div 4 at
-        columns 128 wn + 32 j + 16 (g mod 2) + 4 (r mod 4) .. + 3.
-    Bank geometry (gfx950, measured): 64 banks of 4 bytes seen by 8- and 16-byte accesses, which are
-    served in phases of 32 and 16 lanes (the page's model with those constants).
+        columns n0 + 32 j + 16 (g mod 2) + 4 (r mod 4) .. + 3.
+    Bank geometry (gfx950, measured with SQ_LDS_BANK_CONFLICT on the GEMM itself): 64 banks of 4
+    bytes; both the 8-byte and the 16-byte reads are served in phases of 32 lanes (half a wave),
+    which need 1 and 2 passes without conflicts (the page's model with those constants).
     Returns (extra passes of all A reads, extra passes of all B reads) per workgroup and k step.
     """
-    per_wave = tile // 2 if waves == (2, 2) else None
-    if per_wave is None:
-        raise ValueError("2 x 2 waves")
+    wave_m, wave_n = tile // waves[0], tile // waves[1]
+    if wave_m % 32 or wave_n % 32:
+        raise ValueError("wave sub-tiles must be whole 32 x 32 MFMA blocks")
     b_stage = tile * 32 * 2            # bytes of A in a stage, where B starts
     extra_a = extra_b = 0
     for wm in range(waves[0]):
         for s in range(2):
-            for q in range(per_wave // 32):
+            for q in range(wave_m // 32):
                 addrs = []
                 for l in range(64):
-                    row = per_wave * wm + 32 * q + (l % 32)
+                    row = wave_m * wm + 32 * q + (l % 32)
                     k0 = 16 * s + 8 * (l // 32)
                     addrs.append(2 * chunk_xor(row, k0, 32, 8, a_per_phase, a_max_phase))
-                p, ph = instruction_passes(addrs, 16, num_banks, bank_bytes)
-                extra_a += (p - ph) * waves[1]        # every wave of this row reads the same A
+                p, ideal = instruction_passes(addrs, 16, num_banks, bank_bytes, lanes_per_phase=32)
+                extra_a += (p - ideal) * waves[1]     # every wave of this row reads the same A
     for wn in range(waves[1]):
         for s in range(2):
-            for j in range(per_wave // 32):
+            for j in range(wave_n // 32):
                 for t in range(2):
                     addrs = []
                     for l in range(64):
                         g, r = l // 16, l % 16
                         k = 16 * s + 4 * t + 8 * (g // 2) + r // 4
-                        n = per_wave * wn + 32 * j + 16 * (g % 2) + 4 * (r % 4)
+                        n = wave_n * wn + 32 * j + 16 * (g % 2) + 4 * (r % 4)
                         addrs.append(b_stage + 2 * chunk_xor(k, n, tile, 8 * b_vec, b_per_phase,
                                                              b_max_phase))
-                    p, ph = instruction_passes(addrs, 8, num_banks, bank_bytes)
-                    extra_b += (p - ph) * waves[0]
+                    p, ideal = instruction_passes(addrs, 8, num_banks, bank_bytes, lanes_per_phase=32)
+                    extra_b += (p - ideal) * waves[0]
     return extra_a, extra_b
 
 
-def gemm_lds_conflicts(M, N, K, layout, tile=256):
+def gemm_lds_conflicts(M, N, K, layout, tile=256, waves=(2, 4)):
     """Predicted LDS bank-conflict cycles (extra passes) of one GEMM launch: every workgroup runs
     every 32-deep k step of its tiles, with the per-step extra passes of gemm_operand_read_passes."""
     tiles = -(-M // tile) * -(-N // tile)
     steps = -(-K // 32)
-    a, b = gemm_operand_read_passes(*layout, tile=tile)
+    a, b = gemm_operand_read_passes(*layout, tile=tile, waves=waves)
     return tiles * steps * (a + b)

@@ -83,6 +83,13 @@ def test_broadcast_and_vector_phases():
     assert lds.instruction_passes([8 * lane for lane in range(32)], 8) == (2, 2)
     # 8 lanes of a 128-bit phase reading the same 16-byte column of 8 rows of 128 bytes: 8 passes
     assert lds.instruction_passes([128 * lane for lane in range(8)], 16) == (8, 1)
+    # explicit phase size: 16-byte reads of 64 lanes in two 32-lane phases on 64 banks need at least
+    # 2 passes each; all lanes of a phase in one bank group need one pass per lane
+    assert lds.instruction_passes([16 * lane for lane in range(64)], 16, 64, lanes_per_phase=32) == (4, 4)
+    assert lds.instruction_passes([256 * lane for lane in range(64)], 16, 64, lanes_per_phase=32) == (64, 4)
+    # two lanes per bank group in each phase (rows of 64 bytes, every row at its own chunk offset)
+    rows = [64 * r + 16 * ((r // 4) % 4) for r in range(64)]
+    assert lds.instruction_passes(rows, 16, 64, lanes_per_phase=32) == (4, 4)
 
 
 def test_page_closed_form_naive_transpose():
@@ -95,35 +102,43 @@ def test_page_closed_form_naive_transpose():
 
 
 # ---- the GEMM's operand reads under the chunk-XOR family (gfx950 geometry: 64 banks x 4 bytes,
-# 16-byte reads in phases of 16 lanes, 8-byte reads in phases of 32 lanes) ----
+# 16-byte and 8-byte reads both served in phases of 32 lanes) ----
 #
 # Hand counts per read instruction, derived from the row pitches alone:
-#   A rows are 64 bytes, so rows r, r+4, r+8, r+12 share one 256-byte bank window. A 16-lane phase
-#   reads 16 consecutive rows at the same logical chunk: unswizzled, 4 rows per window -> 4 passes
-#   instead of 1, i.e. 3 extra per phase, 12 per instruction (4 phases). A phase value that takes
-#   only 2 distinct values among those 4 rows leaves 2 rows per window: 1 extra per phase, 4 per
-#   instruction. Four distinct values: conflict-free.
+#   A rows are 64 bytes, so a 256-byte bank window holds 4 rows, and its 16 sixteen-byte bank
+#   groups are group 4 (r mod 4) + (physical chunk). A 32-lane phase reads 32 consecutive rows at
+#   one logical chunk; conflict-free it puts 2 lanes on each group (2 passes). Unswizzled, or with a
+#   phase value that is a function of r mod 4 (perPhase 1, maxPhase 4), only 4 groups are used,
+#   8 lanes each: 8 passes, 6 extra per phase, 12 per instruction (2 phases). A phase value that adds
+#   one bit of information beyond r mod 4 (perPhase 2 or maxPhase 2) uses 8 groups, 4 lanes each:
+#   2 extra per phase, 4 per instruction. Two more bits (perPhase 4 or 8 with maxPhase 4, i.e. bits
+#   2-3 or 3-4 of r): all 16 groups, conflict-free.
 #   B rows are 512 bytes, all in the same window position. A 32-lane phase of the transposing read
 #   covers 4 k rows x 64 contiguous bytes: unswizzled, 4 rows on the same 16 banks -> 4 passes per
 #   phase, 3 extra, 6 per instruction (2 phases); 2 distinct 64-byte positions -> 2 per instruction.
-# A workgroup issues 32 A reads and 64 B reads per k step (4 waves x 2 k halves x 4 blocks, B
-# twice: two 4-row quarters per block).
-@pytest.mark.parametrize("layout,want", [
+HAND = [
     ((4, 4, 4, 1, 4), (0, 0)),
-    ((1, 1, 4, 1, 4), (32 * 12, 0)), ((1, 4, 4, 1, 4), (32 * 12, 0)),
-    ((2, 4, 4, 1, 4), (32 * 4, 0)), ((4, 2, 4, 1, 4), (32 * 4, 0)), ((8, 4, 4, 1, 4), (32 * 4, 0)),
-    ((4, 4, 1, 1, 1), (0, 64 * 6)), ((4, 4, 1, 1, 4), (0, 64 * 6)),
-    ((4, 4, 2, 1, 4), (0, 64 * 2)), ((4, 4, 4, 1, 2), (0, 64 * 2)), ((4, 4, 4, 2, 2), (0, 64 * 2)),
-    ((4, 4, 8, 1, 4), (0, 64 * 2)),
-])
-def test_gemm_operand_read_passes_hand_counts(layout, want):
-    assert lds.gemm_operand_read_passes(*layout) == want
+    ((1, 1, 4, 1, 4), (12, 0)), ((1, 4, 4, 1, 4), (12, 0)),
+    ((2, 4, 4, 1, 4), (4, 0)), ((4, 2, 4, 1, 4), (4, 0)), ((8, 4, 4, 1, 4), (0, 0)),
+    ((4, 4, 1, 1, 1), (0, 6)), ((4, 4, 1, 1, 4), (0, 6)),
+    ((4, 4, 2, 1, 4), (0, 2)), ((4, 4, 4, 1, 2), (0, 2)), ((4, 4, 4, 2, 2), (0, 2)),
+    ((4, 4, 8, 1, 4), (0, 2)),
+]
+
+
+@pytest.mark.parametrize("waves,reads", [((2, 2), (32, 64)), ((2, 4), (64, 64))])
+@pytest.mark.parametrize("layout,per_inst", HAND)
+def test_gemm_operand_read_passes_hand_counts(layout, per_inst, waves, reads):
+    want = (reads[0] * per_inst[0], reads[1] * per_inst[1])
+    assert lds.gemm_operand_read_passes(*layout, waves=waves) == want
 
 
 def test_gemm_lds_conflicts_scales_with_tiles_and_steps():
     per_step = sum(lds.gemm_operand_read_passes(1, 1, 1, 1, 1))
-    assert per_step == 32 * 12 + 64 * 6
+    assert per_step == 64 * 12 + 64 * 6
     assert lds.gemm_lds_conflicts(4096, 4096, 4096, (1, 1, 1, 1, 1)) == 256 * 128 * per_step
     # partial tiles and a partial k step count as whole ones
     assert lds.gemm_lds_conflicts(300, 520, 40, (1, 1, 1, 1, 1)) == 2 * 3 * 2 * per_step
     assert lds.gemm_lds_conflicts(4096, 4096, 4096, (4, 4, 4, 1, 4)) == 0
+    with pytest.raises(ValueError):
+        lds.gemm_operand_read_passes(4, 4, 4, 1, 4, waves=(2, 16))
