@@ -15,6 +15,8 @@
  *   - tbl_transpose_i32: the int32 shared-memory transpose with naive, padded and XOR-swizzled LDS
  *     layouts ("CUDA Swizzle & bank conflict", whc-imageprocess.github.io: section
  *     "Case Study / Matrix Transpose").
+ *   - tbl_mfma_rate: a measurement aid, the GEMM's inner MFMA stream on its own operand data with no
+ *     memory traffic, which gives the matrix-pipe rate the chip sustains for that data.
  *   - tbl_predict_l2: the offline LRU prediction of an order's L2 hit rate ("CUDA Thread Block
  *     Swizzle", section "CUDA Thread Block Swizzle Benchmark"), generalised to several private
  *     caches; host code only.
@@ -211,6 +213,27 @@ int tbl_predict_l2(int swizzle_mode, int grid_m, int grid_n, int grid_k, int gro
                    int64_t a_block_bytes, int64_t b_block_bytes, int64_t capacity_bytes,
                    int num_caches, int num_programs, int resident, int64_t* hits,
                    int64_t* accesses);
+
+/*
+ * tbl_mfma_rate -- the dense matrix-pipe rate the device sustains on given operand data (a
+ * measurement aid for the GEMM's roofline, not part of the method). Each of the 4 waves of each of
+ * ``workgroups`` 256-thread workgroups loads four 16-byte fragments of A and four of B (wave w,
+ * fragment q, lane l takes the 8 values starting at element 8 x (((4 w + q) x 64 + l) mod (elems / 8)))
+ * and then runs ``iters`` rounds of 16 independent 32x32x16 MFMAs (fp32 accumulate) in the GEMM's
+ * issue order, with no other memory traffic. The MFMA count is 16 x iters x 4 x workgroups, each
+ * 2 x 32 x 32 x 16 flops. The chip lowers its core clock as the operands' switching activity
+ * rises, so this rate, not the clock-only figure, bounds what the GEMM can reach on the same data.
+ *   A, B        device pointers to at least ``elems`` 16-bit values each, 16-byte aligned.
+ *   elems       >= 8.
+ *   dtype       TBL_F16 / TBL_F16_F32OUT (fp16 operands) or TBL_BF16 / TBL_BF16_F32OUT (bf16).
+ *   workgroups  in [1, 65536]; iters in [1, 2^24] (TBL_ERR_INVALID_ARG otherwise).
+ *   out         device float[256 x workgroups]: per-lane sums of the accumulators (keeps the work
+ *               observable; the values carry no meaning). Caller-owned.
+ *   cycles      device int64[2]: core-clock cycles and 100 MHz real-time ticks of workgroup 0's
+ *               first wave over its MFMA loop (their ratio is the core clock). Caller-owned.
+ */
+int tbl_mfma_rate(const void* A, const void* B, int64_t elems, int dtype, int workgroups, int iters,
+                  float* out, int64_t* cycles, void* stream);
 
 /* tbl_gemm_tile_shape -- the tile shape tbl_gemm uses for these sizes (host only, no HIP call). */
 int tbl_gemm_tile_shape(int64_t M, int64_t N, int64_t K, int* block_m, int* block_n, int* block_k);

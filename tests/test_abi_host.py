@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(tbl.exported_names()) == declared
-    assert tbl.version() == 102
+    assert tbl.version() == 103
 
 
 def test_status_strings():
@@ -129,3 +129,20 @@ def _layout(layout=(4, 4, 4, 1, 4), dtype=0, M=512, N=512, K=512, A=FAKE, mode=0
 def test_gemm_lds_layout_rejects(kw, want):
     assert _layout(**kw) == want
 
+
+
+def _rate(A=FAKE, B=FAKE, elems=1 << 20, dtype=0, wg=256, iters=100, out=FAKE, cyc=FAKE):
+    return tbl.lib().tbl_mfma_rate(A, B, elems, dtype, wg, iters, out, cyc, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(A=NULL), tbl.ERR_INVALID_ARG), (dict(B=NULL), tbl.ERR_INVALID_ARG),
+    (dict(out=NULL), tbl.ERR_INVALID_ARG), (dict(cyc=NULL), tbl.ERR_INVALID_ARG),
+    (dict(dtype=4), tbl.ERR_DTYPE), (dict(dtype=-1), tbl.ERR_DTYPE),
+    (dict(elems=7), tbl.ERR_INVALID_ARG), (dict(wg=0), tbl.ERR_INVALID_ARG),
+    (dict(wg=65537), tbl.ERR_INVALID_ARG), (dict(iters=0), tbl.ERR_INVALID_ARG),
+    (dict(iters=(1 << 24) + 1), tbl.ERR_INVALID_ARG), (dict(A=MISALIGNED), tbl.ERR_ALIGN),
+    (dict(B=MISALIGNED), tbl.ERR_ALIGN),
+])
+def test_mfma_rate_rejects(kw, want):
+    assert _rate(**kw) == want

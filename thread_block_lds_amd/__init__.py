@@ -49,6 +49,9 @@ _EXPORTS = {
                                       ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
+    "tbl_mfma_rate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]),
     "tbl_gemm_tile_shape": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                            ctypes.POINTER(ctypes.c_int)]),
@@ -192,6 +195,27 @@ def gemm_lds_layout(a, b, layout, c=None, mode=ROW, group=1, persistent=False, n
                                    _stream(stream))
     _check(st, "tbl_gemm_lds_layout")
     return c
+
+
+def mfma_rate(a, b, workgroups=256, iters=4000, stream=None):
+    """Run tbl_mfma_rate on the leading values of fp16/bf16 CUDA tensors ``a`` and ``b`` (the
+    GEMM's own operands). Returns (flops, out, cycles): the flop count of the launch, the float32
+    sink tensor and the int64 device tensor {core-clock cycles, 100 MHz ticks} of the first wave's
+    MFMA loop. The caller times the launch on its stream."""
+    import torch
+    if a.dtype != b.dtype or a.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("a and b must share dtype float16 or bfloat16")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    elems = min(a.numel(), b.numel())
+    out = torch.empty(256 * int(workgroups), dtype=torch.float32, device=a.device)
+    cycles = torch.zeros(2, dtype=torch.int64, device=a.device)
+    dtype = BF16 if a.dtype == torch.bfloat16 else F16
+    st = lib().tbl_mfma_rate(_ptr(a), _ptr(b), elems, dtype, int(workgroups), int(iters), _ptr(out),
+                             _ptr(cycles), _stream(stream))
+    _check(st, "tbl_mfma_rate")
+    flops = 2 * 32 * 32 * 16 * 16 * int(iters) * 4 * int(workgroups)
+    return flops, out, cycles
 
 
 def tile_map(mode, grid_m, grid_n, group=1, out_m=None, out_n=None, device="cuda", stream=None):

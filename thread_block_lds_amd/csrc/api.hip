@@ -129,7 +129,7 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
 
 extern "C" {
 
-int tbl_version(void) { return 102; }
+int tbl_version(void) { return 103; }
 
 const char* tbl_status_string(int status) {
   switch (status) {
@@ -272,6 +272,20 @@ int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t col
   if (!aligned16(in) || !aligned16(out)) return TBL_ERR_ALIGN;
   if (tbl::launch_transpose_i32(in, out, static_cast<int>(rows), static_cast<int>(cols), layout,
                                 static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TBL_ERR_HIP;
+  return TBL_OK;
+}
+
+int tbl_mfma_rate(const void* A, const void* B, int64_t elems, int dtype, int workgroups, int iters,
+                  float* out, int64_t* cycles, void* stream) {
+  if (A == nullptr || B == nullptr || out == nullptr || cycles == nullptr) return TBL_ERR_INVALID_ARG;
+  if (dtype < TBL_F16 || dtype > TBL_BF16_F32OUT) return TBL_ERR_DTYPE;
+  if (elems < 8 || workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 24))
+    return TBL_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B)) return TBL_ERR_ALIGN;
+  const bool bf16 = dtype == TBL_BF16 || dtype == TBL_BF16_F32OUT;
+  if (tbl::launch_mfma_rate(A, B, elems, bf16, workgroups, iters, out, cycles,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
     return TBL_ERR_HIP;
   return TBL_OK;
 }

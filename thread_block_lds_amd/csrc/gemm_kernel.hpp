@@ -145,6 +145,63 @@ __device__ __forceinline__ int swz_b(int k) {
   return (((k / kBPP) % kBMP) * kBV) & (kChunks - 1);
 }
 
+// Store a wave's sub-tile of the output tile (tile_m, tile_n); the wave sits at (wm, wn) in the
+// workgroup's wave grid and holds TM x TN accumulator blocks of 32 x 32.
+// Lane l holds, for MFMA block (i, j) and group g, row (l mod 32) and columns
+// 8g + 4*(l div 32) .. +3 of that 32 x 32 block. Accumulators stay in AGPRs until their block is
+// stored: fp32 stores take AGPR data directly (16 bytes per lane, 32 contiguous bytes per row and
+// store). The 16-bit path copies one block at a time to VGPRs (an explicit v_accvgpr_read keeps
+// the compiler from copying all of them up front), packs each group's four values into 8 bytes,
+// and swaps halves of the wave between groups g and g + 1 (v_permlane32_swap: lanes 32..63 of
+// the first operand trade places with lanes 0..31 of the second), after which lane l < 32 holds
+// columns 16p .. 16p + 7 of its row and lane l + 32 columns 16p + 8 .. 16p + 15, for p = g / 2.
+// Each store then writes 16 bytes per lane and 32 contiguous bytes per row, half as many
+// stores of twice the width, which the memory system drains several times faster than 8-byte
+// pieces when every workgroup stores its tile at once.
+template <int BM, int BN, int WM, int WN, int TM, int TN, bool kBf16, bool kF32Out>
+__device__ __forceinline__ void store_tile(f32x16_t (&acc)[TM][TN], void* __restrict__ Cv, int M, int N,
+                                           int tile_m, int tile_n, int wm, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const size_t row = static_cast<size_t>(tile_m) * BM + wm * WM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const size_t col0 = static_cast<size_t>(tile_n) * BN + wn * WN + j * 32;
+      if constexpr (kF32Out) {
+        float* C = static_cast<float*>(Cv);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const size_t col = col0 + 8 * g + 4 * (lane >> 5);
+          if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
+          *reinterpret_cast<float4*>(C + row * N + col) =
+              make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        }
+      } else {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]) : "memory");
+        uint32_t pk[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          pk[g][0] = to_out16(v[4 * g], kBf16) | (static_cast<uint32_t>(to_out16(v[4 * g + 1], kBf16)) << 16);
+          pk[g][1] = to_out16(v[4 * g + 2], kBf16) | (static_cast<uint32_t>(to_out16(v[4 * g + 3], kBf16)) << 16);
+        }
+        uint16_t* C = static_cast<uint16_t*>(Cv);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const auto lo = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
+          const auto hi = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
+          const size_t col = col0 + 16 * p + 8 * (lane >> 5);
+          if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
+          *reinterpret_cast<uint4*>(C + row * N + col) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 block at a time
+    }
+  }
+}
+
 template <int BM, int BN, bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4,
           int kBPP = 1, int kBMP = 4>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restrict__ A,
@@ -348,57 +405,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
     }
   };
 
-  // Lane l holds, for MFMA block (i, j) and group g, row (l mod 32) and columns
-  // 8g + 4*(l div 32) .. +3 of that 32 x 32 block. Accumulators stay in AGPRs until their block is
-  // stored: fp32 stores take AGPR data directly (16 bytes per lane, 32 contiguous bytes per row and
-  // store). The 16-bit path copies one block at a time to VGPRs (an explicit v_accvgpr_read keeps
-  // the compiler from copying all of them up front), packs each group's four values into 8 bytes,
-  // and swaps halves of the wave between groups g and g + 1 (v_permlane32_swap: lanes 32..63 of
-  // the first operand trade places with lanes 0..31 of the second), after which lane l < 32 holds
-  // columns 16p .. 16p + 7 of its row and lane l + 32 columns 16p + 8 .. 16p + 15, for p = g / 2.
-  // Each store then writes 16 bytes per lane and 32 contiguous bytes per row, half as many
-  // stores of twice the width, which the memory system drains several times faster than 8-byte
-  // pieces when every workgroup stores its tile at once.
   auto epilogue = [&](int tile_m, int tile_n) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const size_t row = static_cast<size_t>(tile_m) * BM + wm * WM + i * 32 + (lane & 31);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const size_t col0 = static_cast<size_t>(tile_n) * BN + wn * WN + j * 32;
-        if constexpr (kF32Out) {
-          float* C = static_cast<float*>(Cv);
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const size_t col = col0 + 8 * g + 4 * (lane >> 5);
-            if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
-            *reinterpret_cast<float4*>(C + row * N + col) =
-                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          }
-        } else {
-          float v[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]) : "memory");
-          uint32_t pk[4][2];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            pk[g][0] = to_out16(v[4 * g], kBf16) | (static_cast<uint32_t>(to_out16(v[4 * g + 1], kBf16)) << 16);
-            pk[g][1] = to_out16(v[4 * g + 2], kBf16) | (static_cast<uint32_t>(to_out16(v[4 * g + 3], kBf16)) << 16);
-          }
-          uint16_t* C = static_cast<uint16_t*>(Cv);
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const auto lo = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0], false, false);
-            const auto hi = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1], false, false);
-            const size_t col = col0 + 16 * p + 8 * (lane >> 5);
-            if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
-            *reinterpret_cast<uint4*>(C + row * N + col) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 block at a time
-      }
-    }
+    store_tile<BM, BN, WM, WN, TM, TN, kBf16, kF32Out>(acc, Cv, M, N, tile_m, tile_n, wm, wn, lane);
   };
 
   // ---- compute cursor ----
@@ -494,16 +502,6 @@ const void* kernel_for(int dtype) {
     case 3: return reinterpret_cast<const void*>(&gemm_kernel<BM, BN, true, true>);
     default: return nullptr;
   }
-}
-
-// One layout variant of the 256 x 256 fp16 -> fp16 kernel.
-template <int kAPP, int kAMP, int kBV, int kBPP, int kBMP>
-hipError_t launch_layout(const GemmLaunch& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<256, 256, false, false, kAPP, kAMP, kBV, kBPP, kBMP>), dim3(a.num_programs),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(a.A),
-                     static_cast<const uint16_t*>(a.B), a.C, a.M, a.N, a.K, a.order, a.num_programs,
-                     a.trace);
-  return hipGetLastError();
 }
 
 template <int BM, int BN>

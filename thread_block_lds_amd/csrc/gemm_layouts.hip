@@ -1,4 +1,4 @@
-// LDS-layout variants of the 256 x 256 fp16 -> fp16 GEMM (kernel in gemm_kernel.hpp).
+// LDS-layout variants of the 256 x 256 fp16 -> fp16 GEMM (kernel in gemm_pp_kernel.hpp).
 //
 // The operand swizzles are members of the chunk-XOR family of "CUDA Swizzle & bank conflict"
 // (section "Triton - Shared Layout swizzling": vec, perPhase, maxPhase), on 16-byte chunks. Each
@@ -6,7 +6,7 @@
 // chunk sits in LDS, never the arithmetic); what changes is how many LDS bank conflicts the operand
 // reads incur. The set compiled here spans no swizzle, partial swizzles and the default for each
 // operand, with the other operand at its default.
-#include "gemm_kernel.hpp"
+#include "gemm_pp_kernel.hpp"
 
 namespace tbl {
 namespace {
@@ -17,18 +17,18 @@ struct LayoutVariant {
 };
 
 constexpr LayoutVariant kVariants[] = {
-    {4, 4, 4, 1, 4, &launch_layout<4, 4, 4, 1, 4>},   // the default layouts
-    {1, 1, 4, 1, 4, &launch_layout<1, 1, 4, 1, 4>},   // A unswizzled
-    {1, 4, 4, 1, 4, &launch_layout<1, 4, 4, 1, 4>},
-    {2, 4, 4, 1, 4, &launch_layout<2, 4, 4, 1, 4>},
-    {4, 2, 4, 1, 4, &launch_layout<4, 2, 4, 1, 4>},
-    {8, 4, 4, 1, 4, &launch_layout<8, 4, 4, 1, 4>},
-    {4, 4, 1, 1, 1, &launch_layout<4, 4, 1, 1, 1>},   // B unswizzled
-    {4, 4, 1, 1, 4, &launch_layout<4, 4, 1, 1, 4>},
-    {4, 4, 2, 1, 4, &launch_layout<4, 4, 2, 1, 4>},
-    {4, 4, 4, 1, 2, &launch_layout<4, 4, 4, 1, 2>},
-    {4, 4, 4, 2, 2, &launch_layout<4, 4, 4, 2, 2>},
-    {4, 4, 8, 1, 4, &launch_layout<4, 4, 8, 1, 4>},
+    {4, 4, 4, 1, 4, &launch_pp_typed<false, false, 4, 4, 4, 1, 4>},   // the default layouts
+    {1, 1, 4, 1, 4, &launch_pp_typed<false, false, 1, 1, 4, 1, 4>},   // A unswizzled
+    {1, 4, 4, 1, 4, &launch_pp_typed<false, false, 1, 4, 4, 1, 4>},
+    {2, 4, 4, 1, 4, &launch_pp_typed<false, false, 2, 4, 4, 1, 4>},
+    {4, 2, 4, 1, 4, &launch_pp_typed<false, false, 4, 2, 4, 1, 4>},
+    {8, 4, 4, 1, 4, &launch_pp_typed<false, false, 8, 4, 4, 1, 4>},
+    {4, 4, 1, 1, 1, &launch_pp_typed<false, false, 4, 4, 1, 1, 1>},   // B unswizzled
+    {4, 4, 1, 1, 4, &launch_pp_typed<false, false, 4, 4, 1, 1, 4>},
+    {4, 4, 2, 1, 4, &launch_pp_typed<false, false, 4, 4, 2, 1, 4>},
+    {4, 4, 4, 1, 2, &launch_pp_typed<false, false, 4, 4, 4, 1, 2>},
+    {4, 4, 4, 2, 2, &launch_pp_typed<false, false, 4, 4, 4, 2, 2>},
+    {4, 4, 8, 1, 4, &launch_pp_typed<false, false, 4, 4, 8, 1, 4>},
 };
 
 const LayoutVariant* find(int a_pp, int a_mp, int b_vec, int b_pp, int b_mp) {

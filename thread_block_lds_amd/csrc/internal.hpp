@@ -37,6 +37,10 @@ hipError_t launch_tile_map(const TileOrder& o, int32_t* tile_m, int32_t* tile_n,
 void predict_l2(const TileOrder& o, int grid_k, int64_t a_bytes, int64_t b_bytes, int64_t capacity,
                 int num_caches, int num_programs, int resident, int64_t* hits, int64_t* accesses);
 
+// The matrix-pipe rate kernel (mfma_rate.hip); arguments already validated.
+hipError_t launch_mfma_rate(const void* A, const void* B, int64_t elems, bool bf16, int workgroups,
+                            int iters, float* out, int64_t* cycles, hipStream_t s);
+
 hipError_t launch_transpose_i32(const int32_t* in, int32_t* out, int rows, int cols, int layout,
                                 hipStream_t s);
 
