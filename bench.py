@@ -278,10 +278,25 @@ def time_transpose(tbl, torch, stream, reps=10):
         ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
         gbs = 8.0 * TR_SIZE * TR_SIZE / (ms * 1e-3) / 1e9
         res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    # context: a plain device copy of the same bytes (torch's copy kernel), what this board's HBM
+    # sustains for one read stream and one write stream
+    for _ in range(2):
+        out.copy_(x)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        out.copy_(x)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
+    copy_gbs = 8.0 * TR_SIZE * TR_SIZE / (copy_ms * 1e-3) / 1e9
+    best = max(res, key=lambda n: res[n]["GB/s"])
     del x, out
     return {"workload": f"int32 {TR_SIZE}x{TR_SIZE} transpose through 64x64 LDS tiles",
             "algorithmic_bytes_per_launch": 8 * TR_SIZE * TR_SIZE, "peak_GB/s": HBM_PEAK_GBS,
-            "layouts": res}
+            "layouts": res,
+            "device_copy_same_bytes": {"GB/s": round(copy_gbs, 1), "frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+                                       "best_layout_frac_of_copy": round(res[best]["GB/s"] / copy_gbs, 4)}}
 
 
 def _dev16(bits, torch, dtype):

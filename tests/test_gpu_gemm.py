@@ -248,3 +248,23 @@ def test_k_tail_does_not_mix_rows():
         got = host64(c)
         assert np.all(np.isfinite(np.delete(got, 1, axis=0))), tile
         assert not np.all(np.isfinite(got[1])), tile
+
+
+@pytest.mark.parametrize("K", [8, 24, 32, 96, 160])
+@pytest.mark.parametrize("tile", [64, 256])
+def test_short_k_streams_across_tiles(K, tile):
+    # one to five k steps per tile: the load stream runs up to four tiles ahead of the compute, so
+    # a program's later tiles load while earlier ones are still computed; every schedule must give
+    # the same bits and the oracle's product
+    M, N = 3 * tile - 5, 3 * tile
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=K + tile)
+    ref = og.gemm(a, b, "f16")
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    base = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_tol(host64(base), ref, K, f32_out=True, what=f"K {K} tile {tile}")
+    for persistent, P in [(0, 1), (0, 2), (1, 4), (0, 9)]:
+        c = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=torch.float32, mode=tm.SERPENTINE,
+                     group=2, persistent=bool(persistent), num_programs=P)
+        torch.cuda.synchronize()
+        assert torch.equal(c, base), (K, tile, persistent, P)
