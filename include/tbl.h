@@ -50,8 +50,8 @@ enum {
   TBL_OK = 0,
   TBL_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, unknown mode/layout, bad group */
   TBL_ERR_DTYPE = -2,         /* unknown dtype code */
-  TBL_ERR_SHAPE = -3,         /* sizes not multiples of the tile, too large, or unsupported tile */
-  TBL_ERR_NOT_BIJECTIVE = -4, /* GEMM with Morton/XOR on a grid that is not a square power of two */
+  TBL_ERR_SHAPE = -3,         /* sizes out of range, unsupported tile, or a cluster that does not tile the grid */
+  TBL_ERR_NOT_BIJECTIVE = -4, /* GEMM with Morton/XOR on a (cluster) grid that is not a square power of two */
   TBL_ERR_HIP = -5,           /* a HIP runtime call failed (no device, launch failure, ...) */
   TBL_ERR_ALIGN = -6,         /* a GEMM or transpose pointer is not 16-byte aligned */
   TBL_WARN_NOT_BIJECTIVE = 1  /* tbl_tile_map wrote the table, but it is not a bijection */
@@ -85,6 +85,13 @@ enum {
  *   t' = (t % 8) * (T8 / 8) + t / 8 for t < T8 = 8 * floor(T / 8) (t' = t otherwise), so that the
  *   workgroups that round-robin dispatch places on one of the 8 XCDs (each with a private L2) walk one
  *   contiguous eighth of the order.
+ * TBL_CLUSTER(cm, cn) may be OR-ed into any mode (1 <= cm, cn <= 16; TBL_CLUSTER(1, 1) is 0): the
+ *   two-level schedule of the tvm_tirx page ("Example 2"). The order walks the (grid_m / cm) x
+ *   (grid_n / cn) grid of cluster tiles: the (remapped) id t has cluster id c = t / (cm cn), which the
+ *   order maps to cluster tile (m_c, n_c) (group / strip width counted in cluster tiles), and rank
+ *   r = t % (cm cn), which picks tile (m_c cm + r % cm, n_c cn + r / cm). cm and cn must divide the
+ *   tile grid (TBL_ERR_SHAPE otherwise); Morton and XOR need a square power-of-two cluster grid.
+ *   With TBL_XCD_REMAP the ids of one cluster are consecutive on one XCD.
  */
 enum {
   TBL_ROW = 0,
@@ -95,6 +102,7 @@ enum {
   TBL_SERPENTINE = 5,
   TBL_XCD_REMAP = 0x100
 };
+#define TBL_CLUSTER(cm, cn) (((((cm) - 1) & 15) << 16) | ((((cn) - 1) & 15) << 20))
 
 /* ---- LDS layouts of the transpose ---------------------------------------------------------- */
 enum {
@@ -112,8 +120,9 @@ enum {
  *                 advances through LDS 32 deep). The tile grid is ceil(M/BM) x ceil(N/BN); edge tiles
  *                 are masked (TBL_ERR_SHAPE for sizes outside these rules).
  *   dtype         TBL_F16, TBL_BF16, TBL_F16_F32OUT or TBL_BF16_F32OUT.
- *   swizzle_mode  a TBL_* order, optionally | TBL_XCD_REMAP. Morton and XOR need a square
- *                 power-of-two tile grid (TBL_ERR_NOT_BIJECTIVE otherwise).
+ *   swizzle_mode  a TBL_* order, optionally | TBL_XCD_REMAP and | TBL_CLUSTER(cm, cn). Morton and
+ *                 XOR need a square power-of-two grid of (cluster) tiles (TBL_ERR_NOT_BIJECTIVE
+ *                 otherwise).
  *   group_size    group (TBL_PANEL) or strip width (TBL_SERPENTINE), >= 1; ignored by other modes.
  *   persistent    0: one workgroup per tile (num_programs defaults to T). 1: num_programs defaults
  *                 to min(T, CUs x resident workgroups per CU).
@@ -167,7 +176,7 @@ int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_
 
 /*
  * tbl_tile_map -- write the forward table of an order: tile_m[t], tile_n[t] for t in [0, T).
- *   swizzle_mode  as tbl_gemm (TBL_XCD_REMAP allowed).
+ *   swizzle_mode  as tbl_gemm (TBL_XCD_REMAP and TBL_CLUSTER allowed).
  *   grid_m, grid_n  the tile grid, each in [1, 2^20], with grid_m * grid_n < 2^31.
  *   group_size    as tbl_gemm (>= 1 for TBL_PANEL / TBL_SERPENTINE).
  *   tile_m, tile_n  device int32[T], caller-owned.

@@ -12,7 +12,8 @@ Sources:
        "Bitwise XOR Swizzle", and the CPU pid-mapping functions plus the kernel's tile loop in the
        benchmark script of section "CUDA Thread Block Swizzle Benchmark".
   [P3] "tvm_tirx ... ClusterPersistentScheduler2D" (tvm.apache.org): "Tile Ordering" (group-major),
-       "Serpentine Mode", and "Example 1: Basic persistent kernel".
+       "Serpentine Mode", "Example 1: Basic persistent kernel" and "Example 2: 2SM GEMM" (the
+       scheduler works on cluster tiles; each CTA of a cluster expands its cluster tile by its rank).
 
 Where the pages are silent or disagree, the reading taken is marked READING below.
 """
@@ -124,17 +125,44 @@ def order(mode, t, gm, gn, group=1):
     raise ValueError(f"unknown mode {mode}")
 
 
-def tile_table(mode_flags, gm, gn, group=1, num_xcds=8):
+def cluster_expand(m_idx, n_idx, rank, cm, cn):
+    """[P3] "Example 2": the tile of the CTA with cluster rank ``rank`` in scheduler tile
+    (m_idx, n_idx) of a cm x cn cluster: cb_m = rank mod cm, cb_n = rank div cm, and the tile is
+    (m_idx * cm + cb_m, n_idx * cn + cb_n)."""
+    return m_idx * cm + rank % cm, n_idx * cn + rank // cm
+
+
+def clustered(mode, t, gm, gn, group, cm, cn):
+    """[P3] two-level schedule.  READING (gfx950 has no thread-block clusters).
+
+    Tile id t plays the CTA index of page 3's Example 2: its cluster id t div (cm*cn) is the
+    scheduler's work index, which ``order`` maps to a scheduler tile (m_idx, n_idx) of the
+    (gm/cm) x (gn/cn) cluster-tile grid, and its rank t mod (cm*cn) picks the tile inside that
+    cluster tile (``cluster_expand``). cm and cn must divide gm and gn.
+    """
+    if gm % cm or gn % cn:
+        raise ValueError("cluster dimensions must divide the tile grid")
+    cs = cm * cn
+    m_idx, n_idx = order(mode, t // cs, gm // cm, gn // cn, group)
+    return cluster_expand(m_idx, n_idx, t % cs, cm, cn)
+
+
+def tile_table(mode_flags, gm, gn, group=1, num_xcds=8, cluster=(1, 1)):
     """Forward table: for every tile id t = 0..T-1, the (m, n) it is mapped to (two int64 arrays).
 
     ``mode_flags`` is a mode id, optionally OR-ed with XCD_REMAP, in which case the id is first
-    permuted by ``xcd_remap`` and the order is applied to the permuted id.
+    permuted by ``xcd_remap`` and the order is applied to the permuted id. ``cluster`` = (cm, cn)
+    applies the order to cluster tiles and expands them (``clustered``); (1, 1) is the plain order.
     """
     T = gm * gn
     t = np.arange(T, dtype=np.int64)
     if mode_flags & XCD_REMAP:
         t = xcd_remap(t, T, num_xcds)
-    m, n = order(mode_flags & 0xFF, t, gm, gn, group)
+    cm, cn = cluster
+    if (cm, cn) == (1, 1):
+        m, n = order(mode_flags & 0xFF, t, gm, gn, group)
+    else:
+        m, n = clustered(mode_flags & 0xFF, t, gm, gn, group, cm, cn)
     return np.asarray(m, dtype=np.int64), np.asarray(n, dtype=np.int64)
 
 

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(tbl.exported_names()) == declared
-    assert tbl.version() == 103
+    assert tbl.version() == 104
 
 
 def test_status_strings():

@@ -104,6 +104,29 @@ def test_schedule_variants_bit_identical(tile):
                 assert torch.equal(c, base), (mode, remap, persistent, P)
 
 
+@pytest.mark.parametrize("tile", [64, 256])
+def test_cluster_orders_bit_identical(tile):
+    # the two-level order only decides which workgroup computes which tile, and when
+    M, N, K = 8 * tile, 4 * tile, 256
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=6)
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    base = tbl.gemm(ad, bd, tile=(tile, tile, 32))
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, tile)
+    check_tol(host64(base)[rows], og.gemm_rows(a, b, "f16", rows), K, what=f"tile {tile}")
+    for mode, g, (cm, cn) in [(tm.ROW, 1, (2, 1)), (tm.PANEL, 2, (2, 2)), (tm.SERPENTINE, 2, (1, 2)),
+                              (tm.MORTON, 1, (2, 1)), (tm.COL, 1, (4, 4))]:
+        for remap in (0, tm.XCD_REMAP):
+            for persistent in (False, True):
+                c = tbl.gemm(ad, bd, tile=(tile, tile, 32), mode=mode | remap | tbl.cluster(cm, cn),
+                             group=g, persistent=persistent)
+                torch.cuda.synchronize()
+                assert torch.equal(c, base), (mode, remap, cm, cn, persistent)
+    # a cluster that does not tile the grid is rejected
+    with pytest.raises(tbl.TblError):
+        tbl.gemm(ad, bd, tile=(tile, tile, 32), mode=tm.ROW | tbl.cluster(3, 1))
+
+
 def test_c2_4096_fp16_orders():
     M = N = K = 4096
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)

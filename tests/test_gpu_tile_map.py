@@ -47,3 +47,35 @@ def test_tables_match_oracle(gm, gn, remap):
 def test_printed_tables_on_gpu(fixture, mode, group, grid):
     m, n, _ = _gpu_table(mode, grid, grid, group)
     assert np.array_equal(tm.inverse_grid(m, n, grid, grid), golden_grid(fixture))
+
+
+CLUSTER_GRIDS = [(8, 8), (16, 16), (32, 32), (40, 24), (12, 18), (64, 64)]
+
+
+@pytest.mark.parametrize("gm,gn", CLUSTER_GRIDS)
+@pytest.mark.parametrize("cm,cn", [(2, 1), (1, 2), (2, 2), (4, 2), (3, 3), (8, 1)])
+def test_cluster_tables_match_oracle(gm, gn, cm, cn):
+    if gm % cm or gn % cn:
+        pytest.skip("cluster does not tile this grid")
+    cgm, cgn = gm // cm, gn // cn
+    for remap in (0, tm.XCD_REMAP):
+        for mode in (tm.ROW, tm.COL, tm.PANEL, tm.MORTON, tm.XOR, tm.SERPENTINE):
+            for g in ([1, 2, 4, 8] if mode in (tm.PANEL, tm.SERPENTINE) else [1]):
+                m, n, st = _gpu_table(mode | remap | tbl.cluster(cm, cn), gm, gn, g)
+                om, on = tm.tile_table(mode | remap, gm, gn, g, cluster=(cm, cn))
+                assert np.array_equal(m, om) and np.array_equal(n, on), (mode, remap, gm, gn, g, cm, cn)
+                if mode in (tm.MORTON, tm.XOR) and not (cgm == cgn and cgm & (cgm - 1) == 0):
+                    assert st == tbl.WARN_NOT_BIJECTIVE
+                else:
+                    assert st == tbl.OK and tm.is_bijective(om, on, gm, gn)
+
+
+def test_page3_example2_on_gpu():
+    # 8 x 4 tiles in 2 x 1 clusters, cluster tiles in row-major order: CTA ids 12 and 13 form the
+    # cluster whose scheduler tile is (1, 2); the page's worked case gives them (2, 2) and (3, 2)
+    m, n, st = _gpu_table(tm.ROW | tbl.cluster(2, 1), 8, 4, 1)
+    assert st == tbl.OK
+    assert (m[12], n[12]) == (2, 2) and (m[13], n[13]) == (3, 2)
+    # and clusters of 2 rows over row-major reproduce the printed group-major 4x4 table
+    m, n, _ = _gpu_table(tm.ROW | tbl.cluster(2, 1), 4, 4, 1)
+    assert np.array_equal(tm.inverse_grid(m, n, 4, 4), golden_grid("p3_group_major_4x4_g2.txt"))

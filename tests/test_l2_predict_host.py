@@ -70,6 +70,59 @@ def test_library_counts_equal_oracle_xcd_variant(case):
     assert acc == 2 * gm * gn * gk
 
 
+def _cluster_cases():
+    rng = np.random.default_rng(11)
+    modes = [tm.ROW, tm.COL, tm.PANEL, tm.MORTON, tm.XOR, tm.SERPENTINE]
+    out = []
+    for i in range(24):
+        mode = modes[i % len(modes)] | (tm.XCD_REMAP if i % 3 == 2 else 0)
+        cm, cn = int(rng.integers(1, 5)), int(rng.integers(1, 4))
+        if mode & 0xFF in (tm.MORTON, tm.XOR):
+            cgm = cgn = int(2 ** rng.integers(1, 4))
+        else:
+            cgm, cgn = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        group = int(rng.integers(1, 10))
+        caches = int(rng.choice([1, 2, 8]))
+        programs = int(rng.choice([0, 3, cgm * cgn * cm * cn + 1]))
+        out.append((mode, cm, cn, cgm * cm, cgn * cn, group, caches, programs, int(rng.integers(1, 6))))
+    return out
+
+
+@pytest.mark.parametrize("case", _cluster_cases())
+def test_library_counts_equal_oracle_cluster_orders(case):
+    # the library evaluates the two-level order with the same code the GEMM runs; the replay only
+    # agrees with the oracle's when every tile id lands where the oracle's table puts it
+    mode, cm, cn, gm, gn, group, caches, programs, resident = case
+    m, n = tm.tile_table(mode, gm, gn, group, cluster=(cm, cn))
+    P = programs if programs else gm * gn
+    want = l2_model.predict_counts_xcd(m, n, 3, 16, 24, 160, P, resident, num_xcds=caches)
+    hits, acc, st = tbl.predict_l2(mode | tbl.cluster(cm, cn), gm, gn, 3, group, 16, 24, 160, caches,
+                                   programs, resident)
+    assert st == tbl.OK
+    assert (hits, acc) == want
+
+
+def test_cluster_arguments():
+    # a cluster that does not tile the grid, and bits above the cluster field
+    with pytest.raises(tbl.TblError) as e:
+        tbl.predict_l2(tm.ROW | tbl.cluster(2, 1), 5, 4, 1, 1, 8, 8, 64, 1, 0, 1)
+    assert e.value.status == tbl.ERR_SHAPE
+    with pytest.raises(tbl.TblError) as e:
+        tbl.predict_l2(tm.ROW | tbl.cluster(1, 3), 4, 4, 1, 1, 8, 8, 64, 1, 0, 1)
+    assert e.value.status == tbl.ERR_SHAPE
+    with pytest.raises(tbl.TblError) as e:
+        tbl.predict_l2(tm.ROW | (1 << 24), 4, 4, 1, 1, 8, 8, 64, 1, 0, 1)
+    assert e.value.status == tbl.ERR_INVALID_ARG
+    # Morton on a 4x4 grid of 2x2 clusters: the cluster grid 2x2 is a square power of two
+    assert tbl.predict_l2(tm.MORTON | tbl.cluster(2, 2), 4, 4, 1, 1, 8, 8, 64, 1, 0, 1)[2] == tbl.OK
+    # ... on a 4x4 grid of 2x1 clusters (a 2x4 cluster grid) it is not
+    assert tbl.predict_l2(tm.MORTON | tbl.cluster(2, 1), 4, 4, 1, 1, 8, 8, 64, 1, 0, 1)[2] == tbl.WARN_NOT_BIJECTIVE
+    with pytest.raises(ValueError):
+        tbl.cluster(0, 1)
+    with pytest.raises(ValueError):
+        tbl.cluster(1, 17)
+
+
 def test_not_bijective_order_warns_and_still_predicts():
     hits, acc, st = tbl.predict_l2(tm.XOR, 6, 6, 2, 1, 8, 8, 1 << 20, 1, 0, 4)
     assert st == tbl.WARN_NOT_BIJECTIVE and acc == 2 * 36 * 2

@@ -3,8 +3,10 @@
 CPU only. Pins used:
   * the four 8x8 tables of "CUDA Thread Block Swizzle" (sections "Linear Swizzle",
     "Grouped 2D Panel Swizzle", "Morton / Z-order Swizzle", "Bitwise XOR Swizzle");
-  * the 4x4 group-major and serpentine tables and "Example 1" (per-cluster work lists, ownership
-    grid, tile sequences of clusters 1 and 2) of the tvm_tirx ClusterPersistentScheduler2D page;
+  * the 4x4 group-major and serpentine tables, "Example 1" (per-cluster work lists, ownership
+    grid, tile sequences of clusters 1 and 2) and "Example 2" (cluster tile -> CTA tile by rank) of
+    the tvm_tirx ClusterPersistentScheduler2D page; clusters of g tile rows over a row-major
+    cluster grid reproduce the printed group-major table;
   * special cases: panel g=1 is row-major, panel g >= grid rows is column-major, serpentine with
     s >= grid columns is row-major, serpentine s=1 is the column boustrophedon;
   * explicit walks (nested loops that place ids one by one) for panel and serpentine;
@@ -199,3 +201,74 @@ def test_program_tiles_cover_every_id_once():
     for T, P in itertools.product((1, 7, 64, 960, 1024), (1, 3, 8, 192, 256, 2000)):
         seen = sorted(t for p in range(P) for t in tm.program_tiles(p, P, T))
         assert seen == list(range(T))
+
+
+# ---- the two-level (cluster) schedule of page 3 ----
+
+def test_page3_example2_cluster_expansion():
+    sec = golden_sections("p3_example2_cluster_expansion.txt")
+    mt, nt, cm, cn, cgm, cgn = (int(v) for v in sec["grid"][1][0].split())
+    assert (mt // cm, nt // cn) == (cgm, cgn)
+    for ln in sec["expand"][1]:
+        lhs, _, rhs = ln.partition(":")
+        tile, rank = lhs.split()
+        mi, ni = (int(v) for v in tile.split(","))
+        want = tuple(int(v) for v in rhs.split(","))
+        assert tm.cluster_expand(mi, ni, int(rank), cm, cn) == want
+    # the same through the full map: the CTA index t = cluster * CLUSTER_SIZE + rank of a cluster
+    # whose work index the scheduler maps to tile (1, 2) (row-major over the 4 x 4 cluster grid: 6)
+    m, n = tm.tile_table(tm.ROW, mt, nt, cluster=(cm, cn))
+    assert (m[6 * 2], n[6 * 2]) == (2, 2) and (m[6 * 2 + 1], n[6 * 2 + 1]) == (3, 2)
+
+
+def test_clusters_of_rows_over_row_major_are_group_major():
+    # clusters of g tile rows handed out in row-major order walk g rows column by column: page 3's
+    # group-major order, whose 4x4 table the page prints
+    m, n = tm.tile_table(tm.ROW, 4, 4, cluster=(2, 1))
+    assert np.array_equal(tm.inverse_grid(m, n, 4, 4), golden_grid("p3_group_major_4x4_g2.txt"))
+    for gm, gn, g in [(8, 8, 4), (12, 5, 3), (16, 16, 8), (6, 9, 2)]:
+        assert np.array_equal(np.stack(tm.tile_table(tm.ROW, gm, gn, cluster=(g, 1))),
+                              np.stack(tm.tile_table(tm.PANEL, gm, gn, g)))
+
+
+@pytest.mark.parametrize("mode,group", [(tm.ROW, 1), (tm.COL, 1), (tm.PANEL, 2), (tm.PANEL, 3),
+                                        (tm.SERPENTINE, 2), (tm.MORTON, 1), (tm.XOR, 1)])
+def test_unit_clusters_are_the_plain_order(mode, group):
+    for gm, gn in [(4, 4), (8, 8), (6, 10), (16, 16)]:
+        if mode in (tm.MORTON, tm.XOR) and gm != gn:
+            continue
+        for flags in (mode, mode | tm.XCD_REMAP):
+            assert np.array_equal(np.stack(tm.tile_table(flags, gm, gn, group, cluster=(1, 1))),
+                                  np.stack(tm.tile_table(flags, gm, gn, group)))
+            assert np.array_equal(np.stack(tm.tile_table(flags, gm, gn, group, cluster=(1, 1))),
+                                  np.stack(tm.clustered(mode, tm.xcd_remap(np.arange(gm * gn), gm * gn)
+                                                        if flags & tm.XCD_REMAP else np.arange(gm * gn),
+                                                        gm, gn, group, 1, 1)))
+
+
+@pytest.mark.parametrize("cm,cn", [(2, 1), (1, 2), (2, 2), (4, 2), (3, 1)])
+@pytest.mark.parametrize("mode,group", [(tm.ROW, 1), (tm.COL, 1), (tm.PANEL, 2), (tm.SERPENTINE, 3),
+                                        (tm.MORTON, 1), (tm.XOR, 1)])
+def test_clustered_orders_bijective_and_blockwise(mode, group, cm, cn):
+    for cgm, cgn in [(4, 4), (8, 8), (5, 7), (16, 16)]:
+        if mode in (tm.MORTON, tm.XOR) and (cgm != cgn or cgm & (cgm - 1)):
+            continue
+        gm, gn = cgm * cm, cgn * cn
+        for flags in (mode, mode | tm.XCD_REMAP):
+            m, n = tm.tile_table(flags, gm, gn, group, cluster=(cm, cn))
+            assert tm.is_bijective(m, n, gm, gn)
+            # without the remap, every run of cm*cn consecutive ids covers one aligned cluster block,
+            # rank r at offset (r mod cm, r div cm)
+            if flags & tm.XCD_REMAP:
+                continue
+            cs = cm * cn
+            for c in range(gm * gn // cs):
+                mm, nn = m[c * cs:(c + 1) * cs], n[c * cs:(c + 1) * cs]
+                assert np.all(mm // cm == mm[0] // cm) and np.all(nn // cn == nn[0] // cn)
+                assert np.array_equal(mm % cm, np.arange(cs) % cm)
+                assert np.array_equal(nn % cn, np.arange(cs) // cm)
+
+
+def test_clustered_rejects_partial_clusters():
+    with pytest.raises(ValueError):
+        tm.clustered(tm.ROW, np.arange(15), 5, 3, 1, 2, 1)

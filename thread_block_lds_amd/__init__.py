@@ -24,6 +24,15 @@ WARN_NOT_BIJECTIVE = 1
 F16, BF16, F16_F32OUT, BF16_F32OUT = 0, 1, 2, 3
 ROW, COL, PANEL, MORTON, XOR, SERPENTINE = 0, 1, 2, 3, 4, 5
 XCD_REMAP = 0x100
+
+
+def cluster(cm, cn):
+    """Swizzle-mode bits of a cm x cn cluster (1 <= cm, cn <= 16), OR-ed into a mode: the order then
+    walks cluster tiles and the cm*cn consecutive ids of a cluster expand its cluster tile."""
+    if not (1 <= cm <= 16 and 1 <= cn <= 16):
+        raise ValueError("cluster dimensions must be in [1, 16]")
+    return ((cm - 1) << 16) | ((cn - 1) << 20)
+
 T_NAIVE, T_PADDED, T_XOR = 0, 1, 2
 
 _EXPORTS = {

@@ -51,30 +51,42 @@ int device_info(DeviceInfo* out) {
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Cluster dimensions encoded in bits 16..19 (cm - 1) and 20..23 (cn - 1) of a swizzle mode.
+int cluster_m(int swizzle_mode) { return ((swizzle_mode >> 16) & 15) + 1; }
+int cluster_n(int swizzle_mode) { return ((swizzle_mode >> 20) & 15) + 1; }
+
 int check_order(int swizzle_mode, int64_t gm, int64_t gn, int group) {
   const int mode = swizzle_mode & 0xFF;
-  if ((swizzle_mode & ~(0xFF | TBL_XCD_REMAP)) != 0) return TBL_ERR_INVALID_ARG;
+  if ((swizzle_mode & ~(0xFF | TBL_XCD_REMAP | 0xFF0000)) != 0) return TBL_ERR_INVALID_ARG;
   if (mode < TBL_ROW || mode > TBL_SERPENTINE) return TBL_ERR_INVALID_ARG;
   if ((mode == TBL_PANEL || mode == TBL_SERPENTINE) && group < 1) return TBL_ERR_INVALID_ARG;
   if (gm < 1 || gn < 1 || gm > kMaxDim || gn > kMaxDim || gm * gn > INT32_MAX) return TBL_ERR_SHAPE;
+  // a cluster of cm x cn tiles must tile the grid exactly
+  if (gm % cluster_m(swizzle_mode) || gn % cluster_n(swizzle_mode)) return TBL_ERR_SHAPE;
   return TBL_OK;
 }
 
+// Morton and XOR are bijections only on square power-of-two grids (of cluster tiles, when
+// clustered).
 bool bijective_grid(int swizzle_mode, int64_t gm, int64_t gn) {
   const int mode = swizzle_mode & 0xFF;
   if (mode != TBL_MORTON && mode != TBL_XOR) return true;
+  gm /= cluster_m(swizzle_mode);
+  gn /= cluster_n(swizzle_mode);
   return gm == gn && is_pow2(gm);
 }
 
 tbl::TileOrder make_order(int swizzle_mode, int gm, int gn, int group) {
   const int mode = swizzle_mode & 0xFF;
-  // A panel group taller than the grid, or a serpentine strip wider than it, orders the tiles
+  const int cm = cluster_m(swizzle_mode), cn = cluster_n(swizzle_mode);
+  const int cgm = gm / cm, cgn = gn / cn;   // the grid the order walks
+  // A panel group taller than that grid, or a serpentine strip wider than it, orders the tiles
   // exactly as one of the grid's own height / width does; clamping keeps the device arithmetic in
   // 32 bits.
   int g = 1;
-  if (mode == TBL_PANEL) g = group < gm ? group : gm;
-  else if (mode == TBL_SERPENTINE) g = group < gn ? group : gn;
-  return tbl::make_tile_order(mode, (swizzle_mode & TBL_XCD_REMAP) ? 1 : 0, gm, gn, g);
+  if (mode == TBL_PANEL) g = group < cgm ? group : cgm;
+  else if (mode == TBL_SERPENTINE) g = group < cgn ? group : cgn;
+  return tbl::make_tile_order(mode, (swizzle_mode & TBL_XCD_REMAP) ? 1 : 0, cgm, cgn, g, cm, cn);
 }
 
 void tile_rule(int64_t M, int64_t N, int* bm, int* bn, int* bk) {
@@ -129,7 +141,7 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
 
 extern "C" {
 
-int tbl_version(void) { return 103; }
+int tbl_version(void) { return 104; }
 
 const char* tbl_status_string(int status) {
   switch (status) {

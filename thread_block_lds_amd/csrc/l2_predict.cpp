@@ -88,8 +88,9 @@ class BlockLru {
 void predict_l2(const TileOrder& o, int grid_k, int64_t a_bytes, int64_t b_bytes, int64_t capacity,
                 int num_caches, int num_programs, int resident, int64_t* hits, int64_t* accesses) {
   const int64_t T = o.tiles, P = num_programs, gk = grid_k;
-  const int64_t a_ids = static_cast<int64_t>(o.grid_m) * gk;
-  const int64_t ids = a_ids + static_cast<int64_t>(o.grid_n) * gk;
+  // the output-tile grid (the order may walk a grid of cluster tiles)
+  const int64_t a_ids = static_cast<int64_t>(o.grid_m) * o.cm * gk;
+  const int64_t ids = a_ids + static_cast<int64_t>(o.grid_n) * o.cn * gk;
   std::vector<int64_t> am, bn;  // per running tile of a group: its A and B block ids at k = 0
   *hits = 0;
   *accesses = 0;

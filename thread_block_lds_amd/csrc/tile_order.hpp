@@ -5,8 +5,11 @@
 // "Grouped 2D Panel Swizzle", "Morton / Z-order Swizzle", "Bitwise XOR Swizzle" and the pid-mapping
 // functions of its benchmark script; group-major and serpentine follow the tvm_tirx
 // ClusterPersistentScheduler2D page ("Tile Ordering", "Serpentine Mode"). The serpentine order is
-// the column-strip reading that reproduces that page's 4x4 table. The XCD remap is this library's
-// addition for gfx950's eight private L2s.
+// the column-strip reading that reproduces that page's 4x4 table. The two-level (cluster) form
+// follows that page's "Example 2": an order walks a grid of cluster tiles of cm x cn tiles, and the
+// cm * cn consecutive ids of one cluster expand its cluster tile by their rank. The XCD remap is this
+// library's addition for gfx950's eight private L2s; applied before the cluster split, it places a
+// cluster's ids on one XCD.
 //
 // All quantities are wave-uniform, so in the GEMM they live in scalar registers. Every division is
 // by a launch constant whose reciprocal the host computes once (FastDiv), so a division costs a
@@ -48,10 +51,14 @@ __host__ __device__ inline unsigned fmod_(unsigned n, FastDiv f) { return n - fd
 struct TileOrder {
   int mode;      // kRow .. kSerpentine
   int remap;     // 1: apply the XCD remap before the order
-  int grid_m;    // tile rows
-  int grid_n;    // tile columns
+  int grid_m;    // rows of the grid the order walks (cluster tiles when clustered)
+  int grid_n;    // its columns
   int group;     // panel group / serpentine strip width, clamped by the host to [1, grid]
-  int tiles;     // grid_m * grid_n
+  int tiles;     // output tiles: grid_m * grid_n * cluster size
+  int cm;        // cluster rows (1: no clusters)
+  int cn;        // cluster columns
+  FastDiv div_cs;        // cm * cn
+  FastDiv div_cm;        // cm
   FastDiv div_m;         // grid_m
   FastDiv div_n;         // grid_n
   FastDiv div_span;      // panel: group * grid_n ids per group; serpentine: group * grid_m per strip
@@ -78,7 +85,10 @@ __host__ __device__ inline unsigned compact_even_bits(unsigned x) {
 }
 
 __host__ __device__ inline void order_tile(const TileOrder& o, int t_in, int& m, int& n) {
-  const unsigned t = static_cast<unsigned>(o.remap ? xcd_remap(t_in, o.tiles) : t_in);
+  const unsigned tr = static_cast<unsigned>(o.remap ? xcd_remap(t_in, o.tiles) : t_in);
+  // cluster id and rank (identity when the cluster is one tile)
+  const unsigned t = fdiv(tr, o.div_cs);
+  const unsigned rank = tr - t * o.div_cs.d;
   switch (o.mode) {
     case kRow: {
       const unsigned q = fdiv(t, o.div_n);
@@ -125,17 +135,27 @@ __host__ __device__ inline void order_tile(const TileOrder& o, int t_in, int& m,
       break;
     }
   }
+  if (o.div_cs.d > 1) {
+    const unsigned cb_n = fdiv(rank, o.div_cm);
+    m = m * o.cm + static_cast<int>(rank - cb_n * o.div_cm.d);
+    n = n * o.cn + static_cast<int>(cb_n);
+  }
 }
 
-// Host: the complete order description for a launch (group already clamped to the grid).
-inline TileOrder make_tile_order(int mode, int remap, int gm, int gn, int group) {
+// Host: the complete order description for a launch. gm x gn is the grid the order walks (the
+// cluster-tile grid when cm * cn > 1); the group is already clamped to it.
+inline TileOrder make_tile_order(int mode, int remap, int gm, int gn, int group, int cm = 1, int cn = 1) {
   TileOrder o;
   o.mode = mode;
   o.remap = remap;
   o.grid_m = gm;
   o.grid_n = gn;
   o.group = group;
-  o.tiles = gm * gn;
+  o.tiles = gm * gn * cm * cn;
+  o.cm = cm;
+  o.cn = cn;
+  o.div_cs = make_fastdiv(static_cast<unsigned>(cm * cn));
+  o.div_cm = make_fastdiv(static_cast<unsigned>(cm));
   o.div_m = make_fastdiv(static_cast<unsigned>(gm));
   o.div_n = make_fastdiv(static_cast<unsigned>(gn));
   if (mode == kPanel) {
