@@ -1,5 +1,6 @@
-// The GEMM kernel template, shared by the default-layout launches (gemm.hip) and the LDS-layout
-// variants (gemm_layouts.hip).
+// The four-wave GEMM kernel template (64 x 64 and 128 x 128 tiles; launched from gemm.hip) and
+// the helpers it shares with the eight-wave 256 x 256 kernel of gemm_pp_kernel.hpp: direct-to-LDS
+// loads, wait counts, LDS swizzles, the MFMA wrapper and the epilogue (store_tile).
 //
 // Tiled GEMM C = A * B for gfx950 with a swizzled, optionally persistent tile schedule.
 //
