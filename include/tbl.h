@@ -145,7 +145,9 @@ int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_
  *                 {program id, iteration of its tile loop, m, n, XCC id, core-clock cycles and
  *                 100 MHz real-time ticks from the tile's start to its epilogue, the start as the
  *                 low 32 bits of the 100 MHz real-time counter}. A program's first tile starts
- *                 before its prologue loads, a later tile where the previous tile's k loop ends.
+ *                 before its prologue loads, a later tile where the previous tile's epilogue ends
+ *                 (its operands are already loading then). Times are those of the workgroup's
+ *                 first wave.
  *                 Caller-owned. Tracing adds a few instructions per tile.
  *   All other arguments as tbl_gemm.
  */

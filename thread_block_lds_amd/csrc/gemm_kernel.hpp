@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   // Schedule trace (optional): per tile id, the program, its loop iteration, (m, n), the XCD, the
   // core-clock cycles and 100 MHz real-time ticks from the tile's start to its epilogue, and the
   // start itself (low 32 bits of the real-time counter). A program's first tile starts before its
-  // prologue; a later one when its predecessor's k loop ends.
+  // prologue; a later one when its predecessor's epilogue ends.
   uint64_t clk0 = 0, rt0 = 0;
   auto record = [&]() {
     if (trace != nullptr) {
