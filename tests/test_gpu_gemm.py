@@ -291,3 +291,17 @@ def test_short_k_streams_across_tiles(K, tile):
                      group=2, persistent=bool(persistent), num_programs=P)
         torch.cuda.synchronize()
         assert torch.equal(c, base), (K, tile, persistent, P)
+
+
+def test_binding_checks_trace_and_device():
+    a = torch.zeros((512, 512), dtype=torch.float16, device="cuda")
+    b = torch.zeros((512, 512), dtype=torch.float16, device="cuda")
+    # 512 x 512 with 256 tiles: 4 tiles need 32 trace ints
+    with pytest.raises(ValueError, match="at least 32"):
+        tbl.gemm(a, b, tile=(256, 256, 32), trace=torch.zeros(31, dtype=torch.int32, device="cuda"))
+    with pytest.raises(TypeError):
+        tbl.gemm(a, b, tile=(256, 256, 32), trace=torch.zeros(32, dtype=torch.int64, device="cuda"))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tbl.gemm(a, b, c=torch.zeros((512, 512), dtype=torch.float16))
+    with pytest.raises(ValueError, match="at least 16"):
+        tbl.tile_map(tbl.ROW, 4, 4, out_m=torch.zeros(15, dtype=torch.int32, device="cuda"))

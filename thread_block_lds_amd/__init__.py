@@ -125,6 +125,21 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _device_tensor(t, name, dtype=None, min_numel=None, device=None):
+    """Checks that ``t`` is a contiguous tensor in GPU memory (of ``dtype``, with at least
+    ``min_numel`` elements, on ``device``) before its address goes to a kernel."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} needs at least {min_numel} elements (got {t.numel()})")
+
+
 def _gemm_dtype(a, out_dtype):
     import torch
     if a.dtype == torch.float16:
@@ -158,6 +173,11 @@ def gemm(a, b, c=None, mode=ROW, group=1, persistent=False, num_programs=0, out_
         c = torch.empty((M, N), dtype=out_dtype, device=a.device)
     if c.shape != (M, N) or not c.is_contiguous() or c.dtype != out_dtype:
         raise ValueError("C must be a contiguous (M, N) tensor of the output dtype")
+    for t, name in ((a, "A"), (b, "B"), (c, "C")):
+        _device_tensor(t, name, device=a.device)
+    if trace is not None:
+        bm, bn, _ = tile if tile is not None else gemm_tile_shape(M, N, K)
+        _device_tensor(trace, "trace", torch.int32, 8 * (-(-M // bm)) * (-(-N // bn)), a.device)
     s = _stream(stream)
     if tile is None and trace is None:
         st = lib().tbl_gemm(_ptr(a), _ptr(b), _ptr(c), M, N, K, dt, int(mode), int(group),
@@ -198,6 +218,8 @@ def gemm_lds_layout(a, b, layout, c=None, mode=ROW, group=1, persistent=False, n
         c = torch.empty((M, N), dtype=torch.float16, device=a.device)
     if c.shape != (M, N) or not c.is_contiguous() or c.dtype != torch.float16:
         raise ValueError("C must be a contiguous (M, N) fp16 tensor")
+    for t, name in ((a, "A"), (b, "B"), (c, "C")):
+        _device_tensor(t, name, device=a.device)
     app, amp, bv, bpp, bmp = (int(x) for x in layout)
     st = lib().tbl_gemm_lds_layout(_ptr(a), _ptr(b), _ptr(c), M, N, K, F16, int(mode), int(group),
                                    int(bool(persistent)), int(num_programs), app, amp, bv, bpp, bmp,
@@ -216,6 +238,8 @@ def mfma_rate(a, b, workgroups=256, iters=4000, stream=None):
         raise TypeError("a and b must share dtype float16 or bfloat16")
     if not (a.is_contiguous() and b.is_contiguous()):
         raise ValueError("a and b must be contiguous")
+    _device_tensor(a, "a")
+    _device_tensor(b, "b", device=a.device)
     elems = min(a.numel(), b.numel())
     out = torch.empty(256 * int(workgroups), dtype=torch.float32, device=a.device)
     cycles = torch.zeros(2, dtype=torch.int64, device=a.device)
@@ -238,6 +262,8 @@ def tile_map(mode, grid_m, grid_n, group=1, out_m=None, out_n=None, device="cuda
         out_m = torch.empty(T, dtype=torch.int32, device=device)
     if out_n is None:
         out_n = torch.empty(T, dtype=torch.int32, device=device)
+    _device_tensor(out_m, "out_m", torch.int32, T)
+    _device_tensor(out_n, "out_n", torch.int32, T, out_m.device)
     st = lib().tbl_tile_map(int(mode), int(grid_m), int(grid_n), int(group), _ptr(out_m), _ptr(out_n),
                             _stream(stream))
     _check(st, "tbl_tile_map", allow_warning=True)
@@ -252,6 +278,10 @@ def transpose_i32(x, out=None, layout=T_XOR, stream=None):
     rows, cols = x.shape
     if out is None:
         out = torch.empty((cols, rows), dtype=torch.int32, device=x.device)
+    _device_tensor(x, "x")
+    if out.shape != (cols, rows):
+        raise ValueError(f"out must be ({cols}, {rows})")
+    _device_tensor(out, "out", torch.int32, device=x.device)
     st = lib().tbl_transpose_i32(_ptr(x), _ptr(out), rows, cols, int(layout), _stream(stream))
     _check(st, "tbl_transpose_i32")
     return out
