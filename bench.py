@@ -88,6 +88,17 @@ PMC_PASSES = (("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("fetch", ["FETCH_SIZE"])
                       "GRBM_GUI_ACTIVE"]))
 
 
+def _xcd_traffic_floor(xcds=8):
+    """Fewest HBM bytes of one 4096^3 launch with ``xcds`` private L2s: the T tiles split into
+    ``xcds`` rectangular blocks of a x b tiles (a * b = T / xcds, the squarest in bytes), each XCD
+    reading its blocks' A rows and B columns once; plus writing C."""
+    gm, gn = M // TILE, N // TILE
+    per = gm * gn // xcds
+    best = min((a * TILE + (per // a) * TILE) for a in range(1, per + 1) if per % a == 0 and a <= gm
+               and per // a <= gn)
+    return xcds * best * K * 2 + 2 * M * N
+
+
 def _is_gemm(kernel_name):
     """The library's GEMM kernels in a rocprofv3 record (gemm_kernel<...> for 64/128 tiles,
     gemm_pp_kernel<...> for 256 tiles)."""
@@ -739,7 +750,12 @@ def main():
                      "algorithmic_bytes_per_launch": 2 * (M * K + K * N + M * N),
                      # counter KiB per true KiB on a 256 MiB device copy; traffic = counters / factor
                      "traffic_calibration": ({k: round(v, 4) if v else None for k, v in ctr["factors"].items()}
-                                             if ctr else None)},
+                                             if ctr else None),
+                     # traffic averages all 12 variants; the floor with eight private L2s: each XCD
+                     # reads the A and B panels of its 32 tiles (a 4 x 8 block at best) once, plus C
+                     "traffic_floor_8_private_l2s": _xcd_traffic_floor(),
+                     "traffic_best_variant": (min((1e6 * (per_mode[n]["fetch_mb"] + per_mode[n]["write_mb"]), n)
+                                                  for n, _, _ in MODES) if traffic else None)},
         "mfma_ceiling_same_data": {**ceiling, "gemm_frac_of_ceiling": round(achieved / ceiling["tflops"], 4),
                                    "what": "tbl_mfma_rate on the 4096^3 operands: the GEMM's MFMA issue order "
                                            "with no memory traffic, at the clock the board holds for this data"},
