@@ -22,6 +22,8 @@ Modules:
   transpose   int32 transpose definition
   lds         LDS layout maps (naive / padded / XOR / chunk-XOR) and the bank-conflict model
   l2_model    byte-granular LRU L2 model and Spearman rank check (page 1's offline predictor)
+  schedule    the static stride schedule and the dynamic (work-queue) schedule page 1 names as
+              missing: event simulation and the checks every GPU trace of it must pass
 """
 
-from . import tile_maps, gemm, transpose, lds, l2_model  # noqa: F401
+from . import tile_maps, gemm, transpose, lds, l2_model, schedule  # noqa: F401
