@@ -8,6 +8,9 @@
  *     kernel with its persistent tile loop in section "CUDA Thread Block Swizzle Benchmark"), plus the
  *     group-major and serpentine orders of the tvm_tirx ClusterPersistentScheduler2D page
  *     (tvm.apache.org: "Tile Ordering", "Serpentine Mode", "Example 1").
+ *   - tbl_gemm_dynamic: the same GEMM with a dynamic persistent schedule, tiles handed out at run
+ *     time by counters -- what the persistent tile loop of "CUDA Thread Block Swizzle" (section
+ *     "CUDA Thread Block Swizzle Benchmark", its "Known limitations") notes it does not have.
  *   - tbl_gemm_lds_layout: the same GEMM with the operands' LDS swizzles taken from the chunk-XOR
  *     family of "CUDA Swizzle & bank conflict" (section "Triton - Shared Layout swizzling").
  *   - tbl_tile_map: the program-id -> (m, n) table of any order, computed by the same device code
@@ -154,6 +157,43 @@ int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_
 int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
                    int swizzle_mode, int group_size, int persistent, int num_programs, int block_m,
                    int block_n, int block_k, int32_t* trace, void* stream);
+
+/*
+ * tbl_gemm_dynamic -- tbl_gemm on 256x256x32 tiles with a dynamic persistent schedule ("CUDA Thread
+ * Block Swizzle", section "CUDA Thread Block Swizzle Benchmark": its persistent loop hands tile ids
+ * out statically, p, p + P, ...; its "Known limitations" name counter-based assignment as the
+ * missing alternative). Every workgroup takes each of its tiles, the first included, from claim
+ * counters: the positions 0 .. T-1 of the tile order (swizzle_mode, group_size, clusters as
+ * tbl_gemm) are handed out in increasing order, and a workgroup claims its next tile when it starts
+ * its current one. Without TBL_XCD_REMAP one counter serves all positions. With TBL_XCD_REMAP (which
+ * here replaces the remap) there is one counter per XCD: a workgroup on XCD x (the hardware's
+ * XCC id) takes positions floor(x T / 8) .. floor((x + 1) T / 8) - 1 first, then those of XCDs
+ * x + 1, x + 2, ... (mod 8) that are left. With equal tile times this reproduces the stride
+ * schedule (resp. the XCD-remapped one); otherwise faster workgroups take more tiles. The result
+ * bits equal tbl_gemm_tiled's with 256x256x32 tiles.
+ *   num_programs  workgroups; 0 = CUs x the kernel's occupancy; at most 65536.
+ *   workspace     device int32[workspace_ints], 16-byte aligned, caller-owned, with
+ *                 workspace_ints >= tbl_gemm_dynamic_workspace(num_programs as resolved). Its first
+ *                 10 ints must be zero when the kernel starts: fill it with zeros once, and every
+ *                 launch that completes leaves them zero again (the last workgroup to finish
+ *                 claiming resets them). Launches that share a workspace must not overlap in time
+ *                 (same stream, or synchronised); overlapping ones would share the counters. int 9
+ *                 counts hand-over faults between a workgroup's waves (never expected; a test
+ *                 checks it stays 0).
+ *   trace         NULL or device int32[8 * T], as tbl_gemm_tiled, indexed by order position.
+ *   K             at least 257 (nine 32-deep k steps per tile: a tile's successor is claimed and
+ *                 handed to all waves in its first five, before the loads run into it);
+ *                 TBL_ERR_SHAPE otherwise. The tile grid may have at most 2^30 tiles.
+ *   All other arguments as tbl_gemm. Errors: as tbl_gemm_tiled, plus TBL_ERR_INVALID_ARG for a NULL
+ *   or short workspace, TBL_ERR_ALIGN for a misaligned one.
+ */
+int tbl_gemm_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                     int swizzle_mode, int group_size, int num_programs, int32_t* workspace,
+                     int64_t workspace_ints, int32_t* trace, void* stream);
+
+/* int32 elements of the workspace tbl_gemm_dynamic needs for num_programs workgroups (>= 1), or -1
+ * if num_programs is out of range. */
+int64_t tbl_gemm_dynamic_workspace(int num_programs);
 
 /*
  * tbl_gemm_lds_layout -- tbl_gemm on 256x256x32 tiles with chosen LDS swizzles for the operands,

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(tbl.exported_names()) == declared
-    assert tbl.version() == 104
+    assert tbl.version() == 105
 
 
 def test_status_strings():
@@ -68,6 +68,34 @@ def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=32, A=FAKE, dt
 ])
 def test_gemm_validation(kw, want):
     assert _gemm(**kw) == want
+
+
+def _dyn(M=2048, N=2048, K=2048, dtype=0, mode=0, group=1, P=64, ws=FAKE, ws_ints=None, A=FAKE):
+    if ws_ints is None:
+        ws_ints = 32 + 32 * max(P, 1)
+    return tbl.lib().tbl_gemm_dynamic(A, FAKE, FAKE, M, N, K, dtype, mode, group, P, ws, ws_ints, NULL, NULL)
+
+
+def test_gemm_dynamic_workspace_size():
+    ws = tbl.lib().tbl_gemm_dynamic_workspace
+    assert ws(1) == 64 and ws(256) == 32 + 32 * 256 and ws(65536) == 32 + 32 * 65536
+    assert ws(0) == -1 and ws(-3) == -1 and ws(65537) == -1
+    assert tbl.dynamic_workspace_ints(256) == 8224
+    with pytest.raises(ValueError):
+        tbl.dynamic_workspace_ints(0)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(A=NULL), tbl.ERR_INVALID_ARG), (dict(M=0), tbl.ERR_INVALID_ARG), (dict(dtype=7), tbl.ERR_DTYPE),
+    (dict(mode=6), tbl.ERR_INVALID_ARG), (dict(mode=tbl.PANEL, group=0), tbl.ERR_INVALID_ARG),
+    (dict(P=-1), tbl.ERR_INVALID_ARG), (dict(P=65537), tbl.ERR_INVALID_ARG),
+    (dict(K=256), tbl.ERR_SHAPE), (dict(K=32), tbl.ERR_SHAPE), (dict(K=2044), tbl.ERR_SHAPE),
+    (dict(N=2044), tbl.ERR_SHAPE), (dict(M=2048, N=1536, mode=tbl.MORTON), tbl.ERR_NOT_BIJECTIVE),
+    (dict(ws=NULL), tbl.ERR_INVALID_ARG), (dict(ws=MISALIGNED), tbl.ERR_ALIGN),
+    (dict(P=64, ws_ints=32 + 32 * 64 - 1), tbl.ERR_INVALID_ARG), (dict(A=MISALIGNED), tbl.ERR_ALIGN),
+])
+def test_gemm_dynamic_validation(kw, want):
+    assert _dyn(**kw) == want
 
 
 def test_gemm_tiled_validation():

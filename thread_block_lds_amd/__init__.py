@@ -50,6 +50,11 @@ _EXPORTS = {
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "tbl_gemm_dynamic": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
+    "tbl_gemm_dynamic_workspace": (ctypes.c_int64, [ctypes.c_int]),
     "tbl_tile_map": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tbl_transpose_i32": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -192,6 +197,60 @@ def gemm(a, b, c=None, mode=ROW, group=1, persistent=False, num_programs=0, out_
                                   int(bool(persistent)), int(num_programs), int(bm), int(bn), int(bk),
                                   _ptr(trace), s)
         _check(st, "tbl_gemm_tiled")
+    return c
+
+
+def dynamic_workspace_ints(num_programs):
+    """int32 elements of the workspace tbl_gemm_dynamic needs for ``num_programs`` workgroups."""
+    n = lib().tbl_gemm_dynamic_workspace(int(num_programs))
+    if n < 0:
+        raise ValueError(f"num_programs {num_programs} out of range")
+    return n
+
+
+def dynamic_workspace(num_programs, device="cuda"):
+    """A zero-filled workspace for gemm_dynamic with up to ``num_programs`` workgroups. Launches
+    that complete leave its counters at zero, so one workspace serves any number of launches that
+    do not overlap in time."""
+    import torch
+    return torch.zeros(dynamic_workspace_ints(num_programs), dtype=torch.int32, device=device)
+
+
+def gemm_dynamic(a, b, c=None, mode=ROW, group=1, num_programs=0, workspace=None, out_dtype=None,
+                 trace=None, stream=None):
+    """C = A @ B with 256x256x32 tiles and the dynamic (work-queue) schedule, through
+    tbl_gemm_dynamic. ``mode`` may include XCD_REMAP (one claim queue per XCD). ``workspace``: from
+    dynamic_workspace(), sized for the launch's workgroups (default: a fresh one for
+    min(T, 4 x CUs)). ``trace``: int32 CUDA tensor of 8*T entries, indexed by order position.
+    Returns c."""
+    import torch
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shape mismatch {tuple(a.shape)} x {tuple(b.shape)}")
+    if a.dtype != b.dtype:
+        raise TypeError("A and B must share a dtype")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("A and B must be contiguous row-major")
+    M, K = a.shape
+    N = b.shape[1]
+    out_dtype = out_dtype or (c.dtype if c is not None else a.dtype)
+    dt = _gemm_dtype(a, out_dtype)
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if c.shape != (M, N) or not c.is_contiguous() or c.dtype != out_dtype:
+        raise ValueError("C must be a contiguous (M, N) tensor of the output dtype")
+    for t, name in ((a, "A"), (b, "B"), (c, "C")):
+        _device_tensor(t, name, device=a.device)
+    T = (-(-M // 256)) * (-(-N // 256))
+    if workspace is None:
+        P = int(num_programs) or max(1, min(T, 4 * device_info()["num_cus"]))
+        workspace = dynamic_workspace(P, a.device)
+    _device_tensor(workspace, "workspace", torch.int32, device=a.device)
+    if trace is not None:
+        _device_tensor(trace, "trace", torch.int32, 8 * T, a.device)
+    st = lib().tbl_gemm_dynamic(_ptr(a), _ptr(b), _ptr(c), M, N, K, dt, int(mode), int(group),
+                                int(num_programs), _ptr(workspace), workspace.numel(), _ptr(trace),
+                                _stream(stream))
+    _check(st, "tbl_gemm_dynamic")
     return c
 
 

@@ -17,6 +17,8 @@
 namespace {
 
 constexpr int64_t kMaxDim = int64_t{1} << 20;
+constexpr int kMaxDynamicPrograms = 1 << 16;
+constexpr int kMinDynamicKSteps = 9;
 constexpr int kMaxDevices = 64;
 
 struct DeviceInfo {
@@ -141,7 +143,7 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
 
 extern "C" {
 
-int tbl_version(void) { return 104; }
+int tbl_version(void) { return 105; }
 
 const char* tbl_status_string(int status) {
   switch (status) {
@@ -219,6 +221,45 @@ int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_
   if (tbl::launch_gemm_layout(a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase, a,
                               static_cast<hipStream_t>(stream)) != hipSuccess)
     return TBL_ERR_HIP;
+  return TBL_OK;
+}
+
+int64_t tbl_gemm_dynamic_workspace(int num_programs) {
+  if (num_programs < 1 || num_programs > kMaxDynamicPrograms) return -1;
+  return 32 + 32 * static_cast<int64_t>(num_programs);
+}
+
+int tbl_gemm_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                     int swizzle_mode, int group_size, int num_programs, int32_t* workspace,
+                     int64_t workspace_ints, int32_t* trace, void* stream) {
+  int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, 1, num_programs, 256, 256, 32);
+  if (rc != TBL_OK) return rc;
+  // wave 0 posts the next tile at k step 0 and the others read it at step 4; the load cursor
+  // moves to the next tile at the end of step nk - 5's loads
+  if ((K + 31) / 32 < kMinDynamicKSteps) return TBL_ERR_SHAPE;
+  const int gm = static_cast<int>((M + 255) / 256), gn = static_cast<int>((N + 255) / 256);
+  if (static_cast<int64_t>(gm) * gn > (int64_t{1} << 30)) return TBL_ERR_SHAPE;
+  int programs = 0;
+  rc = resolve_programs(dtype, 256, 256, 32, static_cast<int64_t>(gm) * gn, 1, num_programs, &programs);
+  if (rc != TBL_OK) return rc;
+  if (programs > kMaxDynamicPrograms) return TBL_ERR_INVALID_ARG;
+  if (workspace == nullptr || !aligned16(workspace)) return workspace == nullptr ? TBL_ERR_INVALID_ARG
+                                                                                 : TBL_ERR_ALIGN;
+  if (workspace_ints < tbl_gemm_dynamic_workspace(programs)) return TBL_ERR_INVALID_ARG;
+  tbl::GemmLaunch a;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  // the claim queues take the remap's place: positions are the order's own ids
+  a.order = make_order(swizzle_mode & ~TBL_XCD_REMAP, gm, gn, group_size);
+  a.num_programs = programs;
+  a.trace = trace;
+  a.work = workspace;
+  a.xcd_aware = (swizzle_mode & TBL_XCD_REMAP) ? 1 : 0;
+  if (tbl::launch_gemm_dynamic(dtype, a, static_cast<hipStream_t>(stream)) != hipSuccess) return TBL_ERR_HIP;
   return TBL_OK;
 }
 

@@ -15,6 +15,10 @@ hipError_t launch_gemm(int dtype, int bm, int bn, int bk, const GemmLaunch& a, h
   return launch_pp(dtype, a, s);
 }
 
+hipError_t launch_gemm_dynamic(int dtype, const GemmLaunch& a, hipStream_t s) {
+  return launch_pp_dynamic(dtype, a, s);
+}
+
 hipError_t gemm_blocks_per_cu(int dtype, int bm, int bn, int bk, int* out) {
   if (!gemm_tile_supported(bm, bn, bk)) return hipErrorInvalidValue;
   const void* k = bm == 64 ? kernel_for<64, 64>(dtype)

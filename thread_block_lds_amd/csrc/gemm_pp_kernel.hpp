@@ -27,12 +27,37 @@ namespace {
 
 constexpr int kPPThreads = 512;
 
-template <bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4, int kBPP = 1, int kBMP = 4>
+// Vector-memory accesses of the dynamic schedule (claim counters, mailboxes). Those returning a value
+// wait for it inside the asm (vmcnt(0): also for every load in flight), so the compiler never sees
+// a pending result it would have to track through the pipeline's steps -- it would then wait for
+// all loads in every step. The cache-policy bits are the ones the compiler itself emits for these
+// scopes on gfx950: atomics return with sc0 and are device-coherent; sc0 marks workgroup-scope
+// loads and stores, sc1 device-scope stores.
+__device__ __forceinline__ unsigned dyn_atomic_add(unsigned* p, unsigned v) {   // device scope
+  unsigned r;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(p), "v"(v) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint64_t dyn_load_wg(const uint64_t* p) {   // workgroup scope
+  uint64_t r;
+  asm volatile("global_load_dwordx2 %0, %1, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+__device__ __forceinline__ void dyn_store_wg(uint64_t* p, uint64_t v) {   // workgroup scope
+  asm volatile("global_store_dwordx2 %0, %1, off sc0" : : "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void dyn_store_device(unsigned* p, unsigned v) {   // device scope
+  asm volatile("global_store_dword %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+
+template <bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4, int kBPP = 1, int kBMP = 4,
+          bool kDyn = false>
 __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B,
                                                              void* __restrict__ Cv, int M, int N, int K,
                                                              TileOrder order, int num_programs,
-                                                             int32_t* __restrict__ trace) {
+                                                             int32_t* __restrict__ trace,
+                                                             int32_t* __restrict__ work, int xcd_aware) {
   constexpr int BM = 256, BN = 256;
   constexpr int WM = 128, WN = 64;                 // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;        // 4 x 2 MFMA blocks per wave
@@ -60,9 +85,64 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   const int grp = wave >> 2, wn = wave & 3;
   const int nk = (K + kBK - 1) / kBK;
   const int P = num_programs;
-  if (static_cast<int>(blockIdx.x) >= order.tiles) return;
-  const int my_tiles = (order.tiles - 1 - static_cast<int>(blockIdx.x)) / P + 1;
+  // static schedule: this workgroup's tiles are blockIdx.x + i P; the dynamic one takes every tile,
+  // the first included, from the claim counters, so every workgroup runs its prologue claim
+  if (!kDyn && static_cast<int>(blockIdx.x) >= order.tiles) return;
+  const int my_tiles = kDyn ? 0 : (order.tiles - 1 - static_cast<int>(blockIdx.x)) / P + 1;
   const int total = my_tiles * nk;
+
+  // ---- dynamic schedule: claims of order positions (wave 0) and their hand-over to the others ----
+  // work[0..7]: claim counters -- one queue over all positions, or (xcd_aware) one per XCD over the
+  // block floor(q T / 8) .. floor((q + 1) T / 8) - 1, taken from the own XCD's block first, then from
+  // the next blocks in turn; work[8]: workgroups done claiming, the last of which zeroes work[0..8];
+  // work[9]: hand-over faults (stays 0); work[32 + 32 p ..]: workgroup p's two mailbox slots, each a
+  // 64-bit (claim number << 32 | position). A position < 0 means no work is left.
+  const unsigned T = static_cast<unsigned>(order.tiles);
+  const int own_q = kDyn && xcd_aware ? xcc_id() : 0;
+  int cur_q = own_q;
+  uint64_t* mailbox = kDyn ? reinterpret_cast<uint64_t*>(work + 32 + 32 * static_cast<size_t>(blockIdx.x))
+                           : nullptr;
+  auto claim_one = [&]() -> unsigned {   // wave 0: one claim on the current queue
+    unsigned r = 0;
+    if (lane == 0) r = dyn_atomic_add(reinterpret_cast<unsigned*>(work) + cur_q, 1u);
+    return __builtin_amdgcn_readfirstlane(r);
+  };
+  auto claim = [&]() -> int {   // wave 0: the next position, rotating through empty queues; -1: none
+    for (;;) {
+      const unsigned c = claim_one();
+      const unsigned lo = xcd_aware ? static_cast<unsigned>(static_cast<uint64_t>(cur_q) * T / kNumXcds) : 0u;
+      const unsigned hi = xcd_aware ? static_cast<unsigned>(static_cast<uint64_t>(cur_q + 1) * T / kNumXcds) : T;
+      if (c < hi - lo) return static_cast<int>(lo + c);
+      if (!xcd_aware) return -1;
+      cur_q = (cur_q + 1) & (kNumXcds - 1);
+      if (cur_q == own_q) return -1;
+    }
+  };
+  auto claims_done = [&]() {   // wave 0, once: count this workgroup out; the last one resets the counters
+    unsigned e = 0;
+    if (lane == 0) e = dyn_atomic_add(reinterpret_cast<unsigned*>(work) + 8, 1u);
+    e = __builtin_amdgcn_readfirstlane(e);
+    if (e == gridDim.x - 1 && lane <= 8) dyn_store_device(reinterpret_cast<unsigned*>(work) + lane, 0u);
+  };
+  auto mailbox_put = [&](int k, int pos) {   // wave 0
+    if (lane == 0)
+      dyn_store_wg(mailbox + (k & 1),
+                   (static_cast<uint64_t>(static_cast<unsigned>(k)) << 32) | static_cast<unsigned>(pos));
+  };
+  auto mailbox_take = [&](int k) -> int {   // other waves: read the slot, check its claim number
+    for (int tries = 0; tries < 1024; ++tries) {
+      const uint64_t v = dyn_load_wg(mailbox + (k & 1));
+      if (__builtin_amdgcn_readfirstlane(static_cast<unsigned>(v >> 32)) == static_cast<unsigned>(k)) {
+        const int pos = static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(v)));
+        if (pos < static_cast<int>(T)) return pos;   // -1 (no work) or a position of this grid
+        break;
+      }
+    }
+    // never expected: the slot was written, and its store completed, before a barrier. Counted,
+    // and no tile is taken, so no address outside the operands is formed.
+    if (lane == 0) dyn_atomic_add(reinterpret_cast<unsigned*>(work) + 9, 1u);
+    return -1;
+  };
 
   // ---- per-lane constants of the direct loads (as gemm_kernel, eight waves) ----
   constexpr int kOutOfRange = 0x7FFFFFF0;
@@ -102,8 +182,23 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     }
   }
 
+  // the first tile: blockIdx.x, or (dynamic) claimed by wave 0 and handed over through the mailbox
+  int first = static_cast<int>(blockIdx.x);
+  int nxt = -1;   // dynamic: position of the tile after the current one, known from k step 4 on
+  if constexpr (kDyn) {
+    if (wave == 0) {
+      first = claim();
+      mailbox_put(0, first);
+      if (first < 0) claims_done();
+      wait_vm<0>();   // the mailbox store has landed before the barrier
+    }
+    lds_barrier();
+    if (wave != 0) first = mailbox_take(0);
+    if (first < 0) return;   // every wave of the workgroup alike
+  }
+
   // ---- load cursor (as gemm_kernel) ----
-  int ld_t = blockIdx.x, ld_kt = 0, ld_issued = 0, ld_stage = 0;
+  int ld_t = first, ld_kt = 0, ld_issued = 0, ld_stage = 0;
   uint64_t ld_a = 0, ld_b = 0;
   const unsigned a_step = kBK * 2;
   const uint64_t b_step = static_cast<uint64_t>(kBK) * static_cast<unsigned>(N) * 2;
@@ -125,7 +220,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   // issue this wave's loads of the next step in the stream (zero-length ones past its end, which
   // keep the number of loads per step, and so every wait count, the same)
   auto load_step = [&]() {
-    const bool real = ld_issued < total;
+    const bool real = kDyn ? ld_t >= 0 : ld_issued < total;
     const int k_left = K - ld_kt * kBK;
     const unsigned b_rows = static_cast<unsigned>(k_left < kBK ? k_left : kBK);
     const bool tail = k_left < kBK;
@@ -145,8 +240,13 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     a_range -= a_step;
     if (++ld_kt == nk) {
       ld_kt = 0;
-      ld_t += P;
-      if (ld_t < order.tiles) enter_tile();
+      if constexpr (kDyn) {
+        ld_t = nxt;
+        if (ld_t >= 0) enter_tile();
+      } else {
+        ld_t += P;
+        if (ld_t < order.tiles) enter_tile();
+      }
     }
   };
 
@@ -183,7 +283,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   };
 
   // ---- compute cursor and optional schedule trace (as gemm_kernel) ----
-  int c_t = blockIdx.x, c_iter = 0, c_m = 0, c_n = 0;
+  int c_t = first, c_iter = 0, c_m = 0, c_n = 0;
   order_tile(order, c_t, c_m, c_n);
   uint64_t clk0 = 0, rt0 = 0;
   auto record = [&]() {
@@ -240,9 +340,28 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     c_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int tile = 0; tile < my_tiles; ++tile) {
+  // dynamic: at the start of tile j's k step 0, wave 0 claims tile j + 1 and posts it; the other
+  // waves read it at the start of step 4 (the post, issued before step 0's loads, has landed by
+  // wave 0's wait at the end of step 2); the load cursor moves to tile j + 1 at the end of step
+  // nk - 5's loads, so nk >= 9. A claim or a read waits for its result at once, and with it for the
+  // wave's loads in flight: about one load latency per tile and wave. The claim number in each slot
+  // catches a stale read.
+  auto dyn_hook = [&](int kt) {
+    const int k = c_iter + 1;
+    if (wave == 0) {
+      if (kt == 0) {
+        nxt = claim();
+        mailbox_put(k, nxt);
+        if (nxt < 0) claims_done();
+      }
+    } else if (kt == 4) {
+      nxt = mailbox_take(k);
+    }
+  };
+  for (int tile = 0; kDyn || tile < my_tiles; ++tile) {
     zero_acc();
     for (int kt = 0; kt < nk; ++kt) {
+      if constexpr (kDyn) dyn_hook(kt);
       memory_half();
       compute_half();
       lds_barrier();
@@ -251,11 +370,19 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     // the epilogue overlaps the other group's last compute half-period
     record_time();
     store_tile<BM, BN, WM, WN, TM, TN, kBf16, kF32Out>(acc, Cv, M, N, c_m, c_n, grp, wn, lane);
-    c_t += P;
-    ++c_iter;
-    if (c_t < order.tiles) {
+    if constexpr (kDyn) {
+      c_t = nxt;
+      ++c_iter;
+      if (c_t < 0) break;
       order_tile(order, c_t, c_m, c_n);
       record();
+    } else {
+      c_t += P;
+      ++c_iter;
+      if (c_t < order.tiles) {
+        order_tile(order, c_t, c_m, c_n);
+        record();
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -278,12 +405,13 @@ const void* pp_kernel_for(int dtype) {
   }
 }
 
-template <bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4, int kBPP = 1, int kBMP = 4>
+template <bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4, int kBPP = 1, int kBMP = 4,
+          bool kDyn = false>
 hipError_t launch_pp_typed(const GemmLaunch& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_pp_kernel<kBf16, kF32Out, kAPP, kAMP, kBV, kBPP, kBMP>), dim3(a.num_programs),
+  hipLaunchKernelGGL((gemm_pp_kernel<kBf16, kF32Out, kAPP, kAMP, kBV, kBPP, kBMP, kDyn>), dim3(a.num_programs),
                      dim3(kPPThreads), 0, s, static_cast<const uint16_t*>(a.A),
                      static_cast<const uint16_t*>(a.B), a.C, a.M, a.N, a.K, a.order, a.num_programs,
-                     a.trace);
+                     a.trace, a.work, a.xcd_aware);
   return hipGetLastError();
 }
 
@@ -293,6 +421,17 @@ hipError_t launch_pp(int dtype, const GemmLaunch& a, hipStream_t s) {
     case 1: return launch_pp_typed<true, false>(a, s);
     case 2: return launch_pp_typed<false, true>(a, s);
     case 3: return launch_pp_typed<true, true>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The dynamic schedule (claim counters and mailboxes in a.work).
+hipError_t launch_pp_dynamic(int dtype, const GemmLaunch& a, hipStream_t s) {
+  switch (dtype) {
+    case 0: return launch_pp_typed<false, false, 4, 4, 4, 1, 4, true>(a, s);
+    case 1: return launch_pp_typed<true, false, 4, 4, 4, 1, 4, true>(a, s);
+    case 2: return launch_pp_typed<false, true, 4, 4, 4, 1, 4, true>(a, s);
+    case 3: return launch_pp_typed<true, true, 4, 4, 4, 1, 4, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,6 +16,8 @@ struct GemmLaunch {
   TileOrder order;
   int num_programs;
   int32_t* trace;   // nullable
+  int32_t* work = nullptr;   // dynamic schedule: claim counters and mailboxes
+  int xcd_aware = 0;         // dynamic schedule: one claim queue per XCD
 };
 
 // dtype: TBL_F16 .. TBL_BF16_F32OUT. Returns hipSuccess or the launch error.
@@ -23,6 +25,8 @@ hipError_t launch_gemm(int dtype, int bm, int bn, int bk, const GemmLaunch& a, h
 // Resident workgroups per CU of the kernel for (dtype, tile), from the HIP occupancy query.
 hipError_t gemm_blocks_per_cu(int dtype, int bm, int bn, int bk, int* out);
 bool gemm_tile_supported(int bm, int bn, int bk);
+// The 256 x 256 x 32 kernel with the dynamic (work-queue) schedule; a.work and a.xcd_aware set.
+hipError_t launch_gemm_dynamic(int dtype, const GemmLaunch& a, hipStream_t s);
 
 // The 256 x 256 x 32 fp16 -> fp16 kernel with the LDS swizzles (A: perPhase, maxPhase; B: vec in
 // 16-byte chunks, perPhase, maxPhase) of one compiled variant; gemm_layout_supported lists them.
