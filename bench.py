@@ -26,9 +26,10 @@ Printed: one JSON line with
                of it;
   transpose    the int32 LDS transpose at 16384 x 16384 per layout: GB/s against 8 TB/s;
   target_8192  the 8192^3 bf16 persistent GEMM (group-major g8 and serpentine s8, each with and
-               without the XCD remap, and group-major g4 over 2x2 clusters of tiles with the remap):
-               TFLOP/s, % of peak and predicted L2 hit rate of each order (the 70 % target), and
-               the MFMA ceiling on its bf16 operands;
+               without the XCD remap, and group-major g4 over 2x2 clusters of tiles with the remap;
+               then both orders under the dynamic work-queue schedule, with one claim queue and
+               with one per XCD): TFLOP/s, % of peak and predicted L2 hit rate of each static order
+               (the 70 % target), and the MFMA ceiling on its bf16 operands;
   cpu_baseline the fp64 CPU oracle on a sample of output rows of the same product.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-counters] [--no-cpu]
@@ -78,6 +79,10 @@ CLUSTER_2X2 = (1 << 16) | (1 << 20)   # two-level order: 2 x 2 clusters of tiles
 C3_MODES = [("group_major_g8", 2, 8), ("serpentine_s8", 5, 8),
             ("group_major_g8+remap", 2 | REMAP, 8), ("serpentine_s8+remap", 5 | REMAP, 8),
             ("group_major_g4+remap+cluster2x2", 2 | REMAP | CLUSTER_2X2, 4)]
+# the dynamic (work-queue) schedule on the same orders: one claim queue, or one per XCD (REMAP)
+C3_DYNAMIC = [("group_major_g8 dynamic", 2, 8), ("serpentine_s8 dynamic", 5, 8),
+              ("group_major_g8 dynamic+xcd_queues", 2 | REMAP, 8),
+              ("serpentine_s8 dynamic+xcd_queues", 5 | REMAP, 8)]
 PS = 8192                     # the swizzle page's own sweep: 8192^3 fp16 N(0,1), 128x128x32 tiles
 PS_TILE = (128, 128, 32)
 PS_ORDERS = ([("row", 0, 1), ("col", 1, 1)] + [(f"panel_g{g}", 2, g) for g in (1, 2, 4, 8, 16, 32, 64)]
@@ -384,11 +389,21 @@ def target_check(tbl, torch, stream, reps=10):
                                       resident=max(1, progs // info["num_xcds"]))
         res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2),
                      "pred_l2_hit_pct": round(100.0 * hits / acc, 2)}
+    ws = tbl.dynamic_workspace(progs)
+    for name, mode, g in C3_DYNAMIC:
+        def launch():
+            tbl.gemm_dynamic(ad, bd, c, mode=mode, group=g, workspace=ws, stream=stream.cuda_stream)
+        launch()
+        launch()
+        ms = _median_ms(torch, stream, launch, reps)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2),
+                     "schedule": "dynamic"}
     best = max(res, key=lambda n: res[n]["tflops"])
     ceiling = mfma_ceiling(tbl, torch, stream, ad, bd, gemm_tflops=res[best]["tflops"])
     del ad, bd, c
     return {"workload": "gemm 8192^3 bf16 N(0,1)/sqrt(K) -> bf16 (fp32 accumulate), 256x256x32 tiles, "
-                        "persistent stride schedule over CUs x occupancy programs",
+                        "persistent stride schedule (and the dynamic work-queue schedule) over CUs x occupancy programs",
             "programs": tbl.default_num_programs(C3, C3, C3, tbl.BF16, persistent=True),
             "orders": res, "best": best, "best_pct_peak": res[best]["pct_peak"], "target_pct_peak": 70.0,
             "mfma_ceiling_same_data": ceiling}

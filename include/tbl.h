@@ -162,24 +162,23 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * tbl_gemm_dynamic -- tbl_gemm on 256x256x32 tiles with a dynamic persistent schedule ("CUDA Thread
  * Block Swizzle", section "CUDA Thread Block Swizzle Benchmark": its persistent loop hands tile ids
  * out statically, p, p + P, ...; its "Known limitations" name counter-based assignment as the
- * missing alternative). Every workgroup takes each of its tiles, the first included, from claim
- * counters: the positions 0 .. T-1 of the tile order (swizzle_mode, group_size, clusters as
- * tbl_gemm) are handed out in increasing order, and a workgroup claims its next tile when it starts
- * its current one. Without TBL_XCD_REMAP one counter serves all positions. With TBL_XCD_REMAP (which
- * here replaces the remap) there is one counter per XCD: a workgroup on XCD x (the hardware's
- * XCC id) takes positions floor(x T / 8) .. floor((x + 1) T / 8) - 1 first, then those of XCDs
- * x + 1, x + 2, ... (mod 8) that are left. With equal tile times this reproduces the stride
- * schedule (resp. the XCD-remapped one); otherwise faster workgroups take more tiles. The result
- * bits equal tbl_gemm_tiled's with 256x256x32 tiles.
+ * missing alternative). The positions 0 .. T-1 of the tile order (swizzle_mode, group_size,
+ * clusters as tbl_gemm) are handed out in increasing order by claim counters; a workgroup claims
+ * its next tile when it starts its current one. Without TBL_XCD_REMAP one counter serves all
+ * positions and workgroup p's first tile is position p. With TBL_XCD_REMAP (which here replaces the
+ * remap) there is one counter per XCD over the block floor(x T / 8) .. floor((x + 1) T / 8) - 1:
+ * workgroup p's first tile is the (p / 8)-th position of block p mod 8 (the XCD round-robin
+ * dispatch puts it on), and a workgroup on XCD x (the hardware's XCC id) claims from block x, then,
+ * once it is empty, from the block with the most positions left. With equal tile times this
+ * reproduces the stride schedule (resp. the XCD-remapped one); otherwise faster workgroups take
+ * more tiles. The result bits equal tbl_gemm_tiled's with 256x256x32 tiles.
  *   num_programs  workgroups; 0 = CUs x the kernel's occupancy; at most 65536.
  *   workspace     device int32[workspace_ints], 16-byte aligned, caller-owned, with
- *                 workspace_ints >= tbl_gemm_dynamic_workspace(num_programs as resolved). Its first
- *                 10 ints must be zero when the kernel starts: fill it with zeros once, and every
- *                 launch that completes leaves them zero again (the last workgroup to finish
- *                 claiming resets them). Launches that share a workspace must not overlap in time
- *                 (same stream, or synchronised); overlapping ones would share the counters. int 9
- *                 counts hand-over faults between a workgroup's waves (never expected; a test
- *                 checks it stays 0).
+ *                 workspace_ints >= tbl_gemm_dynamic_workspace(num_programs as resolved). Each call
+ *                 first enqueues a one-workgroup kernel that zeroes the claim counters (ints 0..8),
+ *                 so no initial contents are needed; calls that share a workspace must not overlap
+ *                 in time (same stream, or synchronised). int 9 counts hand-over faults between a
+ *                 workgroup's waves: never expected, never reset; zero it to watch it.
  *   trace         NULL or device int32[8 * T], as tbl_gemm_tiled, indexed by order position.
  *   K             at least 257 (nine 32-deep k steps per tile: a tile's successor is claimed and
  *                 handed to all waves in its first five, before the loads run into it);

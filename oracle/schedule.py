@@ -20,8 +20,9 @@ ones its notes support:
     Lookahead 0 (claim on finishing a tile) is the textbook greedy list schedule.
   * XCD-aware variant (gfx950 has eight XCDs with private L2s): the order's positions are cut into
     X contiguous blocks, block x = [floor(x T / X), floor((x + 1) T / X)), each with its own counter.
-    A program on XCD x claims from block x; once block x is empty it claims from blocks x + 1,
-    x + 2, ... (mod X) in turn, never returning to a block it found empty.
+    A program on XCD x claims from block x while it has positions left; then from the block with
+    the most unclaimed positions (ties: the nearest after x in the order x + 1, x + 2, ... mod X),
+    keeping to that block while it lasts; it stops when every block is empty.
   * Simultaneous claims are served in order of claim number, then program index (in the kernel they
     race; the tests of GPU traces check only what holds for every interleaving).
 """
@@ -53,20 +54,29 @@ class _Queues:
         self.xcd_aware = xcd_aware
         self.X = X
 
+    def left(self, q):
+        lo, hi = self.blocks[q]
+        return max(0, hi - lo - self.count[q])
+
     def claim(self, cursor):
         """cursor = [own queue, queue now claimed from]; returns a position or -1."""
-        while True:
-            q = cursor[1]
-            lo, hi = self.blocks[q]
-            c = self.count[q]
-            self.count[q] += 1
-            if lo + c < hi:
-                return lo + c
-            if not self.xcd_aware:
-                return -1
-            cursor[1] = (q + 1) % self.X
-            if cursor[1] == cursor[0]:
-                return -1
+        q = cursor[1]
+        lo, hi = self.blocks[q]
+        c = self.count[q]
+        self.count[q] += 1
+        if lo + c < hi:
+            return lo + c
+        if not self.xcd_aware:
+            return -1
+        own = cursor[0]
+        best = max(range(self.X), key=lambda r: (self.left(r), -((r - own) % self.X)))
+        if self.left(best) == 0:
+            return -1
+        cursor[1] = best
+        lo, hi = self.blocks[best]
+        c = self.count[best]
+        self.count[best] += 1
+        return lo + c
 
 
 def simulate_dynamic(durations, P, lookahead=1, xcd_aware=False, xcd_of=None, X=8):
@@ -158,10 +168,11 @@ def check_dynamic_trace(program, iteration, xcd, T, xcd_aware, X=8):
             assert np.all(np.diff(pos) > 0), f"program {p}: claims not increasing {pos.tolist()}"
         else:
             own = int(xs[0])
-            dist = (block_of[pos] - own) % X
-            assert np.all(np.diff(dist) >= 0), f"program {p}: queues out of rotation {pos.tolist()}"
-            for d in np.unique(dist):
-                sel = pos[dist == d]
-                assert np.all(np.diff(sel) > 0), f"program {p}: claims in a block not increasing"
+            mine = block_of[pos] == own
+            n_own = int(np.sum(mine))
+            assert np.all(mine[:n_own]), f"program {p}: left its own block and came back {pos.tolist()}"
+            for q in np.unique(block_of[pos]):
+                sel = pos[block_of[pos] == q]
+                assert np.all(np.diff(sel) > 0), f"program {p}: claims in block {q} not increasing"
         seqs[int(p)] = pos.tolist()
     return seqs

@@ -7,8 +7,8 @@ What is checked:
   * the schedule, from the trace: every order position runs exactly once, each at its (m, n) in the
     order's tile table, and every per-workgroup sequence is one that oracle.schedule's claim rules
     allow (check_dynamic_trace);
-  * the workspace: its counters are zero again after every launch (so launches chain), and the
-    hand-over fault count stays zero;
+  * the workspace: launches chain on one workspace (each resets its counters), and the hand-over
+    fault count stays zero;
   * edges: one workgroup running every tile, more workgroups than tiles, the minimum of nine k
     steps, ragged M, N, K, fp32 output, and queues with no local workgroup (XCD-aware with four
     workgroups), which are emptied by rotation.
@@ -38,8 +38,7 @@ def _run(ad, bd, mode, g, P, out_dtype=None, trace=True):
     c = tbl.gemm_dynamic(ad, bd, mode=mode, group=g, num_programs=P, workspace=ws, out_dtype=out_dtype,
                          trace=tr)
     torch.cuda.synchronize()
-    w = ws[:10].cpu().numpy()
-    assert np.all(w == 0), f"workspace counters not reset: {w.tolist()}"
+    assert int(ws[9].item()) == 0, "hand-over fault"
     return c, (tr.cpu().numpy().reshape(T, 8).astype(np.int64) if trace else None)
 
 
@@ -79,12 +78,13 @@ def test_workspace_chains_launches(square2048):
     a, b, ref = square2048
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     ws = tbl.dynamic_workspace(32)
+    ws[:9] = 12345                 # whatever the counters hold, each launch starts from zero
     outs = []
     for mode in (tm.PANEL, tm.PANEL | tm.XCD_REMAP, tm.SERPENTINE, tm.ROW | tm.XCD_REMAP):
         for _ in range(3):   # back to back on one stream, no synchronisation in between
             outs.append(tbl.gemm_dynamic(ad, bd, mode=mode, group=4, num_programs=32, workspace=ws))
     torch.cuda.synchronize()
-    assert np.all(ws[:10].cpu().numpy() == 0)
+    assert int(ws[9].item()) == 0
     for c in outs[1:]:
         assert torch.equal(c, outs[0])
     check_tol(host64(outs[0]), ref, 2048, what="chained launches")

@@ -133,6 +133,23 @@ def test_lookahead_one_bound(seed, xcd_aware):
     sc.check_dynamic_trace(program, iteration, xcd, T, xcd_aware)
 
 
+def test_steal_takes_the_fullest_block():
+    """Hand case, T = 16 (blocks of 2), four programs on XCDs 0..3, program 0's tiles 10x slower:
+    programs 1..3 empty their blocks, then each steals from the block with the most positions left
+    (4..7 hold 2 each; ties go to the nearest block after the thief's own XCD)."""
+    d = [1.0] * 16
+    d[0] = d[1] = 10.0
+    tiles, _, _, owner, ms = sc.simulate_dynamic(d, 4, lookahead=1, xcd_aware=True)
+    assert tiles[0][:2] == [0, 1]
+    assert tiles[1][:2] == [2, 3] and tiles[2][:2] == [4, 5] and tiles[3][:2] == [6, 7]
+    # time 0, second claims (one ahead): 0 -> 1, 1 -> 3, 2 -> 5, 3 -> 7, all from their own blocks.
+    # time 1, programs 1..3 claim again and find their blocks empty. Program 1: blocks 4..7 have 2
+    # left each, the nearest after XCD 1 is block 4 -> position 8. Program 2: block 4 now has 1, 5..7
+    # have 2, nearest is 5 -> 10. Program 3: 6 and 7 have 2, nearest is 6 -> 12.
+    assert tiles[1][2] == 8 and tiles[2][2] == 10 and tiles[3][2] == 12
+    assert ms <= sum(d) / 4 + 2 * max(d)
+
+
 def test_xcd_aware_steals_from_other_blocks():
     """Equal times: every position stays on its block's XCD. Block 0's tiles taking 3 units and the
     rest 1: the other XCDs' programs empty their own blocks, then take block 0's remaining ones."""

@@ -209,9 +209,9 @@ def dynamic_workspace_ints(num_programs):
 
 
 def dynamic_workspace(num_programs, device="cuda"):
-    """A zero-filled workspace for gemm_dynamic with up to ``num_programs`` workgroups. Launches
-    that complete leave its counters at zero, so one workspace serves any number of launches that
-    do not overlap in time."""
+    """A zero-filled workspace for gemm_dynamic with up to ``num_programs`` workgroups. Each launch
+    resets its claim counters itself, so one workspace serves any number of launches that do not
+    overlap in time."""
     import torch
     return torch.zeros(dynamic_workspace_ints(num_programs), dtype=torch.int32, device=device)
 

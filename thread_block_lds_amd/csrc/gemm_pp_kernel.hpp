@@ -2,7 +2,10 @@
 //
 // Same computation as gemm_kernel (gemm_kernel.hpp): workgroup p walks tile ids p, p + P, ... and
 // accumulates each output tile in fp32 over k in ascending 16-deep MFMA steps, so the results are
-// bit-identical to it. What differs is how the work is laid out over the CU:
+// bit-identical to it. With kDyn the tiles come instead from claim counters (the dynamic schedule
+// that "CUDA Thread Block Swizzle", section "CUDA Thread Block Swizzle Benchmark", notes its
+// persistent loop lacks); only the schedule changes, never a tile's arithmetic. What differs from
+// gemm_kernel is how the work is laid out over the CU:
 //   * 512 threads = 8 wave64s, two per SIMD. Group 0 (waves 0-3) owns output rows 0-127 of the
 //     tile, group 1 (waves 4-7) rows 128-255; inside a group wave w owns columns 64 (w mod 4) ..
 //     + 63, a 128 x 64 sub-tile of 4 x 2 blocks of 32 x 32 (128 accumulator registers).
@@ -32,7 +35,7 @@ constexpr int kPPThreads = 512;
 // a pending result it would have to track through the pipeline's steps -- it would then wait for
 // all loads in every step. The cache-policy bits are the ones the compiler itself emits for these
 // scopes on gfx950: atomics return with sc0 and are device-coherent; sc0 marks workgroup-scope
-// loads and stores, sc1 device-scope stores.
+// loads and stores, sc1 device-scope loads.
 __device__ __forceinline__ unsigned dyn_atomic_add(unsigned* p, unsigned v) {   // device scope
   unsigned r;
   asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(p), "v"(v) : "memory");
@@ -46,8 +49,10 @@ __device__ __forceinline__ uint64_t dyn_load_wg(const uint64_t* p) {   // workgr
 __device__ __forceinline__ void dyn_store_wg(uint64_t* p, uint64_t v) {   // workgroup scope
   asm volatile("global_store_dwordx2 %0, %1, off sc0" : : "v"(p), "v"(v) : "memory");
 }
-__device__ __forceinline__ void dyn_store_device(unsigned* p, unsigned v) {   // device scope
-  asm volatile("global_store_dword %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+__device__ __forceinline__ unsigned dyn_load_device(const unsigned* p) {   // device scope
+  unsigned r;
+  asm volatile("global_load_dword %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(p) : "memory");
+  return r;
 }
 
 template <bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4, int kBPP = 1, int kBMP = 4,
@@ -92,37 +97,59 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   const int total = my_tiles * nk;
 
   // ---- dynamic schedule: claims of order positions (wave 0) and their hand-over to the others ----
-  // work[0..7]: claim counters -- one queue over all positions, or (xcd_aware) one per XCD over the
-  // block floor(q T / 8) .. floor((q + 1) T / 8) - 1, taken from the own XCD's block first, then from
-  // the next blocks in turn; work[8]: workgroups done claiming, the last of which zeroes work[0..8];
+  // work[0..7]: claim counters, zeroed by dyn_reset_kernel before the launch -- one queue over all
+  // positions, or (xcd_aware) one per XCD over the block floor(q T / 8) .. floor((q + 1) T / 8) - 1;
   // work[9]: hand-over faults (stays 0); work[32 + 32 p ..]: workgroup p's two mailbox slots, each a
   // 64-bit (claim number << 32 | position). A position < 0 means no work is left.
+  // The first claims of all workgroups (made together at the start, in workgroup order) are settled
+  // without atomics: workgroup p takes position p of the one queue, or (xcd_aware; round-robin
+  // dispatch puts p on XCD p mod 8) the (p / 8)-th position of block p mod 8 while that block has
+  // one; the counters then hand out the positions after these first ones.
   const unsigned T = static_cast<unsigned>(order.tiles);
   const int own_q = kDyn && xcd_aware ? xcc_id() : 0;
   int cur_q = own_q;
   uint64_t* mailbox = kDyn ? reinterpret_cast<uint64_t*>(work + 32 + 32 * static_cast<size_t>(blockIdx.x))
                            : nullptr;
-  auto claim_one = [&]() -> unsigned {   // wave 0: one claim on the current queue
+  auto queue_lo = [&](int q) -> unsigned {
+    return xcd_aware ? static_cast<unsigned>(static_cast<uint64_t>(q) * T / kNumXcds) : 0u;
+  };
+  auto queue_size = [&](int q) -> unsigned {
+    return xcd_aware ? static_cast<unsigned>(static_cast<uint64_t>(q + 1) * T / kNumXcds) - queue_lo(q) : T;
+  };
+  auto queue_first = [&](int q) -> unsigned {   // positions of queue q taken in the first round
+    const unsigned n = xcd_aware ? (P > q ? static_cast<unsigned>(P - 1 - q) / kNumXcds + 1 : 0u)
+                                 : static_cast<unsigned>(P);
+    return min(n, queue_size(q));
+  };
+  auto claim_one = [&]() -> unsigned {   // wave 0: one claim on the current queue, waited for
     unsigned r = 0;
     if (lane == 0) r = dyn_atomic_add(reinterpret_cast<unsigned*>(work) + cur_q, 1u);
     return __builtin_amdgcn_readfirstlane(r);
   };
-  auto claim = [&]() -> int {   // wave 0: the next position, rotating through empty queues; -1: none
+  // wave 0, XCD-aware, once the current queue is empty: read all eight counters at once and claim
+  // from the queue with the most positions left (ties: the nearest after the own XCD); -1 when
+  // none has any. A claim that loses a race for a queue's last positions reads again.
+  auto steal = [&]() -> int {
     for (;;) {
-      const unsigned c = claim_one();
-      const unsigned lo = xcd_aware ? static_cast<unsigned>(static_cast<uint64_t>(cur_q) * T / kNumXcds) : 0u;
-      const unsigned hi = xcd_aware ? static_cast<unsigned>(static_cast<uint64_t>(cur_q + 1) * T / kNumXcds) : T;
-      if (c < hi - lo) return static_cast<int>(lo + c);
-      if (!xcd_aware) return -1;
-      cur_q = (cur_q + 1) & (kNumXcds - 1);
-      if (cur_q == own_q) return -1;
+      const int q = lane & (kNumXcds - 1);
+      unsigned cnt = 0;
+      if (lane < kNumXcds) cnt = dyn_load_device(reinterpret_cast<unsigned*>(work) + q);
+      const unsigned avail = queue_size(q) - queue_first(q);
+      const unsigned left = lane < kNumXcds && cnt < avail ? avail - cnt : 0u;
+      const unsigned key = left ? (left << 3) | (7u - ((q - own_q) & (kNumXcds - 1))) : 0u;
+      unsigned best = 0;
+#pragma unroll
+      for (int l = 0; l < kNumXcds; ++l) best = max(best, __builtin_amdgcn_readlane(key, l));
+      if (best == 0) return -1;
+      cur_q = (own_q + 7 - static_cast<int>(best & 7u)) & (kNumXcds - 1);
+      const unsigned i = queue_first(cur_q) + claim_one();
+      if (i < queue_size(cur_q)) return static_cast<int>(queue_lo(cur_q) + i);
     }
   };
-  auto claims_done = [&]() {   // wave 0, once: count this workgroup out; the last one resets the counters
-    unsigned e = 0;
-    if (lane == 0) e = dyn_atomic_add(reinterpret_cast<unsigned*>(work) + 8, 1u);
-    e = __builtin_amdgcn_readfirstlane(e);
-    if (e == gridDim.x - 1 && lane <= 8) dyn_store_device(reinterpret_cast<unsigned*>(work) + lane, 0u);
+  auto claim = [&]() -> int {   // wave 0, waited for: the next position, or -1
+    const unsigned i = queue_first(cur_q) + claim_one();
+    if (i < queue_size(cur_q)) return static_cast<int>(queue_lo(cur_q) + i);
+    return xcd_aware ? steal() : -1;
   };
   auto mailbox_put = [&](int k, int pos) {   // wave 0
     if (lane == 0)
@@ -182,19 +209,26 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     }
   }
 
-  // the first tile: blockIdx.x, or (dynamic) claimed by wave 0 and handed over through the mailbox
+  // the first tile: blockIdx.x; dynamic: the first-round position, else claimed by wave 0 and
+  // handed over through the mailbox
   int first = static_cast<int>(blockIdx.x);
   int nxt = -1;   // dynamic: position of the tile after the current one, known from k step 4 on
   if constexpr (kDyn) {
-    if (wave == 0) {
-      first = claim();
-      mailbox_put(0, first);
-      if (first < 0) claims_done();
-      wait_vm<0>();   // the mailbox store has landed before the barrier
+    const int p = static_cast<int>(blockIdx.x);
+    const int fq = xcd_aware ? (p & (kNumXcds - 1)) : 0;
+    const unsigned fi = xcd_aware ? static_cast<unsigned>(p) / kNumXcds : static_cast<unsigned>(p);
+    if (fi < queue_size(fq)) {
+      first = static_cast<int>(queue_lo(fq) + fi);
+    } else {   // uniform over the workgroup
+      if (wave == 0) {
+        first = claim();
+        mailbox_put(0, first);
+        wait_vm<0>();   // the mailbox store has landed before the barrier
+      }
+      lds_barrier();
+      if (wave != 0) first = mailbox_take(0);
+      if (first < 0) return;   // every wave of the workgroup alike
     }
-    lds_barrier();
-    if (wave != 0) first = mailbox_take(0);
-    if (first < 0) return;   // every wave of the workgroup alike
   }
 
   // ---- load cursor (as gemm_kernel) ----
@@ -340,19 +374,20 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     c_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
     __builtin_amdgcn_sched_barrier(0);
   };
-  // dynamic: at the start of tile j's k step 0, wave 0 claims tile j + 1 and posts it; the other
-  // waves read it at the start of step 4 (the post, issued before step 0's loads, has landed by
-  // wave 0's wait at the end of step 2); the load cursor moves to tile j + 1 at the end of step
-  // nk - 5's loads, so nk >= 9. A claim or a read waits for its result at once, and with it for the
-  // wave's loads in flight: about one load latency per tile and wave. The claim number in each slot
-  // catches a stale read.
+  // dynamic: at the start of tile j's k step 0, wave 0 claims tile j + 1 and posts it in the
+  // mailbox; the other waves read it at the start of step 4 (the post, issued before step 0's loads,
+  // has landed by wave 0's wait at the end of step 2); the load cursor moves to tile j + 1 at the
+  // end of step nk - 5's loads, so nk >= 9. A claim or a read waits for its result at once, and
+  // with it for the wave's loads in flight: about one load latency per tile and wave. The hook is
+  // reached only from steps 0 .. 4, so every other step pays one compare: in the ping-pong schedule
+  // a memory half-period that grows beyond the other group's MFMAs lengthens the step. The claim
+  // number in each slot catches a stale read.
   auto dyn_hook = [&](int kt) {
     const int k = c_iter + 1;
     if (wave == 0) {
       if (kt == 0) {
         nxt = claim();
         mailbox_put(k, nxt);
-        if (nxt < 0) claims_done();
       }
     } else if (kt == 4) {
       nxt = mailbox_take(k);
@@ -361,7 +396,9 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   for (int tile = 0; kDyn || tile < my_tiles; ++tile) {
     zero_acc();
     for (int kt = 0; kt < nk; ++kt) {
-      if constexpr (kDyn) dyn_hook(kt);
+      if constexpr (kDyn) {
+        if (kt <= 4) dyn_hook(kt);
+      }
       memory_half();
       compute_half();
       lds_barrier();
@@ -425,8 +462,16 @@ hipError_t launch_pp(int dtype, const GemmLaunch& a, hipStream_t s) {
   }
 }
 
+// Zeroes the dynamic schedule's claim counters (vector stores), run on the GEMM's stream before it.
+__global__ __launch_bounds__(64) void dyn_reset_kernel(int32_t* __restrict__ work) {
+  if (threadIdx.x < 9) work[threadIdx.x] = 0;
+}
+
 // The dynamic schedule (claim counters and mailboxes in a.work).
 hipError_t launch_pp_dynamic(int dtype, const GemmLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL(dyn_reset_kernel, dim3(1), dim3(64), 0, s, a.work);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   switch (dtype) {
     case 0: return launch_pp_typed<false, false, 4, 4, 4, 1, 4, true>(a, s);
     case 1: return launch_pp_typed<true, false, 4, 4, 4, 1, 4, true>(a, s);
