@@ -90,7 +90,7 @@ PS_ORDERS = ([("row", 0, 1), ("col", 1, 1)] + [(f"panel_g{g}", 2, g) for g in (1
 PMC_PASSES = (("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("fetch", ["FETCH_SIZE"]),
               ("write", ["WRITE_SIZE"]),
               ("sq", ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
-                      "GRBM_GUI_ACTIVE"]))
+                      "SQ_INSTS_VALU_MFMA_MOPS_F16", "GRBM_GUI_ACTIVE"]))
 
 
 def _xcd_traffic_floor(xcds=8):
@@ -214,6 +214,10 @@ def counters():
             # sums the eight XCDs' busy clocks
             per[name]["mfma_busy_frac"] = r["SQ_VALU_MFMA_BUSY_CYCLES"] / max(
                 r["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0, 1.0)
+            # fp16 MFMA work the matrix pipes did, in units of 512 flops, against 2 M N K: 1.0 means
+            # no MFMA beyond the product's own
+            mops = r.get("SQ_INSTS_VALU_MFMA_MOPS_F16")
+            per[name]["mfma_flops_over_algorithmic"] = mops * 512.0 / FLOPS if mops else None
         return {"per": per, "factors": factors}, None
     except Exception as e:  # counters are reported as null with the reason
         return None, f"{type(e).__name__}: {e}"
@@ -721,6 +725,8 @@ def main():
             per_mode[name]["write_mb"] = round(per[name]["write_kib"] * 1024 / fac_w / 1e6, 1) if fac_w else None
             per_mode[name]["lds_conflict_frac"] = round(per[name]["lds_conflict_frac"], 5)
             per_mode[name]["mfma_busy_frac"] = round(per[name]["mfma_busy_frac"], 4)
+            f = per[name].get("mfma_flops_over_algorithmic")
+            per_mode[name]["mfma_flops_over_algorithmic"] = round(f, 4) if f is not None else None
         if fac_f and fac_w:
             mb = [per_mode[n]["fetch_mb"] + per_mode[n]["write_mb"] for n, _, _ in MODES]
             traffic = round(1e6 * sum(mb) / len(mb))

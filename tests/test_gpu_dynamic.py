@@ -170,6 +170,24 @@ def test_c3_8192_bf16_xcd_aware_equals_static_remap():
         del c
 
 
+def test_c4_rectangular_partial_groups():
+    """10240 x 6144 x 2048 fp16 (40 x 24 tiles, 960 over 256 workgroups): panel g16 (groups of 16,
+    16 and 8 rows) and serpentine s16 (a last strip of 8 columns), one queue and a queue per XCD
+    (blocks of 120 positions); bits of the static schedule, sampled rows against the oracle."""
+    M, N, K = 10240, 6144, 2048
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    rows = np.array(sorted({r * 256 + (r * 53) % 256 for r in range(40)}))
+    ref = og.gemm_rows(a, b, "f16", rows)
+    static = tbl.gemm(ad, bd, mode=tm.PANEL, group=16, persistent=True)
+    for mode, g in ((tm.PANEL, 16), (tm.PANEL | tm.XCD_REMAP, 16), (tm.SERPENTINE, 16),
+                    (tm.SERPENTINE | tm.XCD_REMAP, 16)):
+        c, tr = _run(ad, bd, mode, g, 0)
+        assert torch.equal(c, static), mode
+        check_tol(host64(c[torch.from_numpy(rows).cuda()]), ref, K, what=f"C4 dynamic {mode:#x} g{g}")
+        _check_trace(tr, mode, g, 40, 24)
+
+
 def test_binding_checks_workspace():
     a = torch.zeros((512, 512), dtype=torch.float16, device="cuda")
     with pytest.raises(ValueError):
