@@ -15,6 +15,8 @@ def test_gemm_rejects_host_tensors():
         tbl.gemm(a, b, c)
     with pytest.raises(ValueError, match="GPU tensor"):
         tbl.gemm_lds_layout(a, b, tbl.LDS_LAYOUTS[0], c)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tbl.gemm_dynamic(a, b, c, num_programs=4, workspace=torch.zeros(256, dtype=torch.int32))
 
 
 def test_other_entry_points_reject_host_tensors():
@@ -33,5 +35,9 @@ def test_binding_argument_shapes():
         tbl.gemm(torch.zeros((8, 16), dtype=torch.float16), torch.zeros((8, 16), dtype=torch.float16))
     with pytest.raises(TypeError):
         tbl.gemm(torch.zeros((8, 8), dtype=torch.float16), torch.zeros((8, 8), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        tbl.gemm_dynamic(torch.zeros((8, 16), dtype=torch.float16), torch.zeros((8, 16), dtype=torch.float16))
+    with pytest.raises(TypeError):
+        tbl.gemm_dynamic(torch.zeros((8, 8), dtype=torch.float16), torch.zeros((8, 8), dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         tbl.transpose_i32(torch.zeros((8, 8), dtype=torch.float32))
