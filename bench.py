@@ -29,7 +29,8 @@ Printed: one JSON line with
                without the XCD remap, and group-major g4 over 2x2 clusters of tiles with the remap;
                then both orders under the dynamic work-queue schedule, with one claim queue and
                with one per XCD): TFLOP/s, % of peak and predicted L2 hit rate of each static order
-               (the 70 % target), and the MFMA ceiling on its bf16 operands;
+               (the 70 % target), and the MFMA ceiling on its bf16 operands; then the two remapped
+               orders on fp16 uniform[-1,1] operands of the same shape, with their own ceiling;
   cpu_baseline the fp64 CPU oracle on a sample of output rows of the same product.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-counters] [--no-cpu]
@@ -406,11 +407,32 @@ def target_check(tbl, torch, stream, reps=10):
     best = max(res, key=lambda n: res[n]["tflops"])
     ceiling = mfma_ceiling(tbl, torch, stream, ad, bd, gemm_tflops=res[best]["tflops"])
     del ad, bd, c
+    # the same shape in fp16 (uniform[-1, 1] inputs, fp16 out): the fp16-peak form of the target,
+    # for the two remapped orders, with the MFMA-only rate on these fp16 operands
+    a, b = synth.gemm_operands(C3, C3, C3, "f16", "uniform", seed=0)
+    ad, bd = _dev16(a, torch, torch.float16), _dev16(b, torch, torch.float16)
+    del a, b
+    c = torch.empty((C3, C3), dtype=torch.float16, device="cuda")
+    res16 = {}
+    for name, mode, g in C3_MODES[2:4]:
+        def launch():
+            tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=True, stream=stream.cuda_stream)
+        launch()
+        launch()
+        ms = _median_ms(torch, stream, launch, reps)
+        tf = flops / (ms * 1e-3) / 1e12
+        res16[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2)}
+    best16 = max(res16, key=lambda n: res16[n]["tflops"])
+    ceiling16 = mfma_ceiling(tbl, torch, stream, ad, bd, gemm_tflops=res16[best16]["tflops"])
+    del ad, bd, c
     return {"workload": "gemm 8192^3 bf16 N(0,1)/sqrt(K) -> bf16 (fp32 accumulate), 256x256x32 tiles, "
                         "persistent stride schedule (and the dynamic work-queue schedule) over CUs x occupancy programs",
             "programs": tbl.default_num_programs(C3, C3, C3, tbl.BF16, persistent=True),
             "orders": res, "best": best, "best_pct_peak": res[best]["pct_peak"], "target_pct_peak": 70.0,
-            "mfma_ceiling_same_data": ceiling}
+            "mfma_ceiling_same_data": ceiling,
+            "f16": {"workload": "the same shape in fp16: uniform[-1,1] inputs, fp16 out, persistent",
+                    "orders": res16, "best": best16, "best_pct_peak": res16[best16]["pct_peak"],
+                    "mfma_ceiling_same_data": ceiling16}}
 
 
 def _page_printed():
