@@ -122,6 +122,24 @@ def test_more_workgroups_than_tiles():
         _check_trace(tr, mode, 1, 4, 3)
 
 
+@pytest.mark.parametrize("mode", [tm.PANEL, tm.PANEL | tm.XCD_REMAP])
+def test_more_workgroups_than_resident(mode):
+    """1024 and 777 workgroups on 256 tiles: the first 256 take their first-round tiles, the rest
+    (dispatched as earlier ones finish) find every queue empty and leave."""
+    M, N, K = 4096, 4096, 512
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=9)
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    static = tbl.gemm(ad, bd, mode=mode & ~tm.XCD_REMAP, group=4, tile=(256, 256, 32))
+    rows = np.arange(3, M, 97)
+    ref = og.gemm_rows(a, b, "f16", rows)
+    for P in (1024, 777):
+        c, tr = _run(ad, bd, mode, 4, P)
+        assert torch.equal(c, static), P
+        check_tol(host64(c)[rows], ref, K, what=f"P={P} mode {mode:#x}")
+        seqs = _check_trace(tr, mode, 4, 16, 16)
+        assert max(seqs) < 256 and all(len(v) == 1 for v in seqs.values())
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_ragged_fp32_out(dtype):
     M, N, K = 1000, 776, 1000     # partial tiles at M and N edges, a k tail of 8
