@@ -50,13 +50,15 @@ def test_printed_tables_on_gpu(fixture, mode, group, grid):
 
 
 CLUSTER_GRIDS = [(8, 8), (16, 16), (32, 32), (40, 24), (12, 18), (64, 64)]
+CLUSTER_SHAPES = [(2, 1), (1, 2), (2, 2), (4, 2), (3, 3), (8, 1)]
+CLUSTER_CASES = [(gm, gn, cm, cn) for gm, gn in CLUSTER_GRIDS for cm, cn in CLUSTER_SHAPES
+                 if gm % cm == 0 and gn % cn == 0]
+CLUSTER_PARTIAL = [(gm, gn, cm, cn) for gm, gn in CLUSTER_GRIDS for cm, cn in CLUSTER_SHAPES
+                   if gm % cm or gn % cn]
 
 
-@pytest.mark.parametrize("gm,gn", CLUSTER_GRIDS)
-@pytest.mark.parametrize("cm,cn", [(2, 1), (1, 2), (2, 2), (4, 2), (3, 3), (8, 1)])
+@pytest.mark.parametrize("gm,gn,cm,cn", CLUSTER_CASES)
 def test_cluster_tables_match_oracle(gm, gn, cm, cn):
-    if gm % cm or gn % cn:
-        pytest.skip("cluster does not tile this grid")
     cgm, cgn = gm // cm, gn // cn
     for remap in (0, tm.XCD_REMAP):
         for mode in (tm.ROW, tm.COL, tm.PANEL, tm.MORTON, tm.XOR, tm.SERPENTINE):
@@ -68,6 +70,16 @@ def test_cluster_tables_match_oracle(gm, gn, cm, cn):
                     assert st == tbl.WARN_NOT_BIJECTIVE
                 else:
                     assert st == tbl.OK and tm.is_bijective(om, on, gm, gn)
+
+
+@pytest.mark.parametrize("gm,gn,cm,cn", CLUSTER_PARTIAL)
+def test_partial_clusters_rejected(gm, gn, cm, cn):
+    """A cluster that does not tile the grid is refused before any launch (as the oracle refuses it)."""
+    with pytest.raises(tbl.TblError) as e:
+        _gpu_table(tm.ROW | tbl.cluster(cm, cn), gm, gn, 1)
+    assert e.value.status == tbl.ERR_SHAPE
+    with pytest.raises(ValueError):
+        tm.tile_table(tm.ROW, gm, gn, 1, cluster=(cm, cn))
 
 
 def test_page3_example2_on_gpu():
