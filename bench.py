@@ -788,7 +788,7 @@ def main():
         "l2_model": l2_model,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "gemm_pp_kernel<f16,f16-out> (256x256x32, 8 waves)", "kernel_avg_ms": round(kernel_ms, 5),
+                     "kernel": "gemm_pp_kernel<f16,f16-out> (256x256x32, 8 waves, 16x16x32 MFMA)", "kernel_avg_ms": round(kernel_ms, 5),
                      "algorithmic_flops_per_launch": FLOPS,
                      "algorithmic_bytes_per_launch": 2 * (M * K + K * N + M * N),
                      # counter KiB per true KiB on a 256 MiB device copy; traffic = counters / factor

@@ -200,11 +200,13 @@ int64_t tbl_gemm_dynamic_workspace(int num_programs);
  * Layout swizzling"), on 16-byte chunks. A sits in LDS as rows of 32 k (4 chunks): row r stores
  * logical chunk c at c XOR ((r / a_per_phase) mod a_max_phase). B sits k-major as rows of 256 n
  * (32 chunks): row k stores chunk c at c XOR ((((k / b_per_phase) mod b_max_phase) * b_vec) mod 32).
- * The layout changes which LDS banks the operand reads hit, never the result: every variant
- * returns the same bits as tbl_gemm_tiled with 256x256x32 tiles.
+ * The variants run the 256x256 kernel in its 32x32x16-MFMA form, whose operand reads these
+ * layouts were chosen for (tbl_gemm itself runs the 16x16x32 form, with A at (2,4) and its own B
+ * layout). The layout changes which LDS banks the operand reads hit, never the result: every
+ * variant returns the same bits as tbl_gemm_tiled with 256x256x32 tiles.
  *   dtype         TBL_F16 only (TBL_ERR_DTYPE otherwise).
  *   (a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase) one of the compiled variants:
- *                 (4,4,4,1,4) the tbl_gemm layouts; A varied with B at its default:
+ *                 (4,4,4,1,4) conflict-free for the 32x32x16 reads; A varied with B at its default:
  *                 (1,1,...) no swizzle, (1,4), (2,4), (4,2), (8,4); B varied with A at its default:
  *                 (...,1,1,1) no swizzle, (1,1,4), (2,1,4), (4,1,2), (4,2,2), (8,1,4).
  *                 TBL_ERR_INVALID_ARG for any other combination.
@@ -269,9 +271,9 @@ int tbl_predict_l2(int swizzle_mode, int grid_m, int grid_n, int grid_k, int gro
  * measurement aid for the GEMM's roofline, not part of the method). Each of the 4 waves of each of
  * ``workgroups`` 256-thread workgroups loads four 16-byte fragments of A and four of B (wave w,
  * fragment q, lane l takes the 8 values starting at element 8 x (((4 w + q) x 64 + l) mod (elems / 8)))
- * and then runs ``iters`` rounds of 16 independent 32x32x16 MFMAs (fp32 accumulate) in the GEMM's
- * issue order, with no other memory traffic. The MFMA count is 16 x iters x 4 x workgroups, each
- * 2 x 32 x 32 x 16 flops. The chip lowers its core clock as the operands' switching activity
+ * and then runs ``iters`` rounds of 32 independent 16x16x32 MFMAs (fp32 accumulate, accumulators
+ * in VGPRs) in the GEMM's issue order, with no other memory traffic. The MFMA count is
+ * 32 x iters x 4 x workgroups, each 2 x 16 x 16 x 32 flops. The chip lowers its core clock as the operands' switching activity
  * rises, so this rate, not the clock-only figure, bounds what the GEMM can reach on the same data.
  *   A, B        device pointers to at least ``elems`` 16-bit values each, 16-byte aligned.
  *   elems       >= 8.

@@ -1,8 +1,8 @@
 """tbl_mfma_rate on the GPU: the MFMA stream computes what it claims, and reports its clock.
 
-With every operand value equal to a (in A) and b (in B), each 32x32x16 MFMA adds 16 a b to each of
-a lane's 16 accumulator elements, so after ``iters`` rounds of 16 MFMAs every lane's sink value is
-16 x 16 x iters x 16 a b, exact in fp32 for the small integers used here.
+With every operand value equal to a (in A) and b (in B), each 16x16x32 MFMA adds 32 a b to each of
+a lane's 4 accumulator elements, so after ``iters`` rounds of 32 MFMAs every lane's sink value is
+32 x 4 x iters x 32 a b, exact in fp32 for the small integers used here.
 """
 
 import pytest
@@ -21,13 +21,13 @@ def test_constant_operands_give_exact_sums(dtype, a_val, b_val, elems):
     iters, wg = 50, 7
     flops, out, cycles = tbl.mfma_rate(a, b, workgroups=wg, iters=iters)
     torch.cuda.synchronize()
-    assert flops == 2 * 32 * 32 * 16 * 16 * iters * 4 * wg
-    want = 16 * 16 * iters * 16 * a_val * b_val
+    assert flops == 2 * 16 * 16 * 32 * 32 * iters * 4 * wg
+    want = 32 * 4 * iters * 32 * a_val * b_val
     assert torch.all(out == want), (out.min().item(), out.max().item(), want)
     cyc = cycles.cpu()
     assert cyc[0] > 0 and cyc[1] > 0
-    # a 32x32x16 MFMA takes at least 32 core cycles per SIMD: 16 of them per round
-    assert cyc[0] >= 16 * 32 * iters
+    # a 16x16x32 MFMA takes at least 16 core cycles per SIMD: 32 of them per round
+    assert cyc[0] >= 32 * 16 * iters
 
 
 def test_random_operands_run_and_clock_is_plausible():

@@ -146,6 +146,57 @@ __device__ __forceinline__ int swz_b(int k) {
   return (((k / kBPP) % kBMP) * kBV) & (kChunks - 1);
 }
 
+// The 16 x 16 x 32 MFMA (v_mfma_f32_16x16x32_{f16,bf16}); its lane layout, checked on the device:
+// first operand lane l holds row l mod 16, k 8 (l / 16) .. + 7; second operand lane l holds k
+// 8 (l / 16) .. + 7 of column l mod 16; the result lane l holds rows 4 (l / 16) .. + 3 of column
+// l mod 16. Issued with B as the first operand (as the 32 x 32 form), each lane ends up holding 4
+// consecutive output columns of one row.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <bool kBf16>
+__device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
+  if constexpr (kBf16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  }
+}
+
+// B swizzle for the 16 x 16 x 32 operand reads: chunk c of row k at c XOR (4 (k mod 4) + 2 ((k / 8)
+// mod 2)). One transposing read of a 32-lane phase touches 16 column bytes of rows k0 .. k0 + 3 and
+// k0 + 8 .. k0 + 11; the first term spreads the four rows of each quad over the 256-byte bank window
+// (as the 32 x 32 layout's XOR does), the second separates the two quads, so the phase's 32 pieces
+// of 8 bytes land on 32 distinct bank pairs.
+__device__ __forceinline__ int swz_b16(int k) { return (4 * (k & 3)) | (2 * ((k >> 3) & 1)); }
+
+// Store a wave's sub-tile of 16 x 16 accumulator blocks: lane l holds row (l mod 16) and columns
+// 4 (l / 16) .. + 3 of block (i, j), packed into 8 bytes (16-bit output) or 16 bytes (fp32); each
+// store writes 32 (64) contiguous bytes of 16 rows.
+template <int BM, int BN, int WM, int WN, int TM, int TN, bool kBf16, bool kF32Out>
+__device__ __forceinline__ void store_tile16(f32x4_t (&acc)[TM][TN], void* __restrict__ Cv, int M, int N,
+                                             int tile_m, int tile_n, int wm, int wn, int lane) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const size_t row = static_cast<size_t>(tile_m) * BM + wm * WM + i * 16 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const size_t col = static_cast<size_t>(tile_n) * BN + wn * WN + j * 16 + 4 * (lane >> 4);
+      if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
+      if constexpr (kF32Out) {
+        float* C = static_cast<float*>(Cv);
+        *reinterpret_cast<float4*>(C + row * N + col) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+        uint16_t* C = static_cast<uint16_t*>(Cv);
+        const uint32_t lo = to_out16(acc[i][j][0], kBf16) | (static_cast<uint32_t>(to_out16(acc[i][j][1], kBf16)) << 16);
+        const uint32_t hi = to_out16(acc[i][j][2], kBf16) | (static_cast<uint32_t>(to_out16(acc[i][j][3], kBf16)) << 16);
+        *reinterpret_cast<uint2*>(C + row * N + col) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
 // Store a wave's sub-tile of the output tile (tile_m, tile_n); the wave sits at (wm, wn) in the
 // workgroup's wave grid and holds TM x TN accumulator blocks of 32 x 32.
 // Lane l holds, for MFMA block (i, j) and group g, row (l mod 32) and columns

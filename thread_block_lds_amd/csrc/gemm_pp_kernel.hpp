@@ -1,18 +1,23 @@
 // The 256 x 256 GEMM kernel with eight waves in two alternating groups ("ping-pong").
 //
 // Same computation as gemm_kernel (gemm_kernel.hpp): workgroup p walks tile ids p, p + P, ... and
-// accumulates each output tile in fp32 over k in ascending 16-deep MFMA steps, so the results are
-// bit-identical to it. With kDyn the tiles come instead from claim counters (the dynamic schedule
+// accumulates each output tile in fp32 over k in ascending MFMA steps. In the 32 x 32 x 16 form
+// (kM16 = false) the steps are 16 deep, exactly as gemm_kernel's, so the results are bit-identical
+// to it; the 16 x 16 x 32 form (kM16, the default kernel) takes 32-deep steps, and on gfx950 one
+// 32-deep step leaves the same fp32 bits as two 16-deep ones (checked on the device on random fp16
+// and bf16 operands, and by the layout-variant tests, which compare the two forms bit for bit).
+// With kDyn the tiles come instead from claim counters (the dynamic schedule
 // that "CUDA Thread Block Swizzle", section "CUDA Thread Block Swizzle Benchmark", notes its
 // persistent loop lacks); only the schedule changes, never a tile's arithmetic. What differs from
 // gemm_kernel is how the work is laid out over the CU:
 //   * 512 threads = 8 wave64s, two per SIMD. Group 0 (waves 0-3) owns output rows 0-127 of the
 //     tile, group 1 (waves 4-7) rows 128-255; inside a group wave w owns columns 64 (w mod 4) ..
-//     + 63, a 128 x 64 sub-tile of 4 x 2 blocks of 32 x 32 (128 accumulator registers).
+//     + 63, a 128 x 64 sub-tile (128 accumulator registers): 4 x 2 blocks of 32 x 32, or with kM16
+//     8 x 4 blocks of 16 x 16.
 //   * Each group alternates a memory half-period M(s) -- read all operand fragments of k step s
 //     from LDS into registers, issue this wave's four direct loads of step s + 4, wait until its
-//     loads of step s + 1 have landed -- and a compute half-period C(s) -- the step's 16 MFMAs
-//     back to back, then the epilogue if s ends a tile. Group 1 starts one half-period late, so
+//     loads of step s + 1 have landed -- and a compute half-period C(s) -- the step's 16 MFMAs of
+//     32 x 32 x 16 (or 32 of 16 x 16 x 32) back to back, then the epilogue if s ends a tile. Group 1 starts one half-period late, so
 //     while one wave of a SIMD computes, the other issues its memory operations; a wave stalled on
 //     a load or an LDS read no longer idles the matrix pipe.
 //   * Every half-period ends with a workgroup barrier (which also waits for the wave's LDS reads).
@@ -20,7 +25,9 @@
 //     and step t is read only after both groups' M(t - 1) have closed; loads of step s + 4 go to
 //     the stage of step s - 1, which both groups finished reading before the barrier preceding the
 //     first M(s). Five 32 KiB stages hold the steps in flight.
-// LDS layout, swizzles and direct loads are those of gemm_kernel.
+// LDS layout, swizzles and direct loads are those of gemm_kernel, except that the kM16 form reads
+// its operands in other lane patterns and so takes other chunk XORs: A by (row / 2) mod 4 and B by
+// swz_b16 (both conflict-free for its reads, measured with the LDS bank-conflict counter).
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -56,7 +63,7 @@ __device__ __forceinline__ unsigned dyn_load_device(const unsigned* p) {   // de
 }
 
 template <bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4, int kBPP = 1, int kBMP = 4,
-          bool kDyn = false>
+          bool kDyn = false, bool kM16 = false>
 __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B,
                                                              void* __restrict__ Cv, int M, int N, int K,
@@ -65,7 +72,8 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
                                                              int32_t* __restrict__ work, int xcd_aware) {
   constexpr int BM = 256, BN = 256;
   constexpr int WM = 128, WN = 64;                 // wave sub-tile
-  constexpr int TM = WM / 32, TN = WN / 32;        // 4 x 2 MFMA blocks per wave
+  constexpr int TM = WM / 32, TN = WN / 32;        // 4 x 2 MFMA blocks of 32 x 32 per wave
+  constexpr int TM16 = WM / 16, TN16 = WN / 16;    // or 8 x 4 blocks of 16 x 16 (kM16)
   constexpr int kBRow = BN * 2;                    // bytes of one B row (one k) in LDS
   constexpr int kAStage = BM * kARow;
   constexpr int kBStage = kBK * kBRow;
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   for (int j = 0; j < kBInst; ++j) {
     const int o = (wave * kBInst + j) * 1024 + 16 * lane;
     const int k = o / kBRow;
-    const int chunk = ((o % kBRow) >> 4) ^ swz_b<kBV, kBPP, kBMP, kBChunks>(k);
+    const int chunk = ((o % kBRow) >> 4) ^ (kM16 ? swz_b16(k) : swz_b<kBV, kBPP, kBMP, kBChunks>(k));
     b_voff[j] = (k * N + chunk * 8) * 2;
   }
   // ---- per-lane constants of the operand reads ----
@@ -206,6 +214,22 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
       const int n = wn * WN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
       const int chunk = (n >> 3) ^ swz_b<kBV, kBPP, kBMP, kBChunks>(k);
       b_rd[j] = kAStage + k * kBRow + chunk * 16 + (n & 7) * 2;
+    }
+  }
+  // 16 x 16 x 32 reads: A lane l takes row (l mod 16) of a 16-row block, chunk l / 16 (k 8 (l / 16)
+  // .. + 7); B lane L of 16-lane group G addresses the 8-byte row piece k = 8 G + (L mod 16) / 4,
+  // columns 4 (L mod 4) .. + 3 of a 16-column block, which the transposing read turns into 4 k of
+  // one column per lane (twice: k and k + 4)
+  int a_rd16 = 0, b_rd16[TN16];
+  if constexpr (kM16) {
+    const int row = grp * WM + (lane & 15);
+    a_rd16 = row * kARow + ((lane >> 4) ^ swz_a<kAPP, kAMP>(row)) * 16;
+    const int r = lane & 15;
+    const int k = 8 * (lane >> 4) + (r >> 2);
+#pragma unroll
+    for (int j = 0; j < TN16; ++j) {
+      const int n = wn * WN + j * 16 + 4 * (r & 3);
+      b_rd16[j] = kAStage + k * kBRow + ((n >> 3) ^ swz_b16(k)) * 16 + (n & 7) * 2;
     }
   }
 
@@ -286,8 +310,23 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
 
   // ---- operand fragments of one step: [k half][block] ----
   uint4 af[2][TM], bf[2][TN];
+  uint4 af16[TM16], bf16f[TN16];
   auto read_step = [&](int stage) {
     const char* base = lds + stage * kStage;
+    if constexpr (kM16) {
+#pragma unroll
+      for (int i = 0; i < TM16; ++i)
+        af16[i] = *reinterpret_cast<const uint4*>(base + a_rd16 + i * 16 * kARow);
+#pragma unroll
+      for (int j = 0; j < TN16; ++j) {
+        const char* p = base + b_rd16[j];
+        const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+        const uint2 hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                       (lds_s16x4_t*)(p + 4 * kBRow)));
+        bf16f[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -305,9 +344,19 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   };
 
   f32x16_t acc[TM][TN];
+  f32x4_t acc16[TM16][TN16];
   auto zero_acc = [&]() {
     float z;
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    if constexpr (kM16) {
+#pragma unroll
+      for (int i = 0; i < TM16; ++i)
+#pragma unroll
+        for (int j = 0; j < TN16; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc16[i][j][r] = z;
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -365,12 +414,19 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   };
   // C(s): the step's 16 MFMAs
   auto compute_half = [&]() {
+    if constexpr (kM16) {   // 32 MFMAs of 16 x 16 x 32
+#pragma unroll
+      for (int i = 0; i < TM16; ++i)
+#pragma unroll
+        for (int j = 0; j < TN16; ++j) acc16[i][j] = mfma16x16x32<kBf16>(bf16f[j], af16[i], acc16[i][j]);
+    } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<kBf16>(bf[h][j], af[h][i], acc[i][j]);
+    }
     c_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -406,7 +462,10 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     }
     // the epilogue overlaps the other group's last compute half-period
     record_time();
-    store_tile<BM, BN, WM, WN, TM, TN, kBf16, kF32Out>(acc, Cv, M, N, c_m, c_n, grp, wn, lane);
+    if constexpr (kM16)
+      store_tile16<BM, BN, WM, WN, TM16, TN16, kBf16, kF32Out>(acc16, Cv, M, N, c_m, c_n, grp, wn, lane);
+    else
+      store_tile<BM, BN, WM, WN, TM, TN, kBf16, kF32Out>(acc, Cv, M, N, c_m, c_n, grp, wn, lane);
     if constexpr (kDyn) {
       c_t = nxt;
       ++c_iter;
@@ -427,9 +486,16 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   wait_vm<0>();                  // no direct load may still be writing this workgroup's LDS
 }
 
+// The default 256 x 256 kernel: 16 x 16 x 32 MFMAs with A swizzled by (row / 2) mod 4 (the
+// (perPhase 2, maxPhase 4) member of the chunk-XOR family: conflict-free for 16 rows x 2 chunks
+// per half-wave, where (row / 4) mod 4 costs twice the cycles) and B by swz_b16. The 32 x 32 x 16
+// form (kM16 = false) serves the LDS-layout variants of gemm_layouts.hip.
+constexpr int kM16APP = 2, kM16AMP = 4;
+
 template <bool kBf16, bool kF32Out>
 const void* pp_kernel_ptr() {
-  return reinterpret_cast<const void*>(&gemm_pp_kernel<kBf16, kF32Out>);
+  return reinterpret_cast<const void*>(
+      &gemm_pp_kernel<kBf16, kF32Out, kM16APP, kM16AMP, 4, 1, 4, false, true>);
 }
 
 const void* pp_kernel_for(int dtype) {
@@ -443,9 +509,9 @@ const void* pp_kernel_for(int dtype) {
 }
 
 template <bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4, int kBPP = 1, int kBMP = 4,
-          bool kDyn = false>
+          bool kDyn = false, bool kM16 = false>
 hipError_t launch_pp_typed(const GemmLaunch& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_pp_kernel<kBf16, kF32Out, kAPP, kAMP, kBV, kBPP, kBMP, kDyn>), dim3(a.num_programs),
+  hipLaunchKernelGGL((gemm_pp_kernel<kBf16, kF32Out, kAPP, kAMP, kBV, kBPP, kBMP, kDyn, kM16>), dim3(a.num_programs),
                      dim3(kPPThreads), 0, s, static_cast<const uint16_t*>(a.A),
                      static_cast<const uint16_t*>(a.B), a.C, a.M, a.N, a.K, a.order, a.num_programs,
                      a.trace, a.work, a.xcd_aware);
@@ -454,10 +520,10 @@ hipError_t launch_pp_typed(const GemmLaunch& a, hipStream_t s) {
 
 hipError_t launch_pp(int dtype, const GemmLaunch& a, hipStream_t s) {
   switch (dtype) {
-    case 0: return launch_pp_typed<false, false>(a, s);
-    case 1: return launch_pp_typed<true, false>(a, s);
-    case 2: return launch_pp_typed<false, true>(a, s);
-    case 3: return launch_pp_typed<true, true>(a, s);
+    case 0: return launch_pp_typed<false, false, kM16APP, kM16AMP, 4, 1, 4, false, true>(a, s);
+    case 1: return launch_pp_typed<true, false, kM16APP, kM16AMP, 4, 1, 4, false, true>(a, s);
+    case 2: return launch_pp_typed<false, true, kM16APP, kM16AMP, 4, 1, 4, false, true>(a, s);
+    case 3: return launch_pp_typed<true, true, kM16APP, kM16AMP, 4, 1, 4, false, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -473,10 +539,10 @@ hipError_t launch_pp_dynamic(int dtype, const GemmLaunch& a, hipStream_t s) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (dtype) {
-    case 0: return launch_pp_typed<false, false, 4, 4, 4, 1, 4, true>(a, s);
-    case 1: return launch_pp_typed<true, false, 4, 4, 4, 1, 4, true>(a, s);
-    case 2: return launch_pp_typed<false, true, 4, 4, 4, 1, 4, true>(a, s);
-    case 3: return launch_pp_typed<true, true, 4, 4, 4, 1, 4, true>(a, s);
+    case 0: return launch_pp_typed<false, false, kM16APP, kM16AMP, 4, 1, 4, true, true>(a, s);
+    case 1: return launch_pp_typed<true, false, kM16APP, kM16AMP, 4, 1, 4, true, true>(a, s);
+    case 2: return launch_pp_typed<false, true, kM16APP, kM16AMP, 4, 1, 4, true, true>(a, s);
+    case 3: return launch_pp_typed<true, true, kM16APP, kM16AMP, 4, 1, 4, true, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
