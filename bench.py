@@ -9,7 +9,8 @@ the same HBM-resident inputs.
 
 Printed: one JSON line with
   value        whole-step throughput, TFLOP/s (12 GEMMs x 2*4096^3 flops / step wall time);
-  modes        per variant: warm kernel time (HIP events on the launch stream, inside the steps),
+  modes        per variant: warm kernel time (HIP events on the launch stream around 20 back-to-back
+               launches of that variant, after the timed steps),
                cold kernel time (median and min over launches that each follow a 512 MiB read that
                evicts the L2s and the memory-side cache, as the page's timing clears L2 first),
                TFLOP/s and % of the 2.5 PFLOP/s dense fp16 MFMA peak; the L2 (TCC) hit rate, its
@@ -18,7 +19,9 @@ Printed: one JSON line with
                the library's tbl_predict_l2 for eight private L2s;
   l2_model     Spearman rank correlations of the prediction with the measured hit rate, fetch bytes
                and cold throughput;
-  roofline     the GEMM kernel: average launch time -> TFLOP/s against the MFMA peak, and its HBM
+  roofline     the GEMM kernel: average launch time (two HIP events on the launch stream around the
+               timed steps, over the number of launches; no event between launches, since one
+               costs the next launch several microseconds) -> TFLOP/s against the MFMA peak, and its HBM
                traffic per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size);
   mfma_ceiling_same_data
                tbl_mfma_rate on the same operands: the GEMM's MFMA stream with no memory traffic,
@@ -73,6 +76,7 @@ FLOPS = 2.0 * M * N * K
 COPY_BYTES = 256 << 20        # calibration copy for the HBM traffic counters
 FLUSH_BYTES = 512 << 20       # > 8 x 4 MB L2 + 256 MB memory-side cache
 COLD_REPS = 10
+WARM_REPS = 20
 TR_SIZE = 16384
 TR_LAYOUTS = [("naive", 0), ("padded", 1), ("xor", 2)]
 C3 = 8192                     # the persistent bf16 workload of the 70 %-of-peak target
@@ -292,6 +296,18 @@ def cpu_baseline(a, b, budget_s=10.0):
                       f"{total_t:.1f} s wall"}
 
 
+def _region_ms(torch, stream, launch, reps):
+    """Average time of ``reps`` back-to-back launches: two HIP events on the launch stream around
+    all of them (an event between two launches would delay the second)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def time_transpose(tbl, torch, stream, reps=10):
     x = _transpose_input(TR_SIZE, TR_SIZE, 0)
     out = torch.empty((TR_SIZE, TR_SIZE), dtype=torch.int32, device="cuda")
@@ -299,27 +315,15 @@ def time_transpose(tbl, torch, stream, reps=10):
     for name, layout in TR_LAYOUTS:
         for _ in range(2):
             tbl.transpose_i32(x, out, layout=layout, stream=stream.cuda_stream)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for e0, e1 in evs:
-            e0.record(stream)
-            tbl.transpose_i32(x, out, layout=layout, stream=stream.cuda_stream)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
+        ms = _region_ms(torch, stream, lambda: tbl.transpose_i32(x, out, layout=layout,
+                                                                 stream=stream.cuda_stream), reps)
         gbs = 8.0 * TR_SIZE * TR_SIZE / (ms * 1e-3) / 1e9
         res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     # context: a plain device copy of the same bytes (torch's copy kernel), what this board's HBM
     # sustains for one read stream and one write stream
     for _ in range(2):
         out.copy_(x)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in evs:
-        e0.record(stream)
-        out.copy_(x)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
+    copy_ms = _region_ms(torch, stream, lambda: out.copy_(x), reps)
     copy_gbs = 8.0 * TR_SIZE * TR_SIZE / (copy_ms * 1e-3) / 1e9
     best = max(res, key=lambda n: res[n]["GB/s"])
     del x, out
@@ -674,25 +678,39 @@ def main():
     flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
-        for i, (_, mode, g) in enumerate(MODES):
-            if events is not None:
-                events[i][0].record(stream)
+    def step():
+        for _, mode, g in MODES:
             tbl.gemm(ad, bd, c, mode=mode, group=g, stream=stream.cuda_stream)
-            if events is not None:
-                events[i][1].record(stream)
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in MODES] for _ in range(args.steps)]
+    # The timed region holds only the launches: an event recorded between two launches costs the
+    # next one several microseconds on this device, so the kernels' average duration comes from two
+    # events on the launch stream around the whole region (back-to-back launches of one stream).
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
+    region[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    kernel_ms = region[0].elapsed_time(region[1]) / (args.steps * len(MODES))
+
+    # warm time per variant: WARM_REPS back-to-back launches of it between two events, after two
+    # unmeasured ones
+    warm = {}
+    for name, mode, g in MODES:
+        for _ in range(2):
+            tbl.gemm(ad, bd, c, mode=mode, group=g, stream=stream.cuda_stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(WARM_REPS):
+            tbl.gemm(ad, bd, c, mode=mode, group=g, stream=stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warm[name] = e0.elapsed_time(e1) / WARM_REPS
 
     # cold launches: each after a fill that evicts every cache level, outside the events
     cold = {}
@@ -715,11 +733,8 @@ def main():
 
     ms_step = wall * 1e3 / args.steps
     per_mode = {}
-    all_ms = []
-    for i, (name, mode, g) in enumerate(MODES):
-        ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
-        all_ms += ms
-        avg = sum(ms) / len(ms)
+    for name, mode, g in MODES:
+        avg = warm[name]
         tf = FLOPS / (avg * 1e-3) / 1e12
         cmed, cmin = statistics.median(cold[name]), min(cold[name])
         per_mode[name] = {"mode": mode, "group": g, "ms": round(avg, 5), "tflops": round(tf, 1),
@@ -759,7 +774,6 @@ def main():
         if fac_f:
             l2_model["spearman_pred_vs_measured_fetch"] = round(rank_corr(
                 [pred[n]["fetch_mb"] for n in names], [per_mode[n]["fetch_mb"] for n in names]), 3)
-    kernel_ms = sum(all_ms) / len(all_ms)
     achieved = FLOPS / (kernel_ms * 1e-3) / 1e12
     best = max(per_mode, key=lambda n: per_mode[n]["tflops"])
     value = len(MODES) * FLOPS / (ms_step * 1e-3) / 1e12
@@ -789,6 +803,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": "gemm_pp_kernel<f16,f16-out> (256x256x32, 8 waves, 16x16x32 MFMA)", "kernel_avg_ms": round(kernel_ms, 5),
+                     "kernel_avg_how": "HIP events on the launch stream around the timed steps / launches",
                      "algorithmic_flops_per_launch": FLOPS,
                      "algorithmic_bytes_per_launch": 2 * (M * K + K * N + M * N),
                      # counter KiB per true KiB on a 256 MiB device copy; traffic = counters / factor
