@@ -258,6 +258,25 @@ def test_ragged_integer_exact_and_untouched_padding(dtype):
         assert torch.all(big[M:] == 12345.0), tile
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("tile", [64, 128, 256])
+def test_ragged_integer_16bit_out_is_the_rounded_exact_sum(dtype, tile):
+    # integer inputs: the fp32 sums are exact, so the 16-bit output must be the exact sum rounded
+    # to nearest even in the output type (torch's CPU conversion serves as that rounding); no
+    # element outside C may be written
+    M, N, K = 300, 264, 1000   # sums reach past 256 (bf16) and 2048 (fp16): rounding is exercised
+    a = synth.int_valued((M, K), 43, -7, 7, dtype)
+    b = synth.int_valued((K, N), 44, -7, 7, dtype)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    want = torch.from_numpy(og.gemm(a, b, dtype)).to(tdt)
+    big = torch.full((M + 64, N), -5.0, dtype=tdt, device="cuda")
+    c = big[:M]
+    tbl.gemm(dev16(a, dtype), dev16(b, dtype), c=c, tile=(tile, tile, 32), mode=tm.PANEL, group=2)
+    torch.cuda.synchronize()
+    assert torch.equal(c.cpu().view(torch.int16), want.view(torch.int16)), (dtype, tile)
+    assert torch.all(big[M:] == -5.0), (dtype, tile)
+
+
 def test_k_tail_does_not_mix_rows():
     # A K tail reads past the end of each row of A; those elements belong to the next row. An Inf
     # placed at the start of row 1 must only reach row 1 of C.

@@ -171,27 +171,44 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
 __device__ __forceinline__ int swz_b16(int k) { return (4 * (k & 3)) | (2 * ((k >> 3) & 1)); }
 
 // Store a wave's sub-tile of 16 x 16 accumulator blocks: lane l holds row (l mod 16) and columns
-// 4 (l / 16) .. + 3 of block (i, j), packed into 8 bytes (16-bit output) or 16 bytes (fp32); each
-// store writes 32 (64) contiguous bytes of 16 rows.
+// 4 (l / 16) .. + 3 of block (i, j). fp32 output stores those 16 bytes per lane (64 contiguous
+// bytes of each of 16 rows per store). 16-bit output packs each block's four values into 8 bytes
+// and pairs blocks j and j + 1 with v_permlane16_swap (rows 1 and 3 of 16 lanes of the first operand
+// trade places with rows 0 and 2 of the second): afterwards lane group g = l / 16 holds columns
+// 8 (g / 2) .. + 7 of block j + (g mod 2), so each store writes 16 bytes per lane and 64 contiguous
+// bytes of each of 16 rows, half as many stores of twice the width as 8-byte pieces.
 template <int BM, int BN, int WM, int WN, int TM, int TN, bool kBf16, bool kF32Out>
 __device__ __forceinline__ void store_tile16(f32x4_t (&acc)[TM][TN], void* __restrict__ Cv, int M, int N,
                                              int tile_m, int tile_n, int wm, int wn, int lane) {
+  static_assert(kF32Out || TN % 2 == 0, "16-bit stores pair adjacent blocks");
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const size_t row = static_cast<size_t>(tile_m) * BM + wm * WM + i * 16 + (lane & 15);
+    if constexpr (kF32Out) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const size_t col = static_cast<size_t>(tile_n) * BN + wn * WN + j * 16 + 4 * (lane >> 4);
-      if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
-      if constexpr (kF32Out) {
+      for (int j = 0; j < TN; ++j) {
+        const size_t col = static_cast<size_t>(tile_n) * BN + wn * WN + j * 16 + 4 * (lane >> 4);
+        if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
         float* C = static_cast<float*>(Cv);
         *reinterpret_cast<float4*>(C + row * N + col) =
             make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-      } else {
-        uint16_t* C = static_cast<uint16_t*>(Cv);
-        const uint32_t lo = to_out16(acc[i][j][0], kBf16) | (static_cast<uint32_t>(to_out16(acc[i][j][1], kBf16)) << 16);
-        const uint32_t hi = to_out16(acc[i][j][2], kBf16) | (static_cast<uint32_t>(to_out16(acc[i][j][3], kBf16)) << 16);
-        *reinterpret_cast<uint2*>(C + row * N + col) = make_uint2(lo, hi);
+      }
+    } else {
+      uint16_t* C = static_cast<uint16_t*>(Cv);
+      const int g = lane >> 4;
+#pragma unroll
+      for (int j = 0; j < TN; j += 2) {
+        uint32_t pk[2][2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          pk[b][0] = to_out16(acc[i][j + b][0], kBf16) | (static_cast<uint32_t>(to_out16(acc[i][j + b][1], kBf16)) << 16);
+          pk[b][1] = to_out16(acc[i][j + b][2], kBf16) | (static_cast<uint32_t>(to_out16(acc[i][j + b][3], kBf16)) << 16);
+        }
+        const auto lo = __builtin_amdgcn_permlane16_swap(pk[0][0], pk[1][0], false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(pk[0][1], pk[1][1], false, false);
+        const size_t col = static_cast<size_t>(tile_n) * BN + wn * WN + (j + (g & 1)) * 16 + 8 * (g >> 1);
+        if (row >= static_cast<size_t>(M) || col >= static_cast<size_t>(N)) continue;  // N % 8 == 0
+        *reinterpret_cast<uint4*>(C + row * N + col) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
       }
     }
   }
