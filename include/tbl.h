@@ -134,8 +134,9 @@ enum {
  *                 schedule); < 0 is TBL_ERR_INVALID_ARG.
  *   stream        hipStream_t or NULL.
  * Every output element is computed by exactly one workgroup with fp32 accumulation over k in
- * ascending 16-deep MFMA steps, so the result does not depend on the order, the remap flag,
- * persistence or num_programs.
+ * ascending MFMA steps (16-deep 32x32x16, or 32-deep 16x16x32 in the 256x256 kernel, which on
+ * gfx950 leave the same bits), so the result does not depend on the order, the remap flag,
+ * persistence, num_programs or the tile shape.
  */
 int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
              int swizzle_mode, int group_size, int persistent, int num_programs, void* stream);

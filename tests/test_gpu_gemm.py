@@ -84,6 +84,25 @@ def test_output_rounding_is_nearest_even(dtype):
         assert np.array_equal(bits16(c), want), tile
 
 
+@pytest.mark.parametrize("dtype,dist", [("f16", "uniform"), ("bf16", "normal")])
+@pytest.mark.parametrize("out_dtype", [None, torch.float32])
+def test_tile_shapes_bit_identical(dtype, dist, out_dtype):
+    # the 64 and 128 kernels take 16-deep 32x32x16 MFMA steps, the 256 kernel 32-deep 16x16x32
+    # ones; both accumulate each element over k in ascending order in fp32, and the results agree
+    # bit for bit (ragged in every dimension, K tail included)
+    M, N, K = 700, 584, 1000
+    a, b = synth.gemm_operands(M, N, K, dtype, dist, seed=77)
+    ad, bd = dev16(a, dtype), dev16(b, dtype)
+    outs = {}
+    for tile in (64, 128, 256):
+        outs[tile] = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, 64)
+    check_tol(host64(outs[256])[rows], og.gemm_rows(a, b, dtype, rows), K, f32_out=out_dtype is not None,
+              what=f"{dtype} tile 256")
+    assert torch.equal(outs[64], outs[256]) and torch.equal(outs[128], outs[256])
+
+
 @pytest.mark.parametrize("tile", [64, 128, 256])
 def test_schedule_variants_bit_identical(tile):
     M = N = 1024
