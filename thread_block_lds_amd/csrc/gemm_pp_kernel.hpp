@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // C(s): the step's 16 MFMAs
+  // C(s): the step's MFMAs (16 of 32 x 32 x 16, or 32 of 16 x 16 x 32)
   auto compute_half = [&]() {
     if constexpr (kM16) {   // 32 MFMAs of 16 x 16 x 32
 #pragma unroll
