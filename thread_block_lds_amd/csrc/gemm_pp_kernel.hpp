@@ -415,10 +415,16 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   // C(s): the step's MFMAs (16 of 32 x 32 x 16, or 32 of 16 x 16 x 32)
   auto compute_half = [&]() {
     if constexpr (kM16) {   // 32 MFMAs of 16 x 16 x 32
+      // The B fragments run forward for even i and backward for odd i, so at every change of A the
+      // B operand stays: fewer operand bits switch per MFMA, which lets the board hold a higher
+      // clock (the MFMA-only loop runs 2-4 % faster in this order).
 #pragma unroll
       for (int i = 0; i < TM16; ++i)
 #pragma unroll
-        for (int j = 0; j < TN16; ++j) acc16[i][j] = mfma16x16x32<kBf16>(bf16f[j], af16[i], acc16[i][j]);
+        for (int jj = 0; jj < TN16; ++jj) {
+          const int j = (i & 1) ? TN16 - 1 - jj : jj;
+          acc16[i][j] = mfma16x16x32<kBf16>(bf16f[j], af16[i], acc16[i][j]);
+        }
     } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h)

@@ -3,8 +3,8 @@
 //
 // Every wave loads four 16-byte A fragments and four B fragments from the caller's operands once,
 // then issues `iters` rounds of 32 independent v_mfma_f32_16x16x32_{f16,bf16} accumulations in the
-// order the GEMM's wave issues them: the B fragment (first operand) changes with every MFMA, the A
-// fragment (second operand) every fourth. Nothing else runs in the loop, so the rate this kernel
+// order the GEMM's wave issues them: the A fragment (second operand) changes every fourth MFMA, and
+// the B fragments (first operand) run forward and backward in turn, so B stays where A changes. Nothing else runs in the loop, so the rate this kernel
 // reaches is what the matrix pipes sustain at the core clock the chip holds for this data: the
 // clock, and with it the rate, falls as the operands' switching activity (and power) rises. The
 // register budget is the GEMM's (512 threads per workgroup allowed, so at most 256 registers per
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(const uint4* __restrict_
   const uint64_t rt0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int q = 0; q < 32; ++q) acc[q] = mfma<kBf16>(b[q & 3], a[(q >> 2) & 3], acc[q]);
+    for (int q = 0; q < 32; ++q) acc[q] = mfma<kBf16>(b[((q >> 2) & 1) ? 3 - (q & 3) : (q & 3)], a[(q >> 2) & 3], acc[q]);
   }
   const uint64_t clk1 = __builtin_readcyclecounter();
   const uint64_t rt1 = __builtin_amdgcn_s_memrealtime();
