@@ -167,7 +167,8 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   auto mailbox_take = [&](int k) -> int {   // other waves: read the slot, check its claim number
     for (int tries = 0; tries < 1024; ++tries) {
       const uint64_t v = dyn_load_wg(mailbox + (k & 1));
-      if (__builtin_amdgcn_readfirstlane(static_cast<unsigned>(v >> 32)) == static_cast<unsigned>(k)) {
+      if (static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(v >> 32))) ==
+          static_cast<unsigned>(k)) {
         const int pos = static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(v)));
         if (pos < static_cast<int>(T)) return pos;   // -1 (no work) or a position of this grid
         break;
