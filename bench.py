@@ -32,7 +32,8 @@ Printed: one JSON line with
                without the XCD remap, and group-major g4 over 2x2 clusters of tiles with the remap;
                then both orders under the dynamic work-queue schedule, with one claim queue and
                with one per XCD): TFLOP/s, % of peak and predicted L2 hit rate of each static order
-               (the 70 % target), and the MFMA ceiling on its bf16 operands; then the two remapped
+               (the 70 % target) with its measured L2 hit rate (rocprofv3 --pmc pass, cold
+               launches), and the MFMA ceiling on its bf16 operands; then the two remapped
                orders on fp16 uniform[-1,1] operands of the same shape, with their own ceiling;
   cpu_baseline the fp64 CPU oracle on a sample of output rows of the same product.
 
@@ -40,6 +41,8 @@ Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-counters] [--n
        python bench.py --counter-pass      (one unmeasured GEMM, one cold GEMM per variant, then a
                                             calibration copy)
        python bench.py --transpose-pass    (each transpose layout at 1024x2048 and 16384x16384)
+       python bench.py --target-counter-pass (the 8192^3 bf16 target: one unmeasured GEMM, one cold
+                                            persistent GEMM per static order)
        python bench.py --lds-sweep         (every LDS operand-layout variant at 4096^3: measured
                                             bank-conflict cycles against the oracle's prediction)
        python bench.py --page-sweep        (the swizzle page's own 8192^3 128x128x32 sweep: one
@@ -147,6 +150,26 @@ def counter_pass():
     print("counter pass done", flush=True)
 
 
+def target_counter_pass():
+    """Run under rocprofv3 --pmc by the parent: the 8192^3 bf16 target, one unmeasured GEMM, then
+    per static order a cache-evicting read and one persistent GEMM."""
+    import torch
+    import thread_block_lds_amd as tbl
+    from thread_block_lds_amd import synth
+    a, b = synth.gemm_operands(C3, C3, C3, "bf16", "normal", seed=0)
+    ad, bd = _dev16(a, torch, torch.bfloat16), _dev16(b, torch, torch.bfloat16)
+    del a, b
+    c = torch.empty((C3, C3), dtype=torch.bfloat16, device="cuda")
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    tbl.gemm(ad, bd, c, persistent=True)
+    torch.cuda.synchronize()
+    for _, mode, g in C3_MODES:
+        _evict(flush)
+        tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=True)
+        torch.cuda.synchronize()
+    print("target counter pass done", flush=True)
+
+
 def _evict(buf):
     """Read a buffer larger than every cache level: clean lines only, so the next kernel pays no
     write-back of the eviction's data."""
@@ -223,7 +246,20 @@ def counters():
             # no MFMA beyond the product's own
             mops = r.get("SQ_INSTS_VALU_MFMA_MOPS_F16")
             per[name]["mfma_flops_over_algorithmic"] = mops * 512.0 / FLOPS if mops else None
-        return {"per": per, "factors": factors}, None
+        # the 8192^3 target: measured L2 hit rate per static order (cold launches); a failure here
+        # leaves only these figures out
+        target = None
+        try:
+            rows = _run_pmc(["TCC_HIT_sum", "TCC_MISS_sum"], "target_l2", tmp, "--target-counter-pass")
+            gemm = [r for r in rows if _is_gemm(r["kernel"])][1:]   # the first is unmeasured
+            if len(gemm) == len(C3_MODES):
+                target = {}
+                for (name, _, _), r in zip(C3_MODES, gemm):
+                    hit, miss = r["TCC_HIT_sum"], r["TCC_MISS_sum"]
+                    target[name] = 100.0 * hit / (hit + miss) if hit + miss > 0 else None
+        except Exception:
+            target = None
+        return {"per": per, "factors": factors, "target_l2_hit_pct": target}, None
     except Exception as e:  # counters are reported as null with the reason
         return None, f"{type(e).__name__}: {e}"
     finally:
@@ -374,7 +410,7 @@ def mfma_ceiling(tbl, torch, stream, ad, bd, gemm_tflops=None, reps=5):
     return out
 
 
-def target_check(tbl, torch, stream, reps=10):
+def target_check(tbl, torch, stream, measured_hit=None, reps=10):
     """The 8192^3 bf16 persistent workload: median kernel time of back-to-back launches per order."""
     from thread_block_lds_amd import synth
     a, b = synth.gemm_operands(C3, C3, C3, "bf16", "normal", seed=0)
@@ -398,6 +434,8 @@ def target_check(tbl, torch, stream, reps=10):
                                       resident=max(1, progs // info["num_xcds"]))
         res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2),
                      "pred_l2_hit_pct": round(100.0 * hits / acc, 2)}
+        if measured_hit and measured_hit.get(name) is not None:
+            res[name]["l2_hit_pct"] = round(measured_hit[name], 2)   # cold launch, rocprofv3 --pmc
     ws = tbl.dynamic_workspace(progs)
     for name, mode, g in C3_DYNAMIC:
         def launch():
@@ -633,6 +671,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counter-pass", action="store_true")
     ap.add_argument("--transpose-pass", action="store_true")
+    ap.add_argument("--target-counter-pass", action="store_true")
     ap.add_argument("--page-sweep", action="store_true")
     ap.add_argument("--page-sweep-pass", action="store_true")
     ap.add_argument("--lds-sweep", action="store_true")
@@ -652,6 +691,9 @@ def main():
         return
     if args.transpose_pass:
         transpose_pass()
+        return
+    if args.target_counter_pass:
+        target_counter_pass()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -729,7 +771,7 @@ def main():
     pred, pred_cfg = predictions(tbl)
     ceiling = mfma_ceiling(tbl, torch, stream, ad, bd)
     transpose = time_transpose(tbl, torch, stream)
-    target = target_check(tbl, torch, stream)
+    target = target_check(tbl, torch, stream, ctr.get("target_l2_hit_pct") if ctr else None)
 
     ms_step = wall * 1e3 / args.steps
     per_mode = {}
