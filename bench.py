@@ -99,6 +99,7 @@ PMC_PASSES = (("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("fetch", ["FETCH_SIZE"])
               ("write", ["WRITE_SIZE"]),
               ("sq", ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
                       "SQ_INSTS_VALU_MFMA_MOPS_F16", "GRBM_GUI_ACTIVE"]))
+TARGET_PMC = ["TCC_HIT_sum", "TCC_MISS_sum"]   # the 8192^3 target's counter pass
 
 
 def _xcd_traffic_floor(xcds=8):
@@ -250,7 +251,7 @@ def counters():
         # leaves only these figures out
         target = None
         try:
-            rows = _run_pmc(["TCC_HIT_sum", "TCC_MISS_sum"], "target_l2", tmp, "--target-counter-pass")
+            rows = _run_pmc(TARGET_PMC, "target_l2", tmp, "--target-counter-pass")
             gemm = [r for r in rows if _is_gemm(r["kernel"])][1:]   # the first is unmeasured
             if len(gemm) == len(C3_MODES):
                 target = {}

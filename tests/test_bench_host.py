@@ -1,0 +1,62 @@
+"""Host logic of bench.py (no GPU): the roofline's traffic floor, the rank correlation, the sweep's
+variants, the rocprofv3 counter passes' per-block limits and the one-GPU guard."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_xcd_traffic_floor_closed_form():
+    # 4096^3 with 256 x 256 tiles: 256 tiles, 32 per XCD; the squarest block in bytes is 4 x 8 tiles,
+    # so each XCD reads 4 row panels of A and 8 column panels of B (256 x 4096 x 2 bytes each) once
+    panel = 256 * 4096 * 2
+    c_bytes = 4096 * 4096 * 2
+    assert bench._xcd_traffic_floor() == 8 * (4 + 8) * panel + c_bytes == 234881024
+    # one cache holding everything: each operand panel read once
+    assert bench._xcd_traffic_floor(xcds=1) == (16 + 16) * panel + c_bytes
+
+
+def test_rank_corr_ties_in_index_order():
+    assert bench.rank_corr([1, 2, 3, 4], [10, 20, 30, 40]) == pytest.approx(1.0)
+    assert bench.rank_corr([1, 2, 3, 4], [4, 3, 2, 1]) == pytest.approx(-1.0)
+    # ties take ranks in index order: x ranks 0, 1, 2 against y ranks 2, 1, 0
+    assert bench.rank_corr([1, 1, 2], [3, 2, 1]) == pytest.approx(-1.0)
+
+
+def test_sweep_variants():
+    names = [n for n, _, _ in bench.MODES]
+    assert len(names) == 12 and len(set(names)) == 12
+    for name, mode, _ in bench.MODES:
+        assert bool(mode & bench.REMAP) == name.endswith("+remap")
+    assert [n for n, _, _ in bench.C3_MODES][:4] == ["group_major_g8", "serpentine_s8",
+                                                     "group_major_g8+remap", "serpentine_s8+remap"]
+
+
+# per-pass hardware limits of rocprofv3 on this GPU (a pass asking for more cannot be collected):
+# 8 SQ_, 4 TCC_ (FETCH_SIZE takes 3, WRITE_SIZE 2), 4 TCP_, 2 TA_, 2 TD_, 2 GRBM_ counters
+_COST = {"FETCH_SIZE": ("TCC_", 3), "WRITE_SIZE": ("TCC_", 2)}
+_LIMIT = {"SQ_": 8, "TCC_": 4, "TCP_": 4, "TA_": 2, "TD_": 2, "GRBM_": 2}
+
+
+@pytest.mark.parametrize("tag,ctrs", list(bench.PMC_PASSES) + [("target_l2", bench.TARGET_PMC)])
+def test_counter_passes_fit_one_run(tag, ctrs):
+    used = {}
+    for c in ctrs:
+        block, n = _COST.get(c, (next((b for b in _LIMIT if c.startswith(b)), None), 1))
+        assert block is not None, (tag, c)
+        used[block] = used.get(block, 0) + n
+    for block, n in used.items():
+        assert n <= _LIMIT[block], (tag, block, n)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
