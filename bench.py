@@ -698,7 +698,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(output tiles shard across GPUs with no exchange; see the design notes). Run with --gpus 1.",
+              "(output tiles would shard across GPUs with no exchange). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
