@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     if constexpr (kM16) {   // 32 MFMAs of 16 x 16 x 32
       // The B fragments run forward for even i and backward for odd i, so at every change of A the
       // B operand stays: fewer operand bits switch per MFMA, which lets the board hold a higher
-      // clock (the MFMA-only loop measured 2-4 % faster in this order).
+      // clock (the MFMA-only loop runs 2-3 % faster in this order).
 #pragma unroll
       for (int i = 0; i < TM16; ++i)
 #pragma unroll
