@@ -15,8 +15,9 @@
 //     + 63, a 128 x 64 sub-tile (128 accumulator registers): 4 x 2 blocks of 32 x 32, or with kM16
 //     8 x 4 blocks of 16 x 16.
 //   * Each group alternates a memory half-period M(s) -- read all operand fragments of k step s
-//     from LDS into registers, issue this wave's four direct loads of step s + 4, wait until its
-//     loads of step s + 1 have landed -- and a compute half-period C(s) -- the step's 16 MFMAs of
+//     from LDS into registers and issue this wave's four direct loads of step s + 4 (in the kM16
+//     form interleaved with the reads), wait until its loads of step s + 1 have landed -- and a
+//     compute half-period C(s) -- the step's 16 MFMAs of
 //     32 x 32 x 16 (or 32 of 16 x 16 x 32) back to back, then the epilogue if s ends a tile. Group 1 starts one half-period late, so
 //     while one wave of a SIMD computes, the other issues its memory operations; a wave stalled on
 //     a load or an LDS read no longer idles the matrix pipe.
@@ -276,22 +277,29 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     b_lead = static_cast<unsigned>(n) * (BN * 2);
   };
   enter_tile();
-  // issue this wave's loads of the next step in the stream (zero-length ones past its end, which
-  // keep the number of loads per step, and so every wait count, the same)
-  auto load_step = [&]() {
+  // this wave's loads of the next step in the stream (zero-length ones past its end, which keep the
+  // number of loads per step, and so every wait count, the same): prepare_step sets up the step's
+  // buffer descriptors, issue_load(q) issues load q (A blocks first, then B blocks),
+  // advance_load_cursor moves to the step after it
+  i32x4_t ld_da, ld_db;
+  unsigned ld_lds = 0;
+  bool ld_tail = false;
+  auto prepare_step = [&]() {
     const bool real = kDyn ? ld_t >= 0 : ld_issued < total;
     const int k_left = K - ld_kt * kBK;
     const unsigned b_rows = static_cast<unsigned>(k_left < kBK ? k_left : kBK);
-    const bool tail = k_left < kBK;
-    const i32x4_t da = make_desc(reinterpret_cast<const void*>(ld_a), real ? a_range : 0u);
-    const i32x4_t db = make_desc(reinterpret_cast<const void*>(ld_b), real ? b_rows * b_row - b_lead : 0u);
-    const unsigned base = lds_address(lds + ld_stage * kStage);
-#pragma unroll
-    for (int q = 0; q < kAInst; ++q)
-      load_to_lds(da, base + (wave * kAInst + q) * 1024, tail ? a_voff_tail[q] : a_voff[q]);
-#pragma unroll
-    for (int q = 0; q < kBInst; ++q)
-      load_to_lds(db, base + kAStage + (wave * kBInst + q) * 1024, b_voff[q]);
+    ld_tail = k_left < kBK;
+    ld_da = make_desc(reinterpret_cast<const void*>(ld_a), real ? a_range : 0u);
+    ld_db = make_desc(reinterpret_cast<const void*>(ld_b), real ? b_rows * b_row - b_lead : 0u);
+    ld_lds = lds_address(lds + ld_stage * kStage);
+  };
+  auto issue_load = [&](int q) {
+    if (q < kAInst)
+      load_to_lds(ld_da, ld_lds + (wave * kAInst + q) * 1024, ld_tail ? a_voff_tail[q] : a_voff[q]);
+    else
+      load_to_lds(ld_db, ld_lds + kAStage + (wave * kBInst + q - kAInst) * 1024, b_voff[q - kAInst]);
+  };
+  auto advance_load_cursor = [&]() {
     ++ld_issued;
     ld_stage = ld_stage == kStages - 1 ? 0 : ld_stage + 1;
     ld_a += a_step;
@@ -308,26 +316,29 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
       }
     }
   };
+  auto load_step = [&]() {
+    prepare_step();
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) issue_load(q);
+    advance_load_cursor();
+  };
 
   // ---- operand fragments of one step: [k half][block] ----
   uint4 af[2][TM], bf[2][TN];
   uint4 af16[TM16], bf16f[TN16];
+  // 16 x 16 x 32 form: A block i (one 16-byte read), B block j (two transposing 8-byte reads)
+  auto read_a16 = [&](int stage, int i) {
+    af16[i] = *reinterpret_cast<const uint4*>(lds + stage * kStage + a_rd16 + i * 16 * kARow);
+  };
+  auto read_b16 = [&](int stage, int j) {
+    const char* p = lds + stage * kStage + b_rd16[j];
+    const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+    const uint2 hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4_t*)(p + 4 * kBRow)));
+    bf16f[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
   auto read_step = [&](int stage) {
     const char* base = lds + stage * kStage;
-    if constexpr (kM16) {
-#pragma unroll
-      for (int i = 0; i < TM16; ++i)
-        af16[i] = *reinterpret_cast<const uint4*>(base + a_rd16 + i * 16 * kARow);
-#pragma unroll
-      for (int j = 0; j < TN16; ++j) {
-        const char* p = base + b_rd16[j];
-        const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
-        const uint2 hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                       (lds_s16x4_t*)(p + 4 * kBRow)));
-        bf16f[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-      return;
-    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -404,10 +415,38 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
 
   int c_stage = 0;
   // M(s): this step's fragments into registers, the loads of step s + 4, then the wait for this
-  // wave's loads of step s + 1; the barrier closes the half-period
+  // wave's loads of step s + 1; the barrier closes the half-period.
+  // In the 16 x 16 x 32 form the four loads are interleaved with the operand reads. Issuing a direct
+  // load stalls the wave until the CU's address unit takes it (about 1 KiB per 16 cycles, shared by
+  // the group's four waves: some 260 cycles for the group's 16 loads), while the reads keep the LDS
+  // busy for about 300 cycles; issued one after the other the two made the memory half-period
+  // longer than the MFMA one (cycle stamps on the device), interleaved they overlap (1240 -> 1165
+  // cycles per step).
   auto memory_half = [&]() {
-    read_step(c_stage);
-    load_step();
+    if constexpr (kM16) {
+      static_assert(kLoads == 4 && TM16 == 8 && TN16 == 4, "interleave written for this wave tile");
+      prepare_step();
+      issue_load(0);
+      read_b16(c_stage, 0);
+      read_a16(c_stage, 0);
+      issue_load(1);
+      read_b16(c_stage, 1);
+      read_a16(c_stage, 1);
+      read_a16(c_stage, 2);
+      issue_load(2);
+      read_b16(c_stage, 2);
+      read_a16(c_stage, 3);
+      read_a16(c_stage, 4);
+      issue_load(3);
+      read_b16(c_stage, 3);
+      read_a16(c_stage, 5);
+      read_a16(c_stage, 6);
+      read_a16(c_stage, 7);
+      advance_load_cursor();
+    } else {
+      read_step(c_stage);
+      load_step();
+    }
     wait_vm<3 * kLoads>();
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
