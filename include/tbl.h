@@ -36,8 +36,12 @@
  *     nothing enqueued, also on a machine without a GPU.
  *   - Return value: TBL_OK (0) on success, a negative TBL_ERR_* on error, a positive TBL_WARN_* on
  *     success with a warning. tbl_status_string() gives text for any code.
- *   - Thread safety: the only global state is a per-device cache of device properties filled on
- *     first use; calls from several host threads are safe. Calls that write the same output race.
+ *   - Thread safety: the only global state is a per-device cache of device properties and of the
+ *     scratch array's address (tbl_gemm_dynamic_noalloc), filled on first use; calls from several
+ *     host threads are safe, except tbl_gemm_dynamic_noalloc calls that overlap on one GPU (they share
+ *     its scratch array). Calls that write the same output race.
+ *   - Every entry point allocates nothing; tbl_gemm_dynamic_noalloc uses a device array of the
+ *     library instead of a workspace argument.
  */
 #ifndef TBL_H_
 #define TBL_H_
@@ -57,6 +61,7 @@ enum {
   TBL_ERR_NOT_BIJECTIVE = -4, /* GEMM with Morton/XOR on a (cluster) grid that is not a square power of two */
   TBL_ERR_HIP = -5,           /* a HIP runtime call failed (no device, launch failure, ...) */
   TBL_ERR_ALIGN = -6,         /* a GEMM or transpose pointer is not 16-byte aligned */
+  TBL_ERR_SCRATCH = -7,       /* tbl_gemm_dynamic_noalloc: more workgroups than its scratch holds */
   TBL_WARN_NOT_BIJECTIVE = 1  /* tbl_tile_map wrote the table, but it is not a bijection */
 };
 
@@ -194,6 +199,25 @@ int tbl_gemm_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N
 /* int32 elements of the workspace tbl_gemm_dynamic needs for num_programs workgroups (>= 1), or -1
  * if num_programs is out of range. */
 int64_t tbl_gemm_dynamic_workspace(int num_programs);
+
+/*
+ * tbl_gemm_dynamic_noalloc -- tbl_gemm_dynamic without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc). The claim counters and mailboxes live in a device array of the library (one per GPU,
+ * 4 * (32 + 32 * TBL_NOALLOC_MAX_PROGRAMS) bytes = 512 KiB, held until the process ends), whose
+ * address is looked up once per device. The call allocates nothing and calls no allocating routine.
+ *   num_programs  as tbl_gemm_dynamic (0 = CUs x occupancy); a count above
+ *                 TBL_NOALLOC_MAX_PROGRAMS returns TBL_ERR_SCRATCH before any HIP call when given,
+ *                 after the occupancy query when resolved.
+ *   Every other argument, the result bits and the errors are those of tbl_gemm_dynamic. Each call
+ *   first zeroes the claim counters with a one-workgroup kernel (no memset), so the array needs no
+ *   initial contents; all calls on one GPU share its array, so calls that overlap in time on one GPU
+ *   (different streams, several host threads) race and must be serialised by the caller.
+ */
+#define TBL_NOALLOC_MAX_PROGRAMS 4096
+int tbl_gemm_dynamic_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                             int dtype, int swizzle_mode, int group_size, int num_programs,
+                             int32_t* trace, void* stream);
 
 /*
  * tbl_gemm_lds_layout -- tbl_gemm on 256x256x32 tiles with chosen LDS swizzles for the operands,

@@ -37,7 +37,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, -5, -6, 1, 12345):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, 1, 12345):
         assert isinstance(tbl.status_string(st), str) and tbl.status_string(st)
 
 
@@ -96,6 +96,30 @@ def test_gemm_dynamic_workspace_size():
 ])
 def test_gemm_dynamic_validation(kw, want):
     assert _dyn(**kw) == want
+
+
+def _dyn_noalloc(A=FAKE, M=2048, N=2048, K=2048, dtype=0, mode=0, group=1, P=0):
+    return tbl.lib().tbl_gemm_dynamic_noalloc(A, FAKE, FAKE, M, N, K, dtype, mode, group, P, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(A=NULL), tbl.ERR_INVALID_ARG), (dict(M=0), tbl.ERR_INVALID_ARG), (dict(dtype=7), tbl.ERR_DTYPE),
+    (dict(mode=tbl.SERPENTINE, group=0), tbl.ERR_INVALID_ARG), (dict(P=-1), tbl.ERR_INVALID_ARG),
+    (dict(K=256), tbl.ERR_SHAPE), (dict(M=2048, N=1536, mode=tbl.XOR), tbl.ERR_NOT_BIJECTIVE),
+    (dict(A=MISALIGNED), tbl.ERR_ALIGN),
+    # the scratch array holds TBL_NOALLOC_MAX_PROGRAMS workgroups; beyond the dynamic schedule's own
+    # limit the workspace-taking entry point's error comes first
+    (dict(P=tbl.NOALLOC_MAX_PROGRAMS + 1), tbl.ERR_SCRATCH), (dict(P=65536), tbl.ERR_SCRATCH),
+    (dict(P=65537), tbl.ERR_INVALID_ARG),
+])
+def test_gemm_dynamic_noalloc_validation(kw, want):
+    assert _dyn_noalloc(**kw) == want
+
+
+def test_noalloc_limit_matches_header():
+    src = open(HEADER).read()
+    assert re.search(r"#define TBL_NOALLOC_MAX_PROGRAMS (\d+)", src).group(1) == str(tbl.NOALLOC_MAX_PROGRAMS)
+    assert "scratch" in tbl.status_string(tbl.ERR_SCRATCH)
 
 
 def test_gemm_tiled_validation():

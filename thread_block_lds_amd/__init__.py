@@ -20,6 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtbl.so")
 
 OK, ERR_INVALID_ARG, ERR_DTYPE, ERR_SHAPE, ERR_NOT_BIJECTIVE, ERR_HIP, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
+ERR_SCRATCH = -7
+NOALLOC_MAX_PROGRAMS = 4096   # TBL_NOALLOC_MAX_PROGRAMS
 WARN_NOT_BIJECTIVE = 1
 F16, BF16, F16_F32OUT, BF16_F32OUT = 0, 1, 2, 3
 ROW, COL, PANEL, MORTON, XOR, SERPENTINE = 0, 1, 2, 3, 4, 5
@@ -55,6 +57,10 @@ _EXPORTS = {
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "tbl_gemm_dynamic_workspace": (ctypes.c_int64, [ctypes.c_int]),
+    "tbl_gemm_dynamic_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_void_p]),
     "tbl_tile_map": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tbl_transpose_i32": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -216,13 +222,8 @@ def dynamic_workspace(num_programs, device="cuda"):
     return torch.zeros(dynamic_workspace_ints(num_programs), dtype=torch.int32, device=device)
 
 
-def gemm_dynamic(a, b, c=None, mode=ROW, group=1, num_programs=0, workspace=None, out_dtype=None,
-                 trace=None, stream=None):
-    """C = A @ B with 256x256x32 tiles and the dynamic (work-queue) schedule, through
-    tbl_gemm_dynamic. ``mode`` may include XCD_REMAP (one claim queue per XCD). ``workspace``: from
-    dynamic_workspace(), sized for the launch's workgroups (default: a fresh one for
-    min(T, 4 x CUs)). ``trace``: int32 CUDA tensor of 8*T entries, indexed by order position.
-    Returns c."""
+def _dynamic_args(a, b, c, out_dtype, trace):
+    """Shared checks of the dynamic-schedule calls: returns (M, N, K, dtype code, c, T)."""
     import torch
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"shape mismatch {tuple(a.shape)} x {tuple(b.shape)}")
@@ -241,12 +242,37 @@ def gemm_dynamic(a, b, c=None, mode=ROW, group=1, num_programs=0, workspace=None
     for t, name in ((a, "A"), (b, "B"), (c, "C")):
         _device_tensor(t, name, device=a.device)
     T = (-(-M // 256)) * (-(-N // 256))
+    if trace is not None:
+        _device_tensor(trace, "trace", torch.int32, 8 * T, a.device)
+    return M, N, K, dt, c, T
+
+
+def gemm_dynamic_noalloc(a, b, c=None, mode=ROW, group=1, num_programs=0, out_dtype=None, trace=None,
+                         stream=None):
+    """gemm_dynamic without a workspace, through tbl_gemm_dynamic_noalloc: the claim counters live in
+    a device array of the library (one per GPU, for at most NOALLOC_MAX_PROGRAMS workgroups), so the
+    library call allocates nothing (``c`` is allocated here when not given). Calls that overlap in
+    time on one GPU share that array and must be serialised. Returns c."""
+    M, N, K, dt, c, _ = _dynamic_args(a, b, c, out_dtype, trace)
+    st = lib().tbl_gemm_dynamic_noalloc(_ptr(a), _ptr(b), _ptr(c), M, N, K, dt, int(mode), int(group),
+                                        int(num_programs), _ptr(trace), _stream(stream))
+    _check(st, "tbl_gemm_dynamic_noalloc")
+    return c
+
+
+def gemm_dynamic(a, b, c=None, mode=ROW, group=1, num_programs=0, workspace=None, out_dtype=None,
+                 trace=None, stream=None):
+    """C = A @ B with 256x256x32 tiles and the dynamic (work-queue) schedule, through
+    tbl_gemm_dynamic. ``mode`` may include XCD_REMAP (one claim queue per XCD). ``workspace``: from
+    dynamic_workspace(), sized for the launch's workgroups (default: a fresh one for
+    min(T, 4 x CUs)). ``trace``: int32 CUDA tensor of 8*T entries, indexed by order position.
+    Returns c."""
+    import torch
+    M, N, K, dt, c, T = _dynamic_args(a, b, c, out_dtype, trace)
     if workspace is None:
         P = int(num_programs) or max(1, min(T, 4 * device_info()["num_cus"]))
         workspace = dynamic_workspace(P, a.device)
     _device_tensor(workspace, "workspace", torch.int32, device=a.device)
-    if trace is not None:
-        _device_tensor(trace, "trace", torch.int32, 8 * T, a.device)
     st = lib().tbl_gemm_dynamic(_ptr(a), _ptr(b), _ptr(c), M, N, K, dt, int(mode), int(group),
                                 int(num_programs), _ptr(workspace), workspace.numel(), _ptr(trace),
                                 _stream(stream))

@@ -154,6 +154,7 @@ const char* tbl_status_string(int status) {
     case TBL_ERR_NOT_BIJECTIVE: return "order is not a bijection on this tile grid (Morton/XOR need a square power-of-two grid)";
     case TBL_ERR_HIP: return "HIP runtime error";
     case TBL_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case TBL_ERR_SCRATCH: return "more workgroups than the allocation-free entry point's scratch holds";
     case TBL_WARN_NOT_BIJECTIVE: return "warning: table written, but the order is not a bijection on this grid";
     default: return "unknown status";
   }
@@ -229,9 +230,14 @@ int64_t tbl_gemm_dynamic_workspace(int num_programs) {
   return 32 + 32 * static_cast<int64_t>(num_programs);
 }
 
-int tbl_gemm_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
-                     int swizzle_mode, int group_size, int num_programs, int32_t* workspace,
-                     int64_t workspace_ints, int32_t* trace, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks the arguments of a dynamic-schedule GEMM and resolves its workgroup count; the workspace
+// is checked by the caller. Returns TBL_OK with *programs set, or the error.
+int prepare_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                    int swizzle_mode, int group_size, int num_programs, int* programs) {
   int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, 1, num_programs, 256, 256, 32);
   if (rc != TBL_OK) return rc;
   // wave 0 posts the next tile at k step 0 and the others read it at step 4; the load cursor
@@ -239,13 +245,16 @@ int tbl_gemm_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N
   if ((K + 31) / 32 < kMinDynamicKSteps) return TBL_ERR_SHAPE;
   const int gm = static_cast<int>((M + 255) / 256), gn = static_cast<int>((N + 255) / 256);
   if (static_cast<int64_t>(gm) * gn > (int64_t{1} << 30)) return TBL_ERR_SHAPE;
-  int programs = 0;
-  rc = resolve_programs(dtype, 256, 256, 32, static_cast<int64_t>(gm) * gn, 1, num_programs, &programs);
+  rc = resolve_programs(dtype, 256, 256, 32, static_cast<int64_t>(gm) * gn, 1, num_programs, programs);
   if (rc != TBL_OK) return rc;
-  if (programs > kMaxDynamicPrograms) return TBL_ERR_INVALID_ARG;
-  if (workspace == nullptr || !aligned16(workspace)) return workspace == nullptr ? TBL_ERR_INVALID_ARG
-                                                                                 : TBL_ERR_ALIGN;
-  if (workspace_ints < tbl_gemm_dynamic_workspace(programs)) return TBL_ERR_INVALID_ARG;
+  if (*programs > kMaxDynamicPrograms) return TBL_ERR_INVALID_ARG;
+  return TBL_OK;
+}
+
+int launch_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                   int swizzle_mode, int group_size, int programs, int32_t* workspace, int32_t* trace,
+                   void* stream) {
+  const int gm = static_cast<int>((M + 255) / 256), gn = static_cast<int>((N + 255) / 256);
   tbl::GemmLaunch a;
   a.A = A;
   a.B = B;
@@ -261,6 +270,69 @@ int tbl_gemm_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N
   a.xcd_aware = (swizzle_mode & TBL_XCD_REMAP) ? 1 : 0;
   if (tbl::launch_gemm_dynamic(dtype, a, static_cast<hipStream_t>(stream)) != hipSuccess) return TBL_ERR_HIP;
   return TBL_OK;
+}
+
+}  // namespace
+
+// The allocation-free variant's workspace: a device array of the library, one copy per GPU, for at
+// most TBL_NOALLOC_MAX_PROGRAMS workgroups (the workspace layout of tbl_gemm_dynamic). In host code
+// ``scratch`` names a host-side stand-in, so its device address is looked up once per device
+// (hipGetSymbolAddress with that device current) and only that address is passed on.
+constexpr int kNoAllocScratchInts = 32 + 32 * TBL_NOALLOC_MAX_PROGRAMS;
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchInts];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of ``scratch`` (nullptr with TBL_ERR_HIP in *rc if the lookup fails).
+int32_t* device_scratch(int* rc) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = TBL_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      *rc = TBL_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *rc = TBL_OK;
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int tbl_gemm_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+                     int swizzle_mode, int group_size, int num_programs, int32_t* workspace,
+                     int64_t workspace_ints, int32_t* trace, void* stream) {
+  int programs = 0;
+  int rc = prepare_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, num_programs, &programs);
+  if (rc != TBL_OK) return rc;
+  if (workspace == nullptr || !aligned16(workspace)) return workspace == nullptr ? TBL_ERR_INVALID_ARG
+                                                                                 : TBL_ERR_ALIGN;
+  if (workspace_ints < tbl_gemm_dynamic_workspace(programs)) return TBL_ERR_INVALID_ARG;
+  return launch_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, programs, workspace, trace,
+                        stream);
+}
+
+int tbl_gemm_dynamic_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                             int dtype, int swizzle_mode, int group_size, int num_programs,
+                             int32_t* trace, void* stream) {
+  int programs = 0;
+  int rc = prepare_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, num_programs, &programs);
+  if (rc != TBL_OK) return rc;
+  if (programs > TBL_NOALLOC_MAX_PROGRAMS) return TBL_ERR_SCRATCH;
+  int32_t* ws = device_scratch(&rc);
+  if (ws == nullptr) return rc;
+  return launch_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, programs, ws, trace, stream);
 }
 
 int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
