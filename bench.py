@@ -84,7 +84,7 @@ TR_SIZE = 16384
 TR_LAYOUTS = [("naive", 0), ("padded", 1), ("xor", 2)]
 C3 = 8192                     # the persistent bf16 workload of the 70 %-of-peak target
 CLUSTER_2X2 = (1 << 16) | (1 << 20)   # two-level order: 2 x 2 clusters of tiles
-C3_MODES = [("group_major_g8", 2, 8), ("serpentine_s8", 5, 8),
+C3_MODES = [("row", 0, 1), ("row+remap", REMAP, 1), ("group_major_g8", 2, 8), ("serpentine_s8", 5, 8),
             ("group_major_g8+remap", 2 | REMAP, 8), ("serpentine_s8+remap", 5 | REMAP, 8),
             ("group_major_g4+remap+cluster2x2", 2 | REMAP | CLUSTER_2X2, 4)]
 # the dynamic (work-queue) schedule on the same orders: one claim queue, or one per XCD (REMAP)
@@ -295,8 +295,9 @@ def predictions(tbl):
     for name, mode, g in MODES:
         hits, acc, _ = tbl.predict_l2(mode, gm, gn, gk, g, block, block, l2, num_caches=xcds,
                                       num_programs=0, resident=resident)
-        out[name] = {"hit_pct": 100.0 * hits / acc,
-                     "fetch_mb": ((acc - hits) * block + 2 * M * N) / 1e6}
+        # operand reads that miss every L2, the model's counterpart of FETCH_SIZE (reads only; the
+        # C writes are WRITE_SIZE)
+        out[name] = {"hit_pct": 100.0 * hits / acc, "fetch_mb": (acc - hits) * block / 1e6}
     return out, {"caches": xcds, "capacity_bytes": l2, "resident_per_cache": resident,
                  "block_bytes": block, "grid": [gm, gn, gk]}
 
@@ -308,9 +309,10 @@ def cpu_baseline(a, b, budget_s=10.0):
     from oracle import gemm as og
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count()
+        blas_threads = None
+    host = _host_cpu()
     rows, total_rows, total_t = 64, 0, 0.0
     start = 0
     passes = 0
@@ -328,9 +330,30 @@ def cpu_baseline(a, b, budget_s=10.0):
     flops = 2.0 * total_rows * N * K
     sample = (f"{total_rows // M} whole 4096^3 products (+{total_rows % M} rows)" if passes
               else f"output rows 0..{total_rows - 1} of the 4096^3 product")
-    return {"value": flops / total_t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": flops / total_t / 1e12, "unit": "TFLOP/s",
+            # the threads the oracle's fp64 matmul ran on (its BLAS pool), beside the host's cores
+            "cores": blas_threads or host["usable_cpus"], "blas_threads": blas_threads, **host,
+            "kind": "oracle",
             "sample": f"fp64 oracle (numpy matmul on exactly decoded fp16 A and B): {sample}, "
                       f"{total_t:.1f} s wall"}
+
+
+def _host_cpu():
+    """The host's logical CPU count, the CPUs this process may run on, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"host_logical_cpus": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
 
 
 def _region_ms(torch, stream, launch, reps):
@@ -447,6 +470,13 @@ def target_check(tbl, torch, stream, measured_hit=None, reps=10):
         tf = flops / (ms * 1e-3) / 1e12
         res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2),
                      "schedule": "dynamic"}
+    # the north star's "gain over linear ordering" at this workload: measured L2 hit-rate points and
+    # throughput of each static order against row-major (no remap)
+    for name, _, _ in C3_MODES:
+        r = res[name]
+        if "l2_hit_pct" in r and "l2_hit_pct" in res["row"]:
+            r["l2_gain_pp_vs_row"] = round(r["l2_hit_pct"] - res["row"]["l2_hit_pct"], 2)
+        r["speedup_vs_row"] = round(r["tflops"] / res["row"]["tflops"], 4)
     best = max(res, key=lambda n: res[n]["tflops"])
     ceiling = mfma_ceiling(tbl, torch, stream, ad, bd, gemm_tflops=res[best]["tflops"])
     del ad, bd, c
@@ -457,7 +487,7 @@ def target_check(tbl, torch, stream, measured_hit=None, reps=10):
     del a, b
     c = torch.empty((C3, C3), dtype=torch.float16, device="cuda")
     res16 = {}
-    for name, mode, g in C3_MODES[2:4]:
+    for name, mode, g in [m for m in C3_MODES if m[0] in ("group_major_g8+remap", "serpentine_s8+remap")]:
         def launch():
             tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=True, stream=stream.cuda_stream)
         launch()

@@ -34,8 +34,18 @@ def test_sweep_variants():
     assert len(names) == 12 and len(set(names)) == 12
     for name, mode, _ in bench.MODES:
         assert bool(mode & bench.REMAP) == name.endswith("+remap")
-    assert [n for n, _, _ in bench.C3_MODES][:4] == ["group_major_g8", "serpentine_s8",
+    # the 8192^3 target: row-major (the linear baseline of the gain), then the two orders the
+    # workload names, each without and with the remap
+    assert [n for n, _, _ in bench.C3_MODES][:6] == ["row", "row+remap", "group_major_g8", "serpentine_s8",
                                                      "group_major_g8+remap", "serpentine_s8+remap"]
+    for name, mode, _ in bench.C3_MODES:
+        assert bool(mode & bench.REMAP) == ("+remap" in name)
+
+
+def test_host_cpu_fields():
+    h = bench._host_cpu()
+    assert h["host_logical_cpus"] >= 1 and 1 <= h["usable_cpus"] <= h["host_logical_cpus"]
+    assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)
 
 
 # per-pass hardware limits of rocprofv3 on this GPU (a pass asking for more cannot be collected):

@@ -184,6 +184,30 @@ def test_c3_8192_bf16_persistent():
             assert torch.equal(c, base), mode
 
 
+def test_c3_integer_exact_full_k_loop():
+    # the 8192^3 workload's launch (persistent, CUs x occupancy programs, four tiles each, 256
+    # k steps per tile) on integer inputs in [-2, 2] with fp32 output: every partial sum is an
+    # integer of magnitude <= 4 K = 32768 < 2^24, so the result is exact and must equal the oracle
+    # bit for bit; a skipped, doubled or misplaced k step anywhere in the loop would show
+    M = N = K = 8192
+    a = synth.int_valued((M, K), 61, -2, 2, "bf16")
+    b = synth.int_valued((K, N), 62, -2, 2, "bf16")
+    ad, bd = dev16(a, "bf16"), dev16(b, "bf16")
+    rows = _sample_rows(M, 256)
+    ref = og.gemm_rows(a, b, "bf16", rows)
+    static = tbl.gemm(ad, bd, out_dtype=torch.float32, mode=tm.SERPENTINE | tm.XCD_REMAP, group=8,
+                      persistent=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(static)[rows], ref)
+    P = tbl.default_num_programs(M, N, K, tbl.BF16, persistent=True)
+    for mode in (tm.PANEL | tm.XCD_REMAP, tm.PANEL):
+        ws = tbl.dynamic_workspace(P)
+        dyn = tbl.gemm_dynamic(ad, bd, out_dtype=torch.float32, mode=mode, group=8, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[9].item()) == 0
+        assert torch.equal(dyn, static), mode
+
+
 def test_c4_rectangular_partial_groups():
     M, N, K = 10240, 6144, 2048
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
@@ -227,8 +251,9 @@ def test_trace_matches_oracle_schedule(mode, g, persistent, P):
     assert np.all((xcc >= 0) & (xcc < 8))
     for p in range(min(programs, T)):
         assert len(set(xcc[p::programs])) == 1, p           # a workgroup never changes XCD
+    # the XCD remap rests on round-robin dispatch: workgroup p runs on XCD p mod 8
     rr = np.mean(xcc[:min(programs, T)] == np.arange(min(programs, T)) % 8)
-    print(f"workgroups on XCD (program mod 8): {rr:.3f}")
+    assert rr == 1.0, f"only {rr:.3f} of the workgroups ran on XCD (program mod 8)"
     # timing fields: a program's tiles start in iteration order, each after the previous k loop
     ticks = tr[:, 6] & 0xFFFFFFFF
     start = tr[:, 7] & 0xFFFFFFFF
