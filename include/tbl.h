@@ -122,11 +122,14 @@ enum {
 /*
  * tbl_gemm -- C = A * B with a swizzled, optionally persistent tile schedule.
  *   A, B, C       device pointers (row-major M x K, K x N, M x N), 16-byte aligned, C not aliasing.
- *   M, N, K       sizes, > 0, each <= 2^20. N and K must be multiples of 8 (rows are whole
- *                 16-byte chunks); M is free. The tile shape is fixed by a rule
- *                 (tbl_gemm_tile_shape): 64x64x32 when max(M, N) <= 1024, else 256x256x32 (k
- *                 advances through LDS 32 deep). The tile grid is ceil(M/BM) x ceil(N/BN); edge tiles
- *                 are masked (TBL_ERR_SHAPE for sizes outside these rules).
+ *   M, N, K       sizes, > 0, each <= 2^20 (TBL_ERR_SHAPE otherwise); any values. The tile shape is
+ *                 fixed by a rule (tbl_gemm_tile_shape): 64x64x32 when max(M, N) <= 1024, else
+ *                 256x256x32 (k advances through LDS 32 deep). The tile grid is ceil(M/BM) x
+ *                 ceil(N/BN); loads and stores are masked at every edge, as the page's kernel masks
+ *                 them. When N and K are multiples of 8 (rows of A and B are whole 16-byte chunks)
+ *                 the fast kernels run, moving operands with 16-byte direct-to-LDS loads; otherwise
+ *                 an element-wise load path with the same tile grid, schedule and trace (far
+ *                 slower: it exists for generality).
  *   dtype         TBL_F16, TBL_BF16, TBL_F16_F32OUT or TBL_BF16_F32OUT.
  *   swizzle_mode  a TBL_* order, optionally | TBL_XCD_REMAP and | TBL_CLUSTER(cm, cn). Morton and
  *                 XOR need a square power-of-two grid of (cluster) tiles (TBL_ERR_NOT_BIJECTIVE
@@ -139,9 +142,9 @@ enum {
  *                 schedule); < 0 is TBL_ERR_INVALID_ARG.
  *   stream        hipStream_t or NULL.
  * Every output element is computed by exactly one workgroup with fp32 accumulation over k in
- * ascending MFMA steps (16-deep 32x32x16, or 32-deep 16x16x32 in the 256x256 kernel, which on
- * gfx950 leave the same bits), so the result does not depend on the order, the remap flag,
- * persistence, num_programs or the tile shape.
+ * ascending MFMA steps (16-deep 32x32x16, or 32-deep 16x16x32 in the 256x256 kernel and the
+ * element-wise path, which on gfx950 leave the same bits), so the result does not depend on the
+ * order, the remap flag, persistence, num_programs or the tile shape.
  */
 int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
              int swizzle_mode, int group_size, int persistent, int num_programs, void* stream);

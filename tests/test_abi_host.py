@@ -56,8 +56,8 @@ def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=32, A=FAKE, dt
     (dict(mode=6), tbl.ERR_INVALID_ARG), (dict(mode=0x200), tbl.ERR_INVALID_ARG), (dict(mode=-1), tbl.ERR_INVALID_ARG),
     (dict(mode=tbl.PANEL, group=0), tbl.ERR_INVALID_ARG), (dict(mode=tbl.SERPENTINE, group=-2), tbl.ERR_INVALID_ARG),
     (dict(persistent=2), tbl.ERR_INVALID_ARG), (dict(P=-1), tbl.ERR_INVALID_ARG),
-    (dict(N=500), tbl.ERR_SHAPE), (dict(K=100), tbl.ERR_SHAPE), (dict(N=512 + 4), tbl.ERR_SHAPE),
-    (dict(M=(1 << 20) + 256, N=2048), tbl.ERR_SHAPE),
+    (dict(M=(1 << 20) + 256, N=2048), tbl.ERR_SHAPE), (dict(N=(1 << 20) + 1), tbl.ERR_SHAPE),
+    (dict(K=(1 << 20) + 3), tbl.ERR_SHAPE),
     (dict(M=10240, N=6144, K=2048, mode=tbl.MORTON), tbl.ERR_NOT_BIJECTIVE),
     (dict(M=10240, N=6144, K=2048, mode=tbl.XOR | tbl.XCD_REMAP), tbl.ERR_NOT_BIJECTIVE),
     (dict(M=1024, N=512, mode=tbl.XOR), tbl.ERR_NOT_BIJECTIVE),
@@ -126,7 +126,8 @@ def test_gemm_tiled_validation():
     assert _tiled(bm=32, bn=32) == tbl.ERR_SHAPE
     assert _tiled(bm=64, bn=128) == tbl.ERR_SHAPE
     assert _tiled(bk=64) == tbl.ERR_SHAPE
-    assert _tiled(K=512 + 4) == tbl.ERR_SHAPE
+    # N and K need not be multiples of 8 here (the element-wise path); the other checks still apply
+    assert _tiled(K=513, bk=64) == tbl.ERR_SHAPE and _tiled(N=515, bm=32, bn=32) == tbl.ERR_SHAPE
     assert _tiled(mode=tbl.MORTON, M=1024, N=512, bm=128, bn=128) == tbl.ERR_NOT_BIJECTIVE
     assert _tiled(A=MISALIGNED) == tbl.ERR_ALIGN
     assert _tiled(dtype=9) == tbl.ERR_DTYPE
@@ -163,8 +164,9 @@ def test_tile_shape_rule_and_default_programs():
     assert tbl.default_num_programs(10240, 6144, 2048, persistent=False) == 960
     assert tbl.default_num_programs(520, 512, 512, persistent=False) == 72     # 9 x 8 padded grid
     assert tbl.default_num_programs(1, 8, 8, persistent=False) == 1
+    assert tbl.default_num_programs(520, 516, 509, persistent=False) == 81   # any N and K
     with pytest.raises(tbl.TblError):
-        tbl.default_num_programs(520, 516, 512)
+        tbl.default_num_programs(520, (1 << 20) + 1, 512)
 
 
 def _layout(layout=(4, 4, 4, 1, 4), dtype=0, M=512, N=512, K=512, A=FAKE, mode=0):

@@ -11,7 +11,8 @@ Workloads (inputs from thread_block_lds_amd.synth, A seed s, B seed s+1):
   512^3 fp16 uniform[-1,1], 64x64 tiles (8x8 grid), every order, full oracle;
   4096^3 fp16 uniform[-1,1], 256x256 tiles (16x16 grid), row / panel 4,8,16 / Morton / XOR;
   8192^3 bf16 N(0,1)/sqrt(K), persistent group-major 8 and serpentine 8;
-  10240 x 6144 x 2048 fp16, 40x24 grid, panel 8/16 and serpentine 8/16, both launch styles.
+  10240 x 6144 x 2048 fp16, 40x24 grid, panel 8/16 and serpentine 8/16, both launch styles;
+  ragged shapes, N and K included (odd N or K run the element-wise path), every tile shape.
 Large workloads are checked on sampled rows that touch every tile row (every tile column is in
 every row), plus bit-identity of the whole output across orders.
 """
@@ -321,19 +322,103 @@ def test_ragged_integer_16bit_out_is_the_rounded_exact_sum(dtype, tile):
     assert torch.all(big[M:] == -5.0), (dtype, tile)
 
 
+# N or K not a multiple of 8: rows of A or B are not whole 16-byte chunks and the element-wise path
+# runs (every load and store masked at the edges, as the swizzle page's kernel masks them)
+ODD = [(257, 263, 259), (1, 1, 1), (1000, 1001, 1003), (3, 5, 7), (64, 63, 65), (129, 130, 31),
+       (300, 256, 100), (520, 8, 13)]
+
+
+@pytest.mark.parametrize("tile", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", ODD)
+def test_odd_n_k_full_oracle(M, N, K, dtype, tile):
+    a, b = synth.gemm_operands(M, N, K, dtype, "uniform" if dtype == "f16" else "normal", seed=M + 2 * N + 3 * K)
+    ref = og.gemm(a, b, dtype)
+    ad, bd = dev16(a, dtype), dev16(b, dtype)
+    c = tbl.gemm(ad, bd, tile=(tile, tile, 32), mode=tm.PANEL, group=2)
+    c32 = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=torch.float32, mode=tm.SERPENTINE, group=3,
+                   persistent=True)
+    torch.cuda.synchronize()
+    check_tol(host64(c), ref, K, what=f"odd {M}x{N}x{K} {dtype} tile {tile}")
+    check_tol(host64(c32), ref, K, f32_out=True, what=f"odd fp32 {M}x{N}x{K} {dtype} tile {tile}")
+
+
+@pytest.mark.parametrize("tile", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_odd_n_k_integer_exact_untouched_padding_and_schedules(dtype, tile):
+    # integer inputs in [-7, 7]: fp32 sums are exact, 16-bit outputs the exact sum rounded to nearest
+    # even; the output sits inside a larger buffer whose other elements must stay untouched; every
+    # order, remap and launch style gives the same bits
+    M, N, K = 301, 263, 1001
+    a = synth.int_valued((M, K), 45, -7, 7, dtype)
+    b = synth.int_valued((K, N), 46, -7, 7, dtype)
+    exact = og.gemm(a, b, dtype)
+    ad, bd = dev16(a, dtype), dev16(b, dtype)
+    big = torch.full((M + 3, N), 777.0, dtype=torch.float32, device="cuda")
+    c = big[:M]
+    tbl.gemm(ad, bd, c=c, out_dtype=torch.float32, tile=(tile, tile, 32))
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(c), exact)
+    assert torch.all(big[M:] == 777.0)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    want = torch.from_numpy(exact).to(tdt)
+    big16 = torch.full((M + 3, N), -5.0, dtype=tdt, device="cuda")
+    base = big16[:M]
+    tbl.gemm(ad, bd, c=base, tile=(tile, tile, 32))
+    torch.cuda.synchronize()
+    assert torch.equal(base.cpu().view(torch.int16), want.view(torch.int16))
+    assert torch.all(big16[M:] == -5.0)
+    T = (-(-M // tile)) * (-(-N // tile))
+    for mode, g in [(tm.COL, 1), (tm.PANEL, 3), (tm.SERPENTINE, 2)]:
+        for remap in (0, tm.XCD_REMAP):
+            for persistent, P in [(0, 0), (1, 0), (0, 1), (0, T + 3)]:
+                o = tbl.gemm(ad, bd, tile=(tile, tile, 32), mode=mode | remap, group=g,
+                             persistent=bool(persistent), num_programs=P)
+                torch.cuda.synchronize()
+                assert torch.equal(o, base), (mode, remap, persistent, P)
+
+
+def test_odd_n_k_tile_shapes_bit_identical():
+    # the element-wise path takes 32-deep 16x16x32 steps in every tile shape
+    M, N, K = 257, 263, 259
+    a, b = synth.gemm_operands(M, N, K, "bf16", "normal", seed=8)
+    ad, bd = dev16(a, "bf16"), dev16(b, "bf16")
+    outs = [tbl.gemm(ad, bd, tile=(t, t, 32), out_dtype=torch.float32) for t in (64, 128, 256)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_odd_n_k_trace_matches_oracle_schedule():
+    M, N, K = 2000, 1999, 37
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=9)
+    gm, gn = -(-M // 256), -(-N // 256)
+    T = gm * gn
+    trace = torch.full((8 * T,), -1, dtype=torch.int32, device="cuda")
+    tbl.gemm(dev16(a, "f16"), dev16(b, "f16"), mode=tm.SERPENTINE | tm.XCD_REMAP, group=2, persistent=True,
+             num_programs=24, trace=trace)
+    torch.cuda.synchronize()
+    tr = trace.cpu().numpy().reshape(T, 8).astype(np.int64)
+    om, on = tm.tile_table(tm.SERPENTINE | tm.XCD_REMAP, gm, gn, 2)
+    for t in range(T):
+        assert tr[t, 0] == t % 24 and tr[t, 1] == t // 24, t
+    assert np.array_equal(tr[:, 2], om) and np.array_equal(tr[:, 3], on)
+
+
 def test_k_tail_does_not_mix_rows():
     # A K tail reads past the end of each row of A; those elements belong to the next row. An Inf
     # placed at the start of row 1 must only reach row 1 of C.
-    M, N, K = 64, 64, 40
-    a = synth.f16_uniform((M, K), 51)
-    b = synth.f16_uniform((K, N), 52)
-    a[1, 0] = np.float16(np.inf).view(np.uint16)
-    for tile in (64, 128, 256):
-        c = tbl.gemm(dev16(a, "f16"), dev16(b, "f16"), out_dtype=torch.float32, tile=(tile, tile, 32))
-        torch.cuda.synchronize()
-        got = host64(c)
-        assert np.all(np.isfinite(np.delete(got, 1, axis=0))), tile
-        assert not np.all(np.isfinite(got[1])), tile
+    # (K = 41: the element-wise path, whose per-element guards must do the same)
+    for K in (40, 41):
+        M, N = 64, 64
+        a = synth.f16_uniform((M, K), 51)
+        b = synth.f16_uniform((K, N), 52)
+        a[1, 0] = np.float16(np.inf).view(np.uint16)
+        for tile in (64, 128, 256):
+            c = tbl.gemm(dev16(a, "f16"), dev16(b, "f16"), out_dtype=torch.float32, tile=(tile, tile, 32))
+            torch.cuda.synchronize()
+            got = host64(c)
+            assert np.all(np.isfinite(np.delete(got, 1, axis=0))), (K, tile)
+            assert not np.all(np.isfinite(got[1])), (K, tile)
 
 
 @pytest.mark.parametrize("K", [8, 24, 32, 96, 160])

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtbl.so")
-SOURCES = ["api.hip", "gemm.hip", "gemm_layouts.hip", "transpose.hip", "tile_map.hip",
+SOURCES = ["api.hip", "gemm.hip", "gemm_any.hip", "gemm_layouts.hip", "transpose.hip", "tile_map.hip",
            "mfma_rate.hip", "l2_predict.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

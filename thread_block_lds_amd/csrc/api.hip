@@ -98,9 +98,15 @@ void tile_rule(int64_t M, int64_t N, int* bm, int* bn, int* bk) {
   *bk = 32;
 }
 
+// Rows of A and B are whole 16-byte chunks: the fast kernels' direct loads apply; otherwise the
+// element-wise path (gemm_any.hip) runs.
+bool chunk_rows(int64_t N, int64_t K) { return N % 8 == 0 && K % 8 == 0; }
+
+// any_shape: N and K need not be multiples of 8 (tbl_gemm, tbl_gemm_tiled); the dynamic schedule
+// and the LDS-layout variants run only the fast kernel and keep that requirement.
 int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
                   int swizzle_mode, int group, int persistent, int num_programs, int bm, int bn,
-                  int bk) {
+                  int bk, bool any_shape = false) {
   if (A == nullptr || B == nullptr || C == nullptr) return TBL_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0) return TBL_ERR_INVALID_ARG;
   if (dtype < TBL_F16 || dtype > TBL_BF16_F32OUT) return TBL_ERR_DTYPE;
@@ -108,8 +114,9 @@ int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, i
   if (num_programs < 0) return TBL_ERR_INVALID_ARG;
   if (!tbl::gemm_tile_supported(bm, bn, bk)) return TBL_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
-  // rows of B and A must be whole 16-byte chunks; partial tiles at the M, N and K edges are masked
-  if (N % 8 || K % 8) return TBL_ERR_SHAPE;
+  // partial tiles at the M, N and K edges are masked; without any_shape rows of B and A must be
+  // whole 16-byte chunks
+  if (!any_shape && !chunk_rows(N, K)) return TBL_ERR_SHAPE;
   const int64_t gm = (M + bm - 1) / bm, gn = (N + bn - 1) / bn;
   int rc = check_order(swizzle_mode, gm, gn, group);
   if (rc != TBL_OK) return rc;
@@ -119,7 +126,7 @@ int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, i
 }
 
 int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persistent,
-                     int num_programs, int* out) {
+                     int num_programs, int* out, bool chunked = true) {
   if (num_programs > 0) {
     *out = num_programs;
     return TBL_OK;
@@ -132,7 +139,9 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
   int rc = device_info(&d);
   if (rc != TBL_OK) return rc;
   int per_cu = 0;
-  if (tbl::gemm_blocks_per_cu(dtype, bm, bn, bk, &per_cu) != hipSuccess) return TBL_ERR_HIP;
+  const hipError_t e = chunked ? tbl::gemm_blocks_per_cu(dtype, bm, bn, bk, &per_cu)
+                               : tbl::gemm_any_blocks_per_cu(dtype, bm, &per_cu);
+  if (e != hipSuccess) return TBL_ERR_HIP;
   if (per_cu < 1) per_cu = 1;
   const int64_t cap = static_cast<int64_t>(d.cus) * per_cu;
   *out = static_cast<int>(tiles < cap ? tiles : cap);
@@ -171,13 +180,14 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
                    int swizzle_mode, int group_size, int persistent, int num_programs, int block_m,
                    int block_n, int block_k, int32_t* trace, void* stream) {
   int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent, num_programs,
-                         block_m, block_n, block_k);
+                         block_m, block_n, block_k, true);
   if (rc != TBL_OK) return rc;
   const int gm = static_cast<int>((M + block_m - 1) / block_m);
   const int gn = static_cast<int>((N + block_n - 1) / block_n);
+  const bool chunked = chunk_rows(N, K);
   int programs = 0;
   rc = resolve_programs(dtype, block_m, block_n, block_k, static_cast<int64_t>(gm) * gn, persistent,
-                        num_programs, &programs);
+                        num_programs, &programs, chunked);
   if (rc != TBL_OK) return rc;
   tbl::GemmLaunch a;
   a.A = A;
@@ -189,8 +199,9 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
   a.order = make_order(swizzle_mode, gm, gn, group_size);
   a.num_programs = programs;
   a.trace = trace;
-  if (tbl::launch_gemm(dtype, block_m, block_n, block_k, a, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return TBL_ERR_HIP;
+  const hipError_t e = chunked ? tbl::launch_gemm(dtype, block_m, block_n, block_k, a, static_cast<hipStream_t>(stream))
+                               : tbl::launch_gemm_any(dtype, block_m, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return TBL_ERR_HIP;
   return TBL_OK;
 }
 
@@ -351,9 +362,9 @@ int tbl_default_num_programs(int64_t M, int64_t N, int64_t K, int dtype, int per
   if (persistent != 0 && persistent != 1) return TBL_ERR_INVALID_ARG;
   int bm, bn, bk;
   tile_rule(M, N, &bm, &bn, &bk);
-  if (N % 8 || K % 8 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
   return resolve_programs(dtype, bm, bn, bk, ((M + bm - 1) / bm) * ((N + bn - 1) / bn), persistent, 0,
-                          num_programs);
+                          num_programs, chunk_rows(N, K));
 }
 
 int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32_t* tile_m,

@@ -25,6 +25,10 @@ hipError_t launch_gemm(int dtype, int bm, int bn, int bk, const GemmLaunch& a, h
 // Resident workgroups per CU of the kernel for (dtype, tile), from the HIP occupancy query.
 hipError_t gemm_blocks_per_cu(int dtype, int bm, int bn, int bk, int* out);
 bool gemm_tile_supported(int bm, int bn, int bk);
+// Shapes whose rows are not whole 16-byte chunks (N or K not a multiple of 8): the element-wise
+// load path of gemm_any.hip, for the tile shapes gemm_tile_supported accepts (bm == bn).
+hipError_t launch_gemm_any(int dtype, int bm, const GemmLaunch& a, hipStream_t s);
+hipError_t gemm_any_blocks_per_cu(int dtype, int bm, int* out);
 // The 256 x 256 x 32 kernel with the dynamic (work-queue) schedule; a.work and a.xcd_aware set.
 hipError_t launch_gemm_dynamic(int dtype, const GemmLaunch& a, hipStream_t s);
 
