@@ -99,7 +99,8 @@ PMC_PASSES = (("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("fetch", ["FETCH_SIZE"])
               ("write", ["WRITE_SIZE"]),
               ("sq", ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
                       "SQ_INSTS_VALU_MFMA_MOPS_F16", "GRBM_GUI_ACTIVE"]))
-TARGET_PMC = ["TCC_HIT_sum", "TCC_MISS_sum"]   # the 8192^3 target's counter pass
+# the 8192^3 target's counter passes (one rocprofv3 run each: FETCH_SIZE alone takes 3 TCC counters)
+TARGET_PMC_PASSES = (("target_l2", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("target_fetch", ["FETCH_SIZE"]))
 
 
 def _xcd_traffic_floor(xcds=8):
@@ -168,6 +169,11 @@ def target_counter_pass():
         _evict(flush)
         tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=True)
         torch.cuda.synchronize()
+    del ad, bd, c, flush
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)               # the last dispatch (the FETCH_SIZE pass calibrates on the main pass's copy)
+    torch.cuda.synchronize()
     print("target counter pass done", flush=True)
 
 
@@ -251,16 +257,21 @@ def counters():
         # leaves only these figures out
         target = None
         try:
-            rows = _run_pmc(TARGET_PMC, "target_l2", tmp, "--target-counter-pass")
-            gemm = [r for r in rows if _is_gemm(r["kernel"])][1:]   # the first is unmeasured
-            if len(gemm) == len(C3_MODES):
-                target = {}
+            target = {name: {} for name, _, _ in C3_MODES}
+            for tag, ctrs in TARGET_PMC_PASSES:
+                rows = _run_pmc(ctrs, tag, tmp, "--target-counter-pass")
+                gemm = [r for r in rows if _is_gemm(r["kernel"])][1:]   # the first is unmeasured
+                if len(gemm) != len(C3_MODES) or _is_gemm(rows[-1]["kernel"]):
+                    raise RuntimeError(f"{tag}: expected 1 + {len(C3_MODES)} GEMM dispatches, then the copy")
                 for (name, _, _), r in zip(C3_MODES, gemm):
-                    hit, miss = r["TCC_HIT_sum"], r["TCC_MISS_sum"]
-                    target[name] = 100.0 * hit / (hit + miss) if hit + miss > 0 else None
+                    if tag == "target_l2":
+                        hit, miss = r["TCC_HIT_sum"], r["TCC_MISS_sum"]
+                        target[name]["l2_hit_pct"] = 100.0 * hit / (hit + miss) if hit + miss > 0 else None
+                    elif factors.get("fetch"):
+                        target[name]["fetch_mb"] = r["FETCH_SIZE"] * 1024 / factors["fetch"] / 1e6
         except Exception:
             target = None
-        return {"per": per, "factors": factors, "target_l2_hit_pct": target}, None
+        return {"per": per, "factors": factors, "target_counters": target}, None
     except Exception as e:  # counters are reported as null with the reason
         return None, f"{type(e).__name__}: {e}"
     finally:
@@ -434,7 +445,31 @@ def mfma_ceiling(tbl, torch, stream, ad, bd, gemm_tflops=None, reps=5):
     return out
 
 
-def target_check(tbl, torch, stream, measured_hit=None, reps=10):
+def _trace_split(tbl, torch, ad, bd, c, mode, g, nk):
+    """One traced persistent launch: core-clock cycles per 32-deep k step (the MFMAs of one step
+    take 1024 cycles at the chip's peak issue rate) and the core clock, from the per-tile cycle and
+    100 MHz tick counts of the kernel's schedule trace."""
+    M, N = ad.shape[0], bd.shape[1]
+    T = (M // 256) * (N // 256)
+    tr = torch.zeros(8 * T, dtype=torch.int32, device="cuda")
+    tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=True, trace=tr)
+    torch.cuda.synchronize()
+    r = tr.view(T, 8).cpu().double()
+    cyc, ticks = float(r[:, 5].sum()), float(r[:, 6].sum())
+    return {"k_step_cycles": round(cyc / T / nk, 1),
+            "core_clock_ghz": round(cyc / (ticks / 100e6) / 1e9, 3) if ticks else None}
+
+
+def torch_matmul_context(torch, stream, ad, bd, reps=10):
+    """torch.matmul (the vendor BLAS) on the same operands: black-box context, not a target."""
+    for _ in range(3):
+        torch.matmul(ad, bd)
+    ms = _region_ms(torch, stream, lambda: torch.matmul(ad, bd), reps)
+    return {"ms": round(ms, 4), "tflops": round(2.0 * ad.shape[0] * ad.shape[1] * bd.shape[1] / (ms * 1e-3) / 1e12, 1),
+            "what": "torch.matmul on the same bf16 operands (vendor library), back-to-back launches"}
+
+
+def target_check(tbl, torch, stream, measured=None, reps=10):
     """The 8192^3 bf16 persistent workload: median kernel time of back-to-back launches per order."""
     from thread_block_lds_amd import synth
     a, b = synth.gemm_operands(C3, C3, C3, "bf16", "normal", seed=0)
@@ -458,8 +493,12 @@ def target_check(tbl, torch, stream, measured_hit=None, reps=10):
                                       resident=max(1, progs // info["num_xcds"]))
         res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2),
                      "pred_l2_hit_pct": round(100.0 * hits / acc, 2)}
-        if measured_hit and measured_hit.get(name) is not None:
-            res[name]["l2_hit_pct"] = round(measured_hit[name], 2)   # cold launch, rocprofv3 --pmc
+        res[name].update(_trace_split(tbl, torch, ad, bd, c, mode, g, C3 // 32))
+        m = (measured or {}).get(name) or {}
+        if m.get("l2_hit_pct") is not None:
+            res[name]["l2_hit_pct"] = round(m["l2_hit_pct"], 2)    # cold launch, rocprofv3 --pmc
+        if m.get("fetch_mb") is not None:
+            res[name]["fetch_mb"] = round(m["fetch_mb"], 1)        # cold launch, calibrated FETCH_SIZE
     ws = tbl.dynamic_workspace(progs)
     for name, mode, g in C3_DYNAMIC:
         def launch():
@@ -479,6 +518,19 @@ def target_check(tbl, torch, stream, measured_hit=None, reps=10):
         r["speedup_vs_row"] = round(r["tflops"] / res["row"]["tflops"], 4)
     best = max(res, key=lambda n: res[n]["tflops"])
     ceiling = mfma_ceiling(tbl, torch, stream, ad, bd, gemm_tflops=res[best]["tflops"])
+    # the best order's distance from 70 % of the spec peak, split: MFMA issue share of a k step
+    # (1024 cycles of MFMAs per 32-deep step) x the core clock against the 2.4 GHz the peak assumes
+    b = res[best]
+    split = None
+    if b.get("k_step_cycles") and b.get("core_clock_ghz"):
+        issue = 1024.0 / b["k_step_cycles"]
+        clock = b["core_clock_ghz"] / 2.4
+        split = {"mfma_issue_share": round(issue, 4), "clock_share": round(clock, 4),
+                 "product": round(issue * clock, 4), "measured_frac": round(b["pct_peak"] / 100, 4),
+                 "mfma_only_clock_ghz": ceiling.get("core_clock_ghz"),
+                 "needed_for_70pct": {"clock_ghz_at_these_cycles": round(0.7 * 2.4 * b["k_step_cycles"] / 1024, 3),
+                                      "k_step_cycles_at_this_clock": round(1024 * b["core_clock_ghz"] / (0.7 * 2.4), 1)}}
+    matmul = torch_matmul_context(torch, stream, ad, bd)
     del ad, bd, c
     # the same shape in fp16 (uniform[-1, 1] inputs, fp16 out): the fp16-peak form of the target,
     # for the two remapped orders, with the MFMA-only rate on these fp16 operands
@@ -502,7 +554,7 @@ def target_check(tbl, torch, stream, measured_hit=None, reps=10):
                         "persistent stride schedule (and the dynamic work-queue schedule) over CUs x occupancy programs",
             "programs": tbl.default_num_programs(C3, C3, C3, tbl.BF16, persistent=True),
             "orders": res, "best": best, "best_pct_peak": res[best]["pct_peak"], "target_pct_peak": 70.0,
-            "mfma_ceiling_same_data": ceiling,
+            "mfma_ceiling_same_data": ceiling, "gap_split_best": split, "torch_matmul_context": matmul,
             "f16": {"workload": "the same shape in fp16: uniform[-1,1] inputs, fp16 out, persistent",
                     "orders": res16, "best": best16, "best_pct_peak": res16[best16]["pct_peak"],
                     "mfma_ceiling_same_data": ceiling16}}
@@ -802,7 +854,7 @@ def main():
     pred, pred_cfg = predictions(tbl)
     ceiling = mfma_ceiling(tbl, torch, stream, ad, bd)
     transpose = time_transpose(tbl, torch, stream)
-    target = target_check(tbl, torch, stream, ctr.get("target_l2_hit_pct") if ctr else None)
+    target = target_check(tbl, torch, stream, ctr.get("target_counters") if ctr else None)
 
     ms_step = wall * 1e3 / args.steps
     per_mode = {}

@@ -54,7 +54,7 @@ _COST = {"FETCH_SIZE": ("TCC_", 3), "WRITE_SIZE": ("TCC_", 2)}
 _LIMIT = {"SQ_": 8, "TCC_": 4, "TCP_": 4, "TA_": 2, "TD_": 2, "GRBM_": 2}
 
 
-@pytest.mark.parametrize("tag,ctrs", list(bench.PMC_PASSES) + [("target_l2", bench.TARGET_PMC)])
+@pytest.mark.parametrize("tag,ctrs", list(bench.PMC_PASSES) + list(bench.TARGET_PMC_PASSES))
 def test_counter_passes_fit_one_run(tag, ctrs):
     used = {}
     for c in ctrs:
