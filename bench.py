@@ -279,19 +279,19 @@ def counters():
 
 
 def rank_corr(x, y):
-    """Spearman coefficient with ties ranked in index order (as the page's harness ranks them)."""
+    """Spearman coefficient (Pearson correlation of ranks) with equal values ranked in index order,
+    the page's rule. The rank of value i counts the values below it plus the equal values at lower
+    indices; n is at most a few dozen here, so the counting is done directly."""
     def ranks(v):
-        r = [0] * len(v)
-        for pos, i in enumerate(sorted(range(len(v)), key=lambda i: v[i])):
-            r[i] = pos
-        return r
-    rx, ry = ranks(list(x)), ranks(list(y))
+        v = list(v)
+        return [sum(1 for j, w in enumerate(v) if w < vi or (w == vi and j < i)) for i, vi in enumerate(v)]
+    rx, ry = ranks(x), ranks(y)
     n = len(rx)
-    mx, my = sum(rx) / n, sum(ry) / n
-    cov = sum((a - mx) * (b - my) for a, b in zip(rx, ry))
-    vx = sum((a - mx) ** 2 for a in rx)
-    vy = sum((b - my) ** 2 for b in ry)
-    return cov / (vx * vy) ** 0.5 if vx and vy else 0.0
+    if n < 2:
+        return 0.0
+    # ranks are a permutation of 0 .. n-1: mean (n - 1) / 2, sum of squared deviations n (n^2 - 1) / 12
+    mean, ss = (n - 1) / 2.0, n * (n * n - 1) / 12.0
+    return sum((a - mean) * (b - mean) for a, b in zip(rx, ry)) / ss
 
 
 def predictions(tbl):

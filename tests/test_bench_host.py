@@ -70,3 +70,21 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_rank_corr_matches_the_oracles_and_the_page():
+    # bench.py's own Spearman (no oracle import on its measured path) against the oracle's, on
+    # random data with ties, and on the page's printed columns (0.045 / 0.064)
+    import numpy as np
+    from conftest import golden_lines
+    from oracle import l2_model
+    rng = np.random.default_rng(3)
+    for n in (2, 5, 12, 30):
+        for _ in range(20):
+            x = rng.integers(0, 6, size=n).tolist()
+            y = rng.integers(0, 6, size=n).tolist()
+            assert abs(bench.rank_corr(x, y) - l2_model.rank_correlation(x, y)) < 1e-12
+    rows = [ln.split() for ln in golden_lines("p1_predicted_l2_hit_rates.txt") if not ln.startswith("spearman")]
+    pred = [float(r[3]) for r in rows]
+    assert round(bench.rank_corr(pred, [float(r[4]) for r in rows]), 3) == 0.045
+    assert round(bench.rank_corr(pred, [float(r[5]) for r in rows]), 3) == 0.064

@@ -77,17 +77,17 @@ def test_lru_matches_brute_force(seed):
         cache.access(key, sz)
     assert cache.hits == _brute_lru(trace, capacity)
     assert cache.hits + cache.misses == len(trace)
-    assert cache.used <= max(capacity, max(sz for _, sz in trace))
+    assert cache.bytes_held <= max(capacity, max(sz for _, sz in trace))
 
 
 def test_oversize_block_is_kept_alone():
     cache = l2_model.ByteLRU(10)
     cache.access("big", 50)
-    assert list(cache.blocks) == ["big"] and cache.used == 50
+    assert list(cache.held) == ["big"] and cache.bytes_held == 50
     cache.access("big", 50)
     assert cache.hits == 1
     cache.access("small", 4)
-    assert list(cache.blocks) == ["small"] and cache.used == 4
+    assert list(cache.held) == ["small"] and cache.bytes_held == 4
 
 
 @pytest.mark.parametrize("mode,group", [(tm.ROW, 1), (tm.PANEL, 3), (tm.SERPENTINE, 2), (tm.COL, 1)])
