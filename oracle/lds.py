@@ -204,3 +204,67 @@ def gemm_lds_conflicts(M, N, K, layout, tile=256, waves=(2, 4)):
     steps = -(-K // 32)
     a, b = gemm_operand_read_passes(*layout, tile=tile, waves=waves)
     return tiles * steps * (a + b)
+
+
+def swz_b_kstep8(k):
+    """The 16x16x32 kernel's B chunk XOR, as a function of the k row: 4 (k mod 4) + 2 ((k / 8) mod 2).
+    The first term is the (vec 4 chunks, perPhase 1, maxPhase 4) member of the Triton family; the
+    second separates rows 8 apart, which one transposing read of this MFMA form pairs up."""
+    return 4 * (k % 4) + 2 * ((k // 8) % 2)
+
+
+def gemm16_operand_read_passes(a_per_phase, a_max_phase, b_xor, tile=256, waves=(2, 4), num_banks=64,
+                               bank_bytes=4):
+    """Extra LDS passes of one workgroup's operand reads in one 32-deep k step of the 16x16x32 form.
+
+    Layouts as gemm_operand_read_passes: A rows of 32 k (4 chunks of 16 bytes) swizzled by the
+    Triton chunk XOR (vec 8 elements, a_per_phase, a_max_phase); B k-major rows of ``tile`` n
+    values whose 16-byte chunk c of row k is stored at chunk c XOR b_xor(k) (b_xor: a function of k,
+    e.g. the family member lambda k: 4 * (k % 4), or swz_b_kstep8).
+    Read instructions of the 16x16x32 MFMA operands (the kernel's lane patterns):
+      * A: one 16-byte read per lane and 16-row block i of a wave's rows: lane l reads row
+        r0 + 16 i + (l mod 16) at k = 8 (l div 16), so a 32-lane half-wave reads 16 rows x 2 chunks;
+      * B: two transposing 8-byte reads per 16-column block j of a wave's columns (h = 0, 1): lane
+        r of 16-lane group g reads row k = 8 g + 4 h + r div 4 at columns n0 + 16 j + 4 (r mod 4)
+        .. + 3, so a half-wave reads 4 rows and the 4 rows 8 further on.
+    Bank geometry as gemm_operand_read_passes (64 banks of 4 bytes, 32-lane phases).
+    Returns (extra passes of all A reads, extra passes of all B reads) per workgroup and k step.
+    """
+    wave_m, wave_n = tile // waves[0], tile // waves[1]
+    if wave_m % 16 or wave_n % 16:
+        raise ValueError("wave sub-tiles must be whole 16 x 16 MFMA blocks")
+    b_stage = tile * 32 * 2
+    extra_a = extra_b = 0
+    for wm in range(waves[0]):
+        for i in range(wave_m // 16):
+            addrs = [2 * chunk_xor(wave_m * wm + 16 * i + (l % 16), 8 * (l // 16), 32, 8, a_per_phase,
+                                   a_max_phase) for l in range(64)]
+            p, ideal = instruction_passes(addrs, 16, num_banks, bank_bytes, lanes_per_phase=32)
+            extra_a += (p - ideal) * waves[1]
+    for wn in range(waves[1]):
+        for j in range(wave_n // 16):
+            for h in range(2):
+                addrs = []
+                for l in range(64):
+                    g, r = l // 16, l % 16
+                    k = 8 * g + 4 * h + r // 4
+                    n = wave_n * wn + 16 * j + 4 * (r % 4)
+                    chunk = (n // 8) ^ b_xor(k)
+                    addrs.append(b_stage + 2 * (k * tile + chunk * 8 + n % 8))
+                p, ideal = instruction_passes(addrs, 8, num_banks, bank_bytes, lanes_per_phase=32)
+                extra_b += (p - ideal) * waves[0]
+    return extra_a, extra_b
+
+
+# B layouts of the 16x16x32 form by name: the kernel's default, the 32x32x16 form's (vec 4 chunks,
+# perPhase 1, maxPhase 4) family member, and no swizzle
+GEMM16_B_LAYOUTS = {"kstep8": swz_b_kstep8, "vec4": lambda k: 4 * (k % 4), "none": lambda k: 0}
+
+
+def gemm16_lds_conflicts(M, N, K, a_per_phase, a_max_phase, b_layout, tile=256, waves=(2, 4)):
+    """Predicted LDS bank-conflict cycles of one 16x16x32 GEMM launch (every workgroup, every 32-deep
+    k step of its tiles, gemm16_operand_read_passes per step)."""
+    tiles = -(-M // tile) * -(-N // tile)
+    steps = -(-K // 32)
+    a, b = gemm16_operand_read_passes(a_per_phase, a_max_phase, GEMM16_B_LAYOUTS[b_layout], tile, waves)
+    return tiles * steps * (a + b)

@@ -142,3 +142,48 @@ def test_gemm_lds_conflicts_scales_with_tiles_and_steps():
     assert lds.gemm_lds_conflicts(4096, 4096, 4096, (4, 4, 4, 1, 4)) == 0
     with pytest.raises(ValueError):
         lds.gemm_operand_read_passes(4, 4, 4, 1, 4, waves=(2, 16))
+
+
+# ---- the 16x16x32 form's operand reads (same geometry) ----
+#
+# Hand counts per read instruction:
+#   A: a 32-lane phase reads 16 consecutive rows at 2 logical chunks (lanes 0-31: chunks 0, 1;
+#   lanes 32-63: chunks 2, 3). Bank group = 4 (r mod 4) + physical chunk. Unswizzled, or with a
+#   phase value that takes one bit from the rows (perPhase 4, maxPhase 2: bit 2), only the chunk
+#   pair's two groups per r mod 4 are used: 8 groups, 4 lanes each -> 4 passes against 2: 2 extra
+#   per phase, 4 per instruction. A phase value with two bits above bit 1 of the row (perPhase 2 or
+#   4 with maxPhase 4) spreads each r mod 4 over all 4 groups of its quarter: conflict-free.
+#   B: a phase reads k rows k0 .. k0 + 3 and k0 + 8 .. k0 + 11 (512-byte pitch: the same window
+#   position) at 4 eight-byte column offsets of one 32-byte span. Unswizzled all 8 rows land on the
+#   same 4 bank pairs: 8 passes against 1, 7 extra per phase, 14 per instruction. The family member
+#   4 (k mod 4) (in chunks) separates k mod 4 but not the rows 8 apart: 2 passes, 2 extra per
+#   instruction. The kernel's layout adds 2 ((k / 8) mod 2): conflict-free.
+HAND16 = [((2, 4, "kstep8"), (0, 0)), ((4, 4, "kstep8"), (0, 0)), ((1, 1, "kstep8"), (4, 0)),
+          ((4, 2, "kstep8"), (4, 0)), ((2, 4, "vec4"), (0, 2)), ((2, 4, "none"), (0, 14))]
+
+
+@pytest.mark.parametrize("layout,per_inst", HAND16)
+def test_gemm16_operand_read_passes_hand_counts(layout, per_inst):
+    # per workgroup and 32-deep step: A 2 row groups x 8 blocks x 4 waves reading each; B 4 column
+    # groups x 4 blocks x 2 reads x 2 waves reading each
+    a_pp, a_mp, b = layout
+    assert lds.gemm16_operand_read_passes(a_pp, a_mp, lds.GEMM16_B_LAYOUTS[b]) == (64 * per_inst[0],
+                                                                                  64 * per_inst[1])
+
+
+def test_gemm16_kernel_b_layout_is_the_family_member_plus_the_kstep8_term():
+    for k in range(64):
+        assert lds.swz_b_kstep8(k) == lds.GEMM16_B_LAYOUTS["vec4"](k) ^ (2 * ((k // 8) % 2))
+    # XOR by a value constant over a row keeps each row's chunks a permutation
+    for k in range(32):
+        assert sorted((c ^ lds.swz_b_kstep8(k)) for c in range(32)) == list(range(32))
+
+
+def test_gemm16_fixture_matches_the_oracle():
+    from conftest import golden_lines
+    names = {(0, 0, 0): "kstep8", (4, 1, 4): "vec4", (1, 1, 1): "none"}
+    for ln in golden_lines("gemm16_lds_conflicts_4096.txt"):
+        v = [int(x) for x in ln.split()]
+        b = names[tuple(v[2:5])]
+        assert lds.gemm16_operand_read_passes(v[0], v[1], lds.GEMM16_B_LAYOUTS[b]) == (v[5], v[6])
+        assert lds.gemm16_lds_conflicts(4096, 4096, 4096, v[0], v[1], b) == v[7]
