@@ -676,10 +676,11 @@ def page_sweep(reps=10):
                       "orders": out, "spearman": spear, "counters_note": note}), flush=True)
 
 
-def _layout_predictions():
-    """The oracle's predicted conflict cycles per layout, from the committed fixture written by
-    tests/golden/make_gemm_lds_conflicts.py."""
-    path = os.path.join(ROOT, "tests", "golden", "gemm_lds_conflicts_4096.txt")
+def _layout_predictions(name="gemm_lds_conflicts_4096.txt"):
+    """The oracle's predicted conflict cycles per layout, from a committed fixture written by
+    tests/golden/make_gemm_lds_conflicts.py (32x32x16 form) or make_gemm16_lds_conflicts.py
+    (16x16x32 form)."""
+    path = os.path.join(ROOT, "tests", "golden", name)
     out = {}
     for ln in open(path):
         tok = ln.split()
@@ -699,6 +700,9 @@ def lds_sweep_pass():
     torch.cuda.synchronize()
     for layout in tbl.LDS_LAYOUTS:
         tbl.gemm_lds_layout(ad, bd, layout, c)
+        torch.cuda.synchronize()
+    for layout in tbl.LDS_LAYOUTS16:
+        tbl.gemm_lds_layout(ad, bd, layout, c, mfma16=True)
         torch.cuda.synchronize()
     print("lds sweep pass done", flush=True)
 
@@ -726,22 +730,25 @@ def lds_sweep(reps=10):
     stream = torch.cuda.current_stream()
     _, _, ad, bd = _operands()
     c = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    pred = _layout_predictions()
+    variants = ([(layout, False) for layout in tbl.LDS_LAYOUTS] + [(layout, True) for layout in tbl.LDS_LAYOUTS16])
+    preds = {False: _layout_predictions(), True: _layout_predictions("gemm16_lds_conflicts_4096.txt")}
     res = []
-    for i, layout in enumerate(tbl.LDS_LAYOUTS):
+    for i, (layout, m16) in enumerate(variants):
         def launch():
-            tbl.gemm_lds_layout(ad, bd, layout, c, stream=stream.cuda_stream)
+            tbl.gemm_lds_layout(ad, bd, layout, c, stream=stream.cuda_stream, mfma16=m16)
         launch()
         ms = _median_ms(torch, stream, launch, reps)
-        rec = {"layout": dict(zip(("a_per_phase", "a_max_phase", "b_vec", "b_per_phase", "b_max_phase"), layout)),
+        rec = {"mfma": "16x16x32" if m16 else "32x32x16",
+               "layout": dict(zip(("a_per_phase", "a_max_phase", "b_vec", "b_per_phase", "b_max_phase"), layout)),
                "ms": round(ms, 5), "tflops": round(FLOPS / (ms * 1e-3) / 1e12, 1),
-               "predicted_conflict_cycles": pred.get(tuple(layout))}
-        if measured is not None and len(measured) == len(tbl.LDS_LAYOUTS):
+               "predicted_conflict_cycles": preds[m16].get(tuple(layout))}
+        if measured is not None and len(measured) == len(variants):
             conf, active, insts = measured[i]
             rec.update({"measured_conflict_cycles": int(conf), "lds_active_cycles": int(active),
                         "lds_instructions": int(insts)})
         res.append(rec)
-    print(json.dumps({"sweep": "LDS operand layouts of the 256x256x32 fp16 GEMM, 4096^3, row order",
+    print(json.dumps({"sweep": "LDS operand layouts of the 256x256x32 fp16 GEMM, 4096^3, row order, in "
+                               "both MFMA forms",
                       "layouts": res, "counters_note": note}), flush=True)
 
 

@@ -11,7 +11,8 @@
  *   - tbl_gemm_dynamic: the same GEMM with a dynamic persistent schedule, tiles handed out at run
  *     time by counters -- what the persistent tile loop of "CUDA Thread Block Swizzle" (section
  *     "CUDA Thread Block Swizzle Benchmark", its "Known limitations") notes it does not have.
- *   - tbl_gemm_lds_layout: the same GEMM with the operands' LDS swizzles taken from the chunk-XOR
+ *   - tbl_gemm_lds_layout, tbl_gemm_lds_layout16: the same GEMM (32x32x16- or 16x16x32-MFMA form)
+ *     with the operands' LDS swizzles taken from the chunk-XOR
  *     family of "CUDA Swizzle & bank conflict" (section "Triton - Shared Layout swizzling").
  *   - tbl_tile_map: the program-id -> (m, n) table of any order, computed by the same device code
  *     the GEMM uses.
@@ -244,6 +245,23 @@ int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_
                         int dtype, int swizzle_mode, int group_size, int persistent, int num_programs,
                         int a_per_phase, int a_max_phase, int b_vec, int b_per_phase,
                         int b_max_phase, void* stream);
+
+/*
+ * tbl_gemm_lds_layout16 -- tbl_gemm_lds_layout in the 16x16x32-MFMA form that tbl_gemm runs (the
+ * same source, same section of "CUDA Swizzle & bank conflict"), whose operand reads take other lane
+ * patterns (A: 16 rows x 2 chunks per half-wave; B: transposing reads of k rows k0..k0+3 and
+ * k0+8..k0+11). b_vec = 0 (with b_per_phase = b_max_phase = 0) selects its default B layout, chunk c
+ * of row k at c XOR (4 (k mod 4) + 2 ((k / 8) mod 2)); other B triples are family members as above.
+ * Every variant returns the same bits as tbl_gemm_tiled with 256x256x32 tiles.
+ *   (a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase) one of the compiled variants:
+ *                 (2,4,0,0,0) the default kernel's layouts; (4,4,0,0,0), (1,1,0,0,0) and (4,2,0,0,0)
+ *                 vary A; (2,4,4,1,4) and (2,4,1,1,1) vary B. TBL_ERR_INVALID_ARG otherwise.
+ *   All other arguments and errors as tbl_gemm_lds_layout.
+ */
+int tbl_gemm_lds_layout16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                          int dtype, int swizzle_mode, int group_size, int persistent, int num_programs,
+                          int a_per_phase, int a_max_phase, int b_vec, int b_per_phase,
+                          int b_max_phase, void* stream);
 
 /*
  * tbl_tile_map -- write the forward table of an order: tile_m[t], tile_n[t] for t in [0, T).

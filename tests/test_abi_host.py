@@ -200,3 +200,16 @@ def _rate(A=FAKE, B=FAKE, elems=1 << 20, dtype=0, wg=256, iters=100, out=FAKE, c
 ])
 def test_mfma_rate_rejects(kw, want):
     assert _rate(**kw) == want
+
+
+def _layout16(layout=(2, 4, 0, 0, 0), dtype=0, M=512, N=512, K=512, A=FAKE):
+    return tbl.lib().tbl_gemm_lds_layout16(A, FAKE, FAKE, M, N, K, dtype, 0, 1, 0, 0, *layout, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(layout=(8, 4, 0, 0, 0)), tbl.ERR_INVALID_ARG), (dict(layout=(4, 4, 4, 1, 4)), tbl.ERR_INVALID_ARG),
+    (dict(layout=(2, 4, 0, 0, 1)), tbl.ERR_INVALID_ARG), (dict(dtype=tbl.BF16), tbl.ERR_DTYPE),
+    (dict(A=NULL), tbl.ERR_INVALID_ARG), (dict(N=500), tbl.ERR_SHAPE), (dict(A=MISALIGNED), tbl.ERR_ALIGN),
+])
+def test_gemm_lds_layout16_rejects(kw, want):
+    assert _layout16(**kw) == want

@@ -1,4 +1,5 @@
-"""GPU parity of tbl_gemm_lds_layout: every compiled operand-layout variant of the 256x256x32 fp16
+"""GPU parity of tbl_gemm_lds_layout and tbl_gemm_lds_layout16: every compiled operand-layout
+variant of the 256x256x32 fp16
 GEMM returns the oracle's product within the fp16-output bar and exactly the bits of the default
 layout (the layout moves operands around in LDS; it never changes which values are multiplied or
 in which k order they are summed).
@@ -56,3 +57,42 @@ def test_layouts_bit_identical_to_default(M, N, K, mode, group):
     # and the result is the product: sampled rows against the oracle
     rows = np.arange(0, M, max(1, M // 7))
     check_tol(host64(ref[torch.from_numpy(rows).cuda()]), og.gemm_rows(a, b, "f16", rows), K)
+
+
+# ---- the 16x16x32 form (tbl_gemm_lds_layout16) ----
+
+def test_layout16_list():
+    assert len(set(tbl.LDS_LAYOUTS16)) == len(tbl.LDS_LAYOUTS16) == 6
+    assert tbl.LDS_LAYOUTS16[0] == (2, 4, 0, 0, 0)
+
+
+@pytest.mark.parametrize("layout", tbl.LDS_LAYOUTS16)
+def test_layout16_matches_oracle_on_ragged_shape(layout):
+    M, N, K = 300, 520, 264
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=13)
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    c = tbl.gemm_lds_layout(ad, bd, layout, mode=tm.SERPENTINE, group=2, mfma16=True)
+    torch.cuda.synchronize()
+    check_tol(host64(c), og.gemm(a, b, "f16"), K, what=str(layout))
+    ref = tbl.gemm(ad, bd, mode=tm.SERPENTINE, group=2, tile=TILE)
+    torch.cuda.synchronize()
+    assert torch.equal(c, ref), layout
+
+
+def test_layouts16_bit_identical_to_default_at_4096():
+    M = N = K = 4096
+    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=14)
+    ad, bd = dev16(a, "f16"), dev16(b, "f16")
+    ref = tbl.gemm(ad, bd, mode=tm.PANEL | tm.XCD_REMAP, group=4, tile=TILE)
+    torch.cuda.synchronize()
+    for layout in tbl.LDS_LAYOUTS16:
+        c = tbl.gemm_lds_layout(ad, bd, layout, mode=tm.PANEL | tm.XCD_REMAP, group=4, mfma16=True)
+        torch.cuda.synchronize()
+        assert torch.equal(c, ref), layout
+
+
+def test_layout16_rejects_unknown_variant():
+    a = torch.zeros((512, 512), dtype=torch.float16, device="cuda")
+    with pytest.raises(tbl.TblError) as e:
+        tbl.gemm_lds_layout(a, a, (8, 4, 0, 0, 0), mfma16=True)   # A must repeat every 16 rows
+    assert e.value.status == tbl.ERR_INVALID_ARG

@@ -52,6 +52,11 @@ _EXPORTS = {
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "tbl_gemm_lds_layout16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "tbl_gemm_dynamic": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -286,10 +291,16 @@ LDS_LAYOUTS = [(4, 4, 4, 1, 4), (1, 1, 4, 1, 4), (1, 4, 4, 1, 4), (2, 4, 4, 1, 4
                (4, 4, 4, 2, 2), (4, 4, 8, 1, 4)]
 
 
+# the same for the 16x16x32 form (tbl_gemm_lds_layout16); b_vec 0 = that form's default B layout
+LDS_LAYOUTS16 = [(2, 4, 0, 0, 0), (4, 4, 0, 0, 0), (1, 1, 0, 0, 0), (4, 2, 0, 0, 0), (2, 4, 4, 1, 4),
+                 (2, 4, 1, 1, 1)]
+
+
 def gemm_lds_layout(a, b, layout, c=None, mode=ROW, group=1, persistent=False, num_programs=0,
-                    stream=None):
+                    stream=None, mfma16=False):
     """C = A @ B (fp16 in, fp16 out, 256x256x32 tiles) with the LDS swizzles ``layout`` =
-    (a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase) through tbl_gemm_lds_layout."""
+    (a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase) through tbl_gemm_lds_layout, or,
+    with ``mfma16``, through tbl_gemm_lds_layout16 (the default kernel's 16x16x32 form)."""
     import torch
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"shape mismatch {tuple(a.shape)} x {tuple(b.shape)}")
@@ -306,10 +317,10 @@ def gemm_lds_layout(a, b, layout, c=None, mode=ROW, group=1, persistent=False, n
     for t, name in ((a, "A"), (b, "B"), (c, "C")):
         _device_tensor(t, name, device=a.device)
     app, amp, bv, bpp, bmp = (int(x) for x in layout)
-    st = lib().tbl_gemm_lds_layout(_ptr(a), _ptr(b), _ptr(c), M, N, K, F16, int(mode), int(group),
-                                   int(bool(persistent)), int(num_programs), app, amp, bv, bpp, bmp,
-                                   _stream(stream))
-    _check(st, "tbl_gemm_lds_layout")
+    fn = lib().tbl_gemm_lds_layout16 if mfma16 else lib().tbl_gemm_lds_layout
+    st = fn(_ptr(a), _ptr(b), _ptr(c), M, N, K, F16, int(mode), int(group), int(bool(persistent)),
+            int(num_programs), app, amp, bv, bpp, bmp, _stream(stream))
+    _check(st, "tbl_gemm_lds_layout16" if mfma16 else "tbl_gemm_lds_layout")
     return c
 
 

@@ -205,15 +205,19 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
   return TBL_OK;
 }
 
-int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                        int dtype, int swizzle_mode, int group_size, int persistent, int num_programs,
-                        int a_per_phase, int a_max_phase, int b_vec, int b_per_phase,
-                        int b_max_phase, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int gemm_lds_layout_impl(bool m16, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                         int64_t K, int dtype, int swizzle_mode, int group_size, int persistent,
+                         int num_programs, int a_per_phase, int a_max_phase, int b_vec,
+                         int b_per_phase, int b_max_phase, void* stream) {
   int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent, num_programs,
                          256, 256, 32);
   if (rc != TBL_OK) return rc;
   if (dtype != TBL_F16) return TBL_ERR_DTYPE;
-  if (!tbl::gemm_layout_supported(a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase))
+  if (!tbl::gemm_layout_supported(m16, a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase))
     return TBL_ERR_INVALID_ARG;
   const int gm = static_cast<int>((M + 255) / 256), gn = static_cast<int>((N + 255) / 256);
   int programs = 0;
@@ -230,10 +234,32 @@ int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_
   a.order = make_order(swizzle_mode, gm, gn, group_size);
   a.num_programs = programs;
   a.trace = nullptr;
-  if (tbl::launch_gemm_layout(a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase, a,
+  if (tbl::launch_gemm_layout(m16, a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase, a,
                               static_cast<hipStream_t>(stream)) != hipSuccess)
     return TBL_ERR_HIP;
   return TBL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                        int dtype, int swizzle_mode, int group_size, int persistent, int num_programs,
+                        int a_per_phase, int a_max_phase, int b_vec, int b_per_phase,
+                        int b_max_phase, void* stream) {
+  return gemm_lds_layout_impl(false, A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent,
+                              num_programs, a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase,
+                              stream);
+}
+
+int tbl_gemm_lds_layout16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                          int dtype, int swizzle_mode, int group_size, int persistent, int num_programs,
+                          int a_per_phase, int a_max_phase, int b_vec, int b_per_phase,
+                          int b_max_phase, void* stream) {
+  return gemm_lds_layout_impl(true, A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent,
+                              num_programs, a_per_phase, a_max_phase, b_vec, b_per_phase, b_max_phase,
+                              stream);
 }
 
 int64_t tbl_gemm_dynamic_workspace(int num_programs) {

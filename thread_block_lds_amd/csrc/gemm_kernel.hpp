@@ -170,6 +170,14 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
 // of 8 bytes land on 32 distinct bank pairs.
 __device__ __forceinline__ int swz_b16(int k) { return (4 * (k & 3)) | (2 * ((k >> 3) & 1)); }
 
+// The B chunk XOR a kernel instantiation uses: in the 16 x 16 x 32 form kBV = 0 selects swz_b16 (the
+// default); any other (kBV, kBPP, kBMP) is that member of the chunk-XOR family.
+template <bool kM16, int kBV, int kBPP, int kBMP, int kChunks>
+__device__ __forceinline__ int swz_b_of(int k) {
+  if constexpr (kM16 && kBV == 0) return swz_b16(k);
+  else return swz_b<kBV, kBPP, kBMP, kChunks>(k);
+}
+
 // Store a wave's sub-tile of 16 x 16 accumulator blocks: lane l holds row (l mod 16) and columns
 // 4 (l / 16) .. + 3 of block (i, j). fp32 output stores those 16 bytes per lane (64 contiguous
 // bytes of each of 16 rows per store). 16-bit output packs each block's four values into 8 bytes

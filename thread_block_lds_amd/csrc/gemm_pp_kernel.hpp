@@ -88,8 +88,10 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   static_assert(kStages == 5, "loads run four steps ahead");
   static_assert(kAPP >= 1 && kAMP >= 1 && kAMP <= 4 && (32 / kAPP) % kAMP == 0 && 32 % kAPP == 0,
                 "A swizzle must repeat every 32 rows");
-  static_assert(kBPP >= 1 && kBMP >= 1 && 4 % kBPP == 0 && (4 / kBPP) % kBMP == 0,
+  static_assert((kM16 && kBV == 0) || (kBPP >= 1 && kBMP >= 1 && 4 % kBPP == 0 && (4 / kBPP) % kBMP == 0),
                 "B swizzle must repeat every 4 k rows");
+  // the 16 x 16 x 32 reads address A blocks 16 rows apart from one base
+  static_assert(!kM16 || (16 / kAPP) % kAMP == 0, "A swizzle must repeat every 16 rows");
 
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
 
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   for (int j = 0; j < kBInst; ++j) {
     const int o = (wave * kBInst + j) * 1024 + 16 * lane;
     const int k = o / kBRow;
-    const int chunk = ((o % kBRow) >> 4) ^ (kM16 ? swz_b16(k) : swz_b<kBV, kBPP, kBMP, kBChunks>(k));
+    const int chunk = ((o % kBRow) >> 4) ^ swz_b_of<kM16, kBV, kBPP, kBMP, kBChunks>(k);
     b_voff[j] = (k * N + chunk * 8) * 2;
   }
   // ---- per-lane constants of the operand reads ----
@@ -207,8 +209,8 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     const int chunk = (2 * h + (lane >> 5)) ^ swz_a<kAPP, kAMP>(row);
     a_rd[h] = row * kARow + chunk * 16;
   }
-  int b_rd[TN];
-  {
+  int b_rd[TN] = {};
+  if constexpr (!kM16) {
     const int g = lane >> 4, r = lane & 15;
     const int k = 8 * (g >> 1) + (r >> 2);
 #pragma unroll
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
 #pragma unroll
     for (int j = 0; j < TN16; ++j) {
       const int n = wn * WN + j * 16 + 4 * (r & 3);
-      b_rd16[j] = kAStage + k * kBRow + ((n >> 3) ^ swz_b16(k)) * 16 + (n & 7) * 2;
+      b_rd16[j] = kAStage + k * kBRow + ((n >> 3) ^ swz_b_of<kM16, kBV, kBPP, kBMP, kBChunks>(k)) * 16 + (n & 7) * 2;
     }
   }
 
@@ -541,7 +543,7 @@ constexpr int kM16APP = 2, kM16AMP = 4;
 template <bool kBf16, bool kF32Out>
 const void* pp_kernel_ptr() {
   return reinterpret_cast<const void*>(
-      &gemm_pp_kernel<kBf16, kF32Out, kM16APP, kM16AMP, 4, 1, 4, false, true>);
+      &gemm_pp_kernel<kBf16, kF32Out, kM16APP, kM16AMP, 0, 0, 0, false, true>);
 }
 
 const void* pp_kernel_for(int dtype) {
@@ -566,10 +568,10 @@ hipError_t launch_pp_typed(const GemmLaunch& a, hipStream_t s) {
 
 hipError_t launch_pp(int dtype, const GemmLaunch& a, hipStream_t s) {
   switch (dtype) {
-    case 0: return launch_pp_typed<false, false, kM16APP, kM16AMP, 4, 1, 4, false, true>(a, s);
-    case 1: return launch_pp_typed<true, false, kM16APP, kM16AMP, 4, 1, 4, false, true>(a, s);
-    case 2: return launch_pp_typed<false, true, kM16APP, kM16AMP, 4, 1, 4, false, true>(a, s);
-    case 3: return launch_pp_typed<true, true, kM16APP, kM16AMP, 4, 1, 4, false, true>(a, s);
+    case 0: return launch_pp_typed<false, false, kM16APP, kM16AMP, 0, 0, 0, false, true>(a, s);
+    case 1: return launch_pp_typed<true, false, kM16APP, kM16AMP, 0, 0, 0, false, true>(a, s);
+    case 2: return launch_pp_typed<false, true, kM16APP, kM16AMP, 0, 0, 0, false, true>(a, s);
+    case 3: return launch_pp_typed<true, true, kM16APP, kM16AMP, 0, 0, 0, false, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -585,10 +587,10 @@ hipError_t launch_pp_dynamic(int dtype, const GemmLaunch& a, hipStream_t s) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (dtype) {
-    case 0: return launch_pp_typed<false, false, kM16APP, kM16AMP, 4, 1, 4, true, true>(a, s);
-    case 1: return launch_pp_typed<true, false, kM16APP, kM16AMP, 4, 1, 4, true, true>(a, s);
-    case 2: return launch_pp_typed<false, true, kM16APP, kM16AMP, 4, 1, 4, true, true>(a, s);
-    case 3: return launch_pp_typed<true, true, kM16APP, kM16AMP, 4, 1, 4, true, true>(a, s);
+    case 0: return launch_pp_typed<false, false, kM16APP, kM16AMP, 0, 0, 0, true, true>(a, s);
+    case 1: return launch_pp_typed<true, false, kM16APP, kM16AMP, 0, 0, 0, true, true>(a, s);
+    case 2: return launch_pp_typed<false, true, kM16APP, kM16AMP, 0, 0, 0, true, true>(a, s);
+    case 3: return launch_pp_typed<true, true, kM16APP, kM16AMP, 0, 0, 0, true, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -34,9 +34,10 @@ hipError_t launch_gemm_dynamic(int dtype, const GemmLaunch& a, hipStream_t s);
 
 // The 256 x 256 x 32 fp16 -> fp16 kernel with the LDS swizzles (A: perPhase, maxPhase; B: vec in
 // 16-byte chunks, perPhase, maxPhase) of one compiled variant; gemm_layout_supported lists them.
-bool gemm_layout_supported(int a_pp, int a_mp, int b_vec, int b_pp, int b_mp);
-hipError_t launch_gemm_layout(int a_pp, int a_mp, int b_vec, int b_pp, int b_mp, const GemmLaunch& a,
-                              hipStream_t s);
+// m16: the 16 x 16 x 32 MFMA form (b_vec 0 = its default B layout) instead of the 32 x 32 x 16 one.
+bool gemm_layout_supported(bool m16, int a_pp, int a_mp, int b_vec, int b_pp, int b_mp);
+hipError_t launch_gemm_layout(bool m16, int a_pp, int a_mp, int b_vec, int b_pp, int b_mp,
+                              const GemmLaunch& a, hipStream_t s);
 
 hipError_t launch_tile_map(const TileOrder& o, int32_t* tile_m, int32_t* tile_n, hipStream_t s);
 
