@@ -1,6 +1,6 @@
 // The four-wave GEMM kernel template (64 x 64 and 128 x 128 tiles; launched from gemm.hip) and
 // the helpers it shares with the eight-wave 256 x 256 kernel of gemm_pp_kernel.hpp: direct-to-LDS
-// loads, wait counts, LDS swizzles, the MFMA wrapper and the epilogue (store_tile).
+// loads, wait counts, LDS swizzles, the MFMA wrappers and the epilogues (store_tile16, store_tile).
 //
 // Tiled GEMM C = A * B for gfx950 with a swizzled, optionally persistent tile schedule.
 //
@@ -12,7 +12,8 @@
 //
 // How it is computed on CDNA4:
 //   * 256 threads = 4 wave64s arranged 2 x 2; each wave owns a (BM/2) x (BN/2) sub-tile made of
-//     32 x 32 MFMA blocks (v_mfma_f32_32x32x16_{f16,bf16}) with fp32 accumulators.
+//     16 x 16 MFMA blocks (v_mfma_f32_16x16x32_{f16,bf16}) with fp32 accumulators in VGPRs, as the
+//     eight-wave kernel (the 32 x 32 x 16 MFMA form remains in that kernel's layout variants).
 //   * A workgroup's tiles form one stream of 32-deep k steps (tile after tile). Operands move
 //     global -> LDS with direct-to-LDS 16-byte buffer loads (no registers in between) into five
 //     LDS stages of (BM + BN) x 32 sixteen-bit values, issued four steps ahead of their use, also
@@ -22,17 +23,16 @@
 //     8 consecutive k of one column that the MFMA B operand wants; no register transposes.
 //   * LDS swizzles (the chunk-XOR idea of "CUDA Swizzle & bank conflict", sections "Hopper TMA 的
 //     swizzling" and "Triton - Shared Layout swizzling", applied to 16-byte chunks and sized to
-//     gfx950's 64 x 4-byte banks): A chunk c of row r is stored at chunk c XOR ((r >> 2) mod 4);
-//     B chunk c of row k at chunk c XOR 4 (k mod 4). These are members of the page's
-//     (vec, perPhase, maxPhase) family, which the kernel template takes as parameters (the
-//     defaults are the two layouts just named). The XOR is applied on the global-address side
-//     of the direct loads, whose LDS destinations are fixed (lane l writes bytes 16 l .. 16 l + 15
-//     of its 1 KiB block). Both operand reads then hit 16 (A) or 32 (B) distinct 16-byte bank
-//     groups per service cycle.
-//   * One barrier per step, between its two 16-deep phases; operand reads run one phase ahead of
-//     the MFMAs that consume them.
+//     gfx950's 64 x 4-byte banks), chosen for the 16 x 16 x 32 read patterns: A chunk c of row r at
+//     c XOR ((r >> 1) mod 4); B chunk c of row k at c XOR swz_b_four_wave(k). The XOR is applied on
+//     the global-address side of the direct loads, whose LDS destinations are fixed (lane l writes
+//     bytes 16 l .. 16 l + 15 of its 1 KiB block).
+//   * One barrier per 32-deep step; the step's MFMAs run on fragments read during the previous step,
+//     while the next step's fragments are read and the loads four steps ahead issue in between.
 //   * The MFMA is issued with B as its first operand, so each lane ends up holding 4 consecutive
 //     output columns of one row; the epilogue stores 16 bytes per lane.
+//   * At most 256 registers per wave (two waves per SIMD): the compiler then keeps the
+//     accumulators in VGPRs, updated in place, instead of the AGPRs it would otherwise pick.
 #pragma once
 
 #include <stdint.h>
@@ -115,6 +115,7 @@ __device__ __forceinline__ void wait_vm() {
   else if constexpr (N == 4) TBL_WAIT_VMCNT(4);
   else if constexpr (N == 5) TBL_WAIT_VMCNT(5);
   else if constexpr (N == 6) TBL_WAIT_VMCNT(6);
+  else if constexpr (N == 8) TBL_WAIT_VMCNT(8);
   else if constexpr (N == 10) TBL_WAIT_VMCNT(10);
   else if constexpr (N == 12) TBL_WAIT_VMCNT(12);
   else if constexpr (N == 20) TBL_WAIT_VMCNT(20);
@@ -279,15 +280,26 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[TM][TN], void* __rest
   }
 }
 
-template <int BM, int BN, bool kBf16, bool kF32Out, int kAPP = 4, int kAMP = 4, int kBV = 4,
-          int kBPP = 1, int kBMP = 4>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restrict__ A,
+// B chunk XOR of the four-wave kernel's 16 x 16 x 32 reads for its row width: 256-byte rows (128
+// columns) take swz_b16; 128-byte rows (64 columns) hold two rows per 256-byte bank window, and one
+// half-wave phase of the transposing read touches rows k0 .. k0 + 3 and k0 + 8 .. k0 + 11 (32 bytes
+// of each): the rows of one parity must then sit at 4 distinct 32-byte positions of their half of
+// the window, which 2 ((k / 2) mod 2) + 4 ((k / 8) mod 2) (in 16-byte chunks) gives. Both are
+// conflict-free under the bank model of the oracle (64 banks, 32-lane phases).
+template <int BN>
+__device__ __forceinline__ int swz_b_four_wave(int k) {
+  if constexpr (BN == 64) return 2 * ((k >> 1) & 1) + 4 * ((k >> 3) & 1);
+  else return swz_b16(k);
+}
+
+template <int BM, int BN, bool kBf16, bool kF32Out>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B,
                                                         void* __restrict__ Cv, int M, int N, int K,
                                                         TileOrder order, int num_programs,
                                                         int32_t* __restrict__ trace) {
-  constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile
-  constexpr int TM = WM / 32, TN = WN / 32;        // 32 x 32 MFMA blocks per wave
+  constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile (2 x 2 waves)
+  constexpr int TM = WM / 16, TN = WN / 16;        // 16 x 16 MFMA blocks per wave
   constexpr int kBRow = BN * 2;                    // bytes of one B row (one k) in LDS
   constexpr int kAStage = BM * kARow;
   constexpr int kBStage = kBK * kBRow;
@@ -295,15 +307,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   constexpr int kAInst = kAStage / 1024 / 4;       // 1 KiB direct loads per wave per step
   constexpr int kBInst = kBStage / 1024 / 4;
   constexpr int kLoads = kAInst + kBInst;
-  constexpr int kBChunks = BN / 8;                 // 16-byte chunks per B row
+  constexpr int kAPP = 2, kAMP = 4;                // A swizzle: chunk c of row r at c XOR ((r / 2) mod 4)
   static_assert(kAInst >= 1 && kBInst >= 1, "each wave loads at least one block of A and B");
   static_assert(kStages == 5, "the wait counts assume four steps in flight");
-  // The read addresses of a wave's A blocks (rows + 32 q) and of B's k offsets (+ 16 s + 4 t) are
-  // one base plus constants only when those offsets leave the swizzle phase unchanged.
-  static_assert(kAPP >= 1 && kAMP >= 1 && kAMP <= 4 && (32 / kAPP) % kAMP == 0 && 32 % kAPP == 0,
-                "A swizzle must repeat every 32 rows");
-  static_assert(kBPP >= 1 && kBMP >= 1 && 4 % kBPP == 0 && (4 / kBPP) % kBMP == 0,
-                "B swizzle must repeat every 4 k rows");
+  static_assert(TN % 2 == 0, "the 16-bit epilogue pairs adjacent blocks");
 
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
 
@@ -319,9 +326,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 
   // ---- per-lane constants ----
   // Direct loads. A block (16 rows of 64 bytes): lane l fills physical chunk l mod 4 of row l / 4,
-  // which holds logical chunk (l mod 4) XOR swz_a(row).
-  // In the last k step of a K that is not a multiple of 32, chunks at k >= K belong to the next
-  // row of A; a_voff_tail points those lanes past the buffer range, so they read zero.
+  // which holds logical chunk (l mod 4) XOR swz_a(row). In the last k step of a K that is not a
+  // multiple of 32, chunks at k >= K belong to the next row of A; a_voff_tail points those lanes
+  // past the buffer range, so they read zero.
   constexpr int kOutOfRange = 0x7FFFFFF0;
   int a_voff[kAInst], a_voff_tail[kAInst];
 #pragma unroll
@@ -337,29 +344,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   for (int j = 0; j < kBInst; ++j) {
     const int o = (wave * kBInst + j) * 1024 + 16 * lane;
     const int k = o / kBRow;
-    const int chunk = ((o % kBRow) >> 4) ^ swz_b<kBV, kBPP, kBMP, kBChunks>(k);
+    const int chunk = ((o % kBRow) >> 4) ^ swz_b_four_wave<BN>(k);
     b_voff[j] = (k * N + chunk * 8) * 2;
   }
-  // MFMA operand reads. A: lane reads row (lane mod 32) of a 32-row block, logical chunk
-  // 2s + lane / 32 of phase s.
-  int a_rd[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int row = wm * WM + (lane & 31);
-    const int chunk = (2 * s + (lane >> 5)) ^ swz_a<kAPP, kAMP>(row);
-    a_rd[s] = row * kARow + chunk * 16;
-  }
-  // B: within each 16-lane group, lane r points at row k0 + r/4, columns n0 + 4 (r mod 4) .. +3;
-  // the transposing read then gives lane i column n0 + i at rows k0 .. k0 + 3.
+  // MFMA operand reads (the 16 x 16 x 32 lane layouts, as in the eight-wave kernel): A lane l takes
+  // row l mod 16 of a 16-row block at chunk l / 16; B lane L of 16-lane group G addresses the 8-byte
+  // row piece k = 8 G + (L mod 16) / 4, columns 4 (L mod 4) .. + 3 of a 16-column block, which the
+  // transposing read turns into 4 k of one column per lane (twice: k and k + 4)
+  const int a_row = wm * WM + (lane & 15);
+  const int a_rd = a_row * kARow + ((lane >> 4) ^ swz_a<kAPP, kAMP>(a_row)) * 16;
   int b_rd[TN];
   {
-    const int g = lane >> 4, r = lane & 15;
-    const int k = 8 * (g >> 1) + (r >> 2);
+    const int r = lane & 15;
+    const int k = 8 * (lane >> 4) + (r >> 2);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = wn * WN + j * 32 + 16 * (g & 1) + 4 * (r & 3);
-      const int chunk = (n >> 3) ^ swz_b<kBV, kBPP, kBMP, kBChunks>(k);
-      b_rd[j] = kAStage + k * kBRow + chunk * 16 + (n & 7) * 2;
+      const int n = wn * WN + j * 16 + 4 * (r & 3);
+      b_rd[j] = kAStage + k * kBRow + ((n >> 3) ^ swz_b_four_wave<BN>(k)) * 16 + (n & 7) * 2;
     }
   }
 
@@ -420,31 +421,32 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
     }
   };
 
-  // ---- operand fragments ----
-  // Read item q of phase s from a stage: items 0 .. TM-1 are A blocks (one 16-byte read each),
-  // items TM .. TM + 2 TN - 1 are halves of B blocks (one transposing 8-byte read each).
+  // ---- operand fragments, double-buffered by step parity ----
+  // Read item q of a step from a stage: items 0 .. TM-1 are A blocks (one 16-byte read each),
+  // items TM .. TM + 2 TN - 1 are halves (k and k + 4) of B blocks (one transposing read each).
   constexpr int kReads = TM + 2 * TN;
-  auto read_item = [&](int stage, int s, int q, uint4 (&af)[TM], uint4 (&bf)[TN]) {
+  uint4 af[2][TM], bf[2][TN];
+  auto read_item = [&](int stage, int buf, int q) {
+    const char* base = lds + stage * kStage;
     if (q < TM) {
-      af[q] = *reinterpret_cast<const uint4*>(lds + stage * kStage + a_rd[s] + q * 32 * kARow);
+      af[buf][q] = *reinterpret_cast<const uint4*>(base + a_rd + q * 16 * kARow);
     } else {
       const int j = (q - TM) >> 1, t = (q - TM) & 1;
-      const char* p = lds + stage * kStage + b_rd[j] + s * 16 * kBRow + t * 4 * kBRow;
-      const uint2 h = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+      const uint2 h = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                    (lds_s16x4_t*)(base + b_rd[j] + t * 4 * kBRow)));
       if (t == 0) {
-        bf[j].x = h.x;
-        bf[j].y = h.y;
+        bf[buf][j].x = h.x;
+        bf[buf][j].y = h.y;
       } else {
-        bf[j].z = h.x;
-        bf[j].w = h.y;
+        bf[buf][j].z = h.x;
+        bf[buf][j].w = h.y;
       }
     }
   };
 
   // Accumulators start from a zero the compiler cannot see through: a visible constant zero lets
-  // it peel the first k step (MFMA with a zero addend) and then shuffle accumulators between
-  // register tuples to join the peeled step and the loop.
-  f32x16_t acc[TM][TN];
+  // it peel the first k step (MFMA with a zero addend) and shuffle accumulators between registers.
+  f32x4_t acc[TM][TN];
   auto zero_acc = [&]() {
     float z;
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
@@ -453,37 +455,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = z;
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = z;
   };
 
-  // One 16-deep phase: MFMA q of the phase, then (on some slots) a direct load and two operand
-  // reads for a later phase; the scheduling barrier after each group keeps this interleaving, so
-  // the matrix pipe always has an MFMA queued while loads and reads issue, and the reads finish
-  // well before the phase that consumes them starts.
-  constexpr int kReadSlots = (kReads + 1) / 2;
-  constexpr int kSlots = (TM * TN > kReadSlots ? (TM * TN > kLoads ? TM * TN : kLoads)
-                                               : (kReadSlots > kLoads ? kReadSlots : kLoads));
-  static_assert(kLoads % 2 == 0, "loads split evenly between the two phases");
-  constexpr int kLoadEvery = kSlots / (kLoads / 2);
-  auto phase = [&](const uint4 (&ua)[TM], const uint4 (&ub)[TN], int load0, int rstage, int rs,
-                   uint4 (&ra)[TM], uint4 (&rb)[TN]) {
+  // One 32-deep step: its TM x TN MFMAs (B fragments forward for even i, backward for odd i, so one
+  // operand stays at every change of A), the operand reads of the next step and the loads of the
+  // step four ahead spread over the MFMA slots; the scheduling barrier after each slot keeps the
+  // interleaving, so the matrix pipe has an MFMA queued while loads and reads issue.
+  constexpr int kSlots = TM * TN;
+  static_assert(kSlots >= kLoads, "one load per slot at most");
+  constexpr int kLoadEvery = kSlots / kLoads;
+  constexpr int kReadsPerSlot = (kReads + kSlots - 1) / kSlots;
+  auto step = [&](int buf, int next_stage) {
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
-      if (q < TM * TN) {
-        const int i = q / TN, j = q % TN;
-        acc[i][j] = mfma32x32x16<kBf16>(ub[j], ua[i], acc[i][j]);
-      }
-      // half of the step's direct loads, spread evenly over the phase's MFMA slots so that the
-      // four waves, released together by the barrier, do not queue their loads in one burst
-      if (q % kLoadEvery == 0 && q / kLoadEvery < kLoads / 2) issue_load(load0 + q / kLoadEvery);
-      if (2 * q < kReads) read_item(rstage, rs, 2 * q, ra, rb);
-      if (2 * q + 1 < kReads) read_item(rstage, rs, 2 * q + 1, ra, rb);
+      const int i = q / TN, jj = q % TN;
+      const int j = (i & 1) ? TN - 1 - jj : jj;
+      acc[i][j] = mfma16x16x32<kBf16>(bf[buf][j], af[buf][i], acc[i][j]);
+      if (q % kLoadEvery == 0 && q / kLoadEvery < kLoads) issue_load(q / kLoadEvery);
+#pragma unroll
+      for (int r = 0; r < kReadsPerSlot; ++r)
+        if (q * kReadsPerSlot + r < kReads) read_item(next_stage, buf ^ 1, q * kReadsPerSlot + r);
       __builtin_amdgcn_sched_barrier(0);
     }
-  };
-
-  auto epilogue = [&](int tile_m, int tile_n) {
-    store_tile<BM, BN, WM, WN, TM, TN, kBf16, kF32Out>(acc, Cv, M, N, tile_m, tile_n, wm, wn, lane);
   };
 
   // ---- compute cursor ----
@@ -518,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   };
   record();
 
-  // prologue: kStages - 1 steps in flight; step 0 must have landed everywhere
+  // prologue: steps 0 .. 3 in flight; step 0 landed everywhere, then its fragments read
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i) {
     prepare_step();
@@ -529,45 +523,49 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
   wait_vm<3 * kLoads>();   // step 0 landed; steps 1..3 may still be in flight
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-
-  uint4 af0[TM], bf0[TN], af1[TM], bf1[TN];
 #pragma unroll
-  for (int q = 0; q < kReads; ++q) read_item(0, 0, q, af0, bf0);
-  bool drained = false;   // an epilogue's stores are in flight: the next wait waits for everything
-  int c_stage = 0;
+  for (int q = 0; q < kReads; ++q) read_item(0, 0, q);
 
-  // Step g: phase 0 multiplies with the operands read during the previous phase, reads phase 1's,
-  // and issues the first half of the loads of step g + 4 into the stage of step g - 1 (free since
-  // the previous barrier: its last reads were issued before it). The barrier certifies step g + 1
-  // in every wave's LDS blocks. Phase 1 multiplies, reads step g + 1's first operands and issues
-  // the second half of step g + 4's loads.
-  for (int tile = 0; tile < my_tiles; ++tile) {
-    zero_acc();
-    for (int kt = 0; kt < nk; ++kt) {
-      prepare_step();
-      phase(af0, bf0, 0, c_stage, 1, af1, bf1);
-      // newer than step g + 1's loads: steps g + 2 and g + 3, and half of step g + 4; after an
-      // epilogue its stores come first, so only the half step just issued may remain
-      if (drained) wait_vm<kLoads / 2>();
-      else wait_vm<2 * kLoads + kLoads / 2>();
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      drained = false;
-      const int next_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
-      phase(af1, bf1, kLoads / 2, next_stage, 0, af0, bf0);
-      advance_load_cursor();
-      c_stage = next_stage;
+  // Step s (global count g, fragments in buffer g mod 2): first this wave's loads of step s + 1 are
+  // waited for (two steps of loads, issued later, may stay in flight; an epilogue's stores, issued
+  // later still, only make the wait longer) and a barrier certifies step s + 1 in every wave's LDS
+  // blocks and every wave's reads of step s done; then the MFMAs of step s run with the reads of step
+  // s + 1 and the loads of step s + 4, into the stage of step s - 1, whose reads all finished before
+  // the previous barrier.
+  // The stream's steps run two per iteration, the first on fragment buffer 0 and the second on
+  // buffer 1, so that every buffer index is a compile-time constant (a runtime parity would make the
+  // compiler keep two copies of the accumulators and move them at every join); a tile's epilogue
+  // follows whichever step ends it.
+  int c_stage = 0, kt = 0;
+  auto run_step = [&](int buf) {
+    wait_vm<2 * kLoads>();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    prepare_step();
+    const int next_stage = c_stage == kStages - 1 ? 0 : c_stage + 1;
+    step(buf, next_stage);
+    advance_load_cursor();
+    c_stage = next_stage;
+    if (++kt == nk) {
+      kt = 0;
+      record_time();
+      store_tile16<BM, BN, WM, WN, TM, TN, kBf16, kF32Out>(acc, Cv, M, N, c_m, c_n, wm, wn, lane);
+      c_t += P;
+      ++c_iter;
+      if (c_t < order.tiles) {
+        order_tile(order, c_t, c_m, c_n);
+        record();
+      }
+      zero_acc();
     }
-    record_time();
-    epilogue(c_m, c_n);
-    drained = true;
-    c_t += P;
-    ++c_iter;
-    if (c_t < order.tiles) {
-      order_tile(order, c_t, c_m, c_n);
-      record();
-    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  zero_acc();
+  for (int g = 0; g < total; g += 2) {
+    run_step(0);
+    if (g + 1 < total) run_step(1);
   }
+  wait_vm<0>();   // no direct load may still be writing this workgroup's LDS
 }
 
 template <int BM, int BN>
