@@ -149,3 +149,110 @@ def test_invalid_arguments(kwargs, status):
     with pytest.raises(tbl.TblError) as e:
         tbl.predict_l2(**args)
     assert e.value.status == status
+
+
+# ---- tbl_predict_l2_lines against oracle.l2_lines (exact integer parity) ----
+
+from oracle import l2_lines  # noqa: E402
+
+
+def _line_cases():
+    rng = np.random.default_rng(23)
+    modes = [tm.ROW, tm.COL, tm.PANEL, tm.MORTON, tm.XOR, tm.SERPENTINE]
+    out = []
+    for i in range(30):
+        mode = modes[i % len(modes)] | (tm.XCD_REMAP if i % 4 == 1 else 0)
+        bm, bn, bk = (int(rng.choice([2, 4, 16, 32])), int(rng.choice([2, 8, 16, 32])),
+                      int(rng.choice([1, 4, 8, 32])))
+        if mode & 0xFF in (tm.MORTON, tm.XOR):
+            g = int(2 ** rng.integers(0, 4))
+            M, N = g * bm - int(rng.integers(0, bm)), g * bn - int(rng.integers(0, bn))
+        else:
+            M, N = int(rng.integers(1, 140)), int(rng.integers(1, 140))
+        K = int(rng.integers(1, 90))
+        e = int(rng.choice([1, 2, 4]))
+        gm, gn = -(-M // bm), -(-N // bn)
+        group = int(rng.integers(1, 6))
+        caches = int(rng.choice([1, 2, 8]))
+        programs = int(rng.choice([0, 1, 3, gm * gn + 2]))
+        sets, ways = int(rng.choice([1, 2, 7, 64])), int(rng.choice([1, 2, 4, 16]))
+        line = int(rng.choice([4, 16, 64, 128]))
+        fold = (int(rng.integers(0, 8)), int(rng.choice([0, 0, 1, 3])))
+        a_base = int(rng.integers(0, 5)) * 4096 + int(rng.choice([0, 2, 60]))
+        b_base = a_base + M * K * e + int(rng.integers(0, 300))
+        out.append((mode, M, N, K, e, (bm, bn, bk), group, caches, programs, int(rng.integers(1, 5)),
+                    sets, ways, line, fold, a_base, b_base))
+    return out
+
+
+@pytest.mark.parametrize("case", _line_cases())
+def test_line_replay_equals_oracle(case):
+    (mode, M, N, K, e, block, group, caches, programs, resident, sets, ways, line, fold, a_base,
+     b_base) = case
+    gm, gn = -(-M // block[0]), -(-N // block[1])
+    m, n = tm.tile_table(mode, gm, gn, group)
+    want = l2_lines.predict_lines(m, n, M, N, K, elem_bytes=e, block=block, num_caches=caches,
+                                  num_programs=programs, resident=resident, sets=sets, ways=ways,
+                                  line_bytes=line, fold_from=fold[0], fold_width=fold[1],
+                                  a_base=a_base, b_base=b_base)
+    got = tbl.predict_l2_lines(mode, M, N, K, group, e, block, caches, programs, resident, sets, ways,
+                               line, fold[0], fold[1], a_base, b_base)
+    assert got[:3] == want
+
+
+@pytest.mark.parametrize("name,mode,group,cluster", [
+    ("group_major_g8", tm.PANEL, 8, (1, 1)),
+    ("group_major_g4+remap+cluster2x2", tm.PANEL | tm.XCD_REMAP, 4, (2, 2)),
+])
+def test_line_replay_equals_oracle_at_8192(name, mode, group, cluster):
+    # the 8192^3 persistent launch (256 programs) with the gfx950 geometry and real-looking bases
+    m, n = tm.tile_table(mode, 32, 32, group, cluster=cluster)
+    a_base, b_base = 0x7F1200000000, 0x7F1208200000
+    want = l2_lines.predict_lines(m, n, 8192, 8192, 8192, num_programs=256, a_base=a_base,
+                                  b_base=b_base, **l2_lines.GFX950)
+    cl = tbl.cluster(*cluster) if cluster != (1, 1) else 0
+    got = tbl.predict_l2_lines(mode | cl, 8192, 8192, 8192, group, num_programs=256, a_base=a_base,
+                               b_base=b_base, **{k: v for k, v in tbl.GFX950_L2.items()})
+    assert got[:3] == want
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(mode=7), tbl.ERR_INVALID_ARG), (dict(M=0), tbl.ERR_SHAPE), (dict(K=(1 << 20) + 1), tbl.ERR_SHAPE),
+    (dict(elem_bytes=3), tbl.ERR_INVALID_ARG), (dict(block=(0, 4, 4)), tbl.ERR_INVALID_ARG),
+    (dict(block=(4, 4, 4097)), tbl.ERR_INVALID_ARG), (dict(num_caches=65), tbl.ERR_INVALID_ARG),
+    (dict(resident=0), tbl.ERR_INVALID_ARG), (dict(sets=0), tbl.ERR_INVALID_ARG),
+    (dict(ways=65), tbl.ERR_INVALID_ARG), (dict(sets=1 << 20, ways=32), tbl.ERR_INVALID_ARG),
+    (dict(line_bytes=0), tbl.ERR_INVALID_ARG), (dict(fold_from=64), tbl.ERR_INVALID_ARG),
+    (dict(fold_width=33), tbl.ERR_INVALID_ARG),
+    (dict(a_base=(1 << 64) - 16), tbl.ERR_INVALID_ARG),
+    # work bound: more than 2^33 line reads
+    (dict(M=1 << 20, N=1 << 20, K=1 << 14, block=(256, 256, 32)), tbl.ERR_SHAPE),
+])
+def test_line_replay_invalid_arguments(kwargs, status):
+    args = dict(mode=tm.ROW, M=64, N=64, K=64, group=1, elem_bytes=2, block=(16, 16, 16), num_caches=1,
+                num_programs=0, resident=1, sets=4, ways=2, line_bytes=64, fold_from=0, fold_width=0,
+                a_base=0, b_base=1 << 20)
+    args.update(kwargs)
+    with pytest.raises(tbl.TblError) as e:
+        tbl.predict_l2_lines(**args)
+    assert e.value.status == status
+
+
+def _fixture_rows():
+    rows = []
+    for ln in golden_lines("l2_lines_predictions.txt"):
+        t = ln.split()
+        rows.append((t[0], t[1], *[int(v) for v in t[2:12]]))
+    return rows
+
+
+@pytest.mark.parametrize("row", [r for r in _fixture_rows()
+                                 if (r[0], r[4]) in {("xor", 8192), ("serpentine_s4", 8192),
+                                                     ("col+remap", 8192), ("serpentine_s8", 4096)}])
+def test_library_reproduces_committed_line_predictions(row):
+    # the fixture was written by the oracle (tests/golden/make_l2_lines_predictions.py); bench.py
+    # reports the library's predictions, which must be the same numbers
+    name, kind, M, N, K, mode, group, cm, cn, hits, acc, miss = row
+    cl = tbl.cluster(cm, cn) if (cm, cn) != (1, 1) else 0
+    got = tbl.predict_l2_lines(mode | cl, M, N, K, group, num_programs=256, **tbl.GFX950_L2)
+    assert got[:3] == (hits, acc, miss)

@@ -425,6 +425,43 @@ int tbl_predict_l2(int swizzle_mode, int grid_m, int grid_n, int grid_k, int gro
   return bijective_grid(swizzle_mode, grid_m, grid_n) ? TBL_OK : TBL_WARN_NOT_BIJECTIVE;
 }
 
+int tbl_predict_l2_lines(int swizzle_mode, int64_t M, int64_t N, int64_t K, int elem_bytes,
+                         int block_m, int block_n, int block_k, int group_size, int num_caches,
+                         int num_programs, int resident, int64_t sets, int ways, int64_t line_bytes,
+                         int fold_from, int fold_width, uint64_t a_base, uint64_t b_base,
+                         int64_t* hits, int64_t* accesses, int64_t* misses) {
+  if (hits == nullptr || accesses == nullptr || misses == nullptr) return TBL_ERR_INVALID_ARG;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return TBL_ERR_INVALID_ARG;
+  if (block_m < 1 || block_n < 1 || block_k < 1 || block_m > 4096 || block_n > 4096 || block_k > 4096)
+    return TBL_ERR_INVALID_ARG;
+  if (num_caches < 1 || num_caches > 64 || num_programs < 0 || resident < 1) return TBL_ERR_INVALID_ARG;
+  if (sets < 1 || ways < 1 || ways > 64 || sets * ways > (int64_t{1} << 24)) return TBL_ERR_INVALID_ARG;
+  if (line_bytes < 1 || line_bytes > (1 << 20)) return TBL_ERR_INVALID_ARG;
+  if (fold_from < 0 || fold_from > 63 || fold_width < 0 || fold_width > 32) return TBL_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
+  const int64_t gm = (M + block_m - 1) / block_m, gn = (N + block_n - 1) / block_n;
+  if (gm > kMaxDim || gn > kMaxDim) return TBL_ERR_SHAPE;
+  int rc = check_order(swizzle_mode, static_cast<int>(gm), static_cast<int>(gn), group_size);
+  if (rc != TBL_OK) return rc;
+  // bounded work: at most 2^33 line reads (each tile row and k row reads at least one line)
+  const int64_t nk = (K + block_k - 1) / block_k;
+  const double lines_a = static_cast<double>(block_m) * (1.0 + static_cast<double>(block_k) * elem_bytes / line_bytes);
+  const double lines_b = static_cast<double>(block_k) * (1.0 + static_cast<double>(block_n) * elem_bytes / line_bytes);
+  if (static_cast<double>(gm) * gn * nk * (lines_a + lines_b) > 8589934592.0) return TBL_ERR_SHAPE;
+  // the last byte of either operand must be addressable
+  const double span = static_cast<double>(M) * K * elem_bytes + static_cast<double>(K) * N * elem_bytes;
+  if (static_cast<double>(a_base) + span > 1.8e19 || static_cast<double>(b_base) + span > 1.8e19)
+    return TBL_ERR_INVALID_ARG;
+  const tbl::TileOrder o = make_order(swizzle_mode, static_cast<int>(gm), static_cast<int>(gn), group_size);
+  const tbl::GemmReadShape r{M, N, K, elem_bytes, block_m, block_n, block_k, a_base, b_base};
+  const tbl::L2Geometry g{sets, ways, line_bytes, fold_from, fold_width};
+  tbl::predict_l2_lines(o, r, g, num_caches, num_programs == 0 ? gm * gn : num_programs, resident,
+                        hits, accesses);
+  *misses = *accesses - *hits;
+  return bijective_grid(swizzle_mode, static_cast<int>(gm), static_cast<int>(gn)) ? TBL_OK
+                                                                                : TBL_WARN_NOT_BIJECTIVE;
+}
+
 int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t cols, int layout,
                       void* stream) {
   if (in == nullptr || out == nullptr) return TBL_ERR_INVALID_ARG;

@@ -46,6 +46,25 @@ hipError_t launch_tile_map(const TileOrder& o, int32_t* tile_m, int32_t* tile_n,
 void predict_l2(const TileOrder& o, int grid_k, int64_t a_bytes, int64_t b_bytes, int64_t capacity,
                 int num_caches, int num_programs, int resident, int64_t* hits, int64_t* accesses);
 
+// The GEMM's operand reads as byte ranges: A (M x K) at a_base and B (K x N) at b_base, row-major,
+// elem_bytes per element, bm x bn x bk tiles.
+struct GemmReadShape {
+  int64_t M, N, K;
+  int elem_bytes, bm, bn, bk;
+  uint64_t a_base, b_base;
+};
+// Set-associative caches: sets x ways lines of line_bytes; line L in set
+// (L xor ((L >> fold_from) mod 2^fold_width)) mod sets.
+struct L2Geometry {
+  int64_t sets;
+  int ways;
+  int64_t line_bytes;
+  int fold_from, fold_width;
+};
+// Line-granular replay with predict_l2's grouping and read order (host only; validated arguments).
+void predict_l2_lines(const TileOrder& o, const GemmReadShape& r, const L2Geometry& g, int num_caches,
+                      int64_t num_programs, int resident, int64_t* hits, int64_t* accesses);
+
 // The matrix-pipe rate kernel (mfma_rate.hip); arguments already validated.
 hipError_t launch_mfma_rate(const void* A, const void* B, int64_t elems, bool bf16, int workgroups,
                             int iters, float* out, int64_t* cycles, hipStream_t s);

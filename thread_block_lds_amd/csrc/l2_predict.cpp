@@ -15,6 +15,7 @@
 // executes (order_tile).
 #include <stdint.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "internal.hpp"
@@ -121,6 +122,101 @@ void predict_l2(const TileOrder& o, int grid_k, int64_t a_bytes, int64_t b_bytes
     }
     *hits += cache.hits;
     *accesses += cache.hits + cache.misses;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Line-granular replay: the same grouping and read order as predict_l2, counted per cache line
+// through set-associative caches indexed by address (the GEMM's loads as the L2 sees them).
+//
+// Each XCD's cache is a flat array of `sets` x `ways` tags (line number + 1; 0 = empty) beside an
+// array of last-use stamps from a per-cache counter; a hit restamps its way, a miss fills the
+// empty way or the way with the oldest stamp. Within a set that is least-recently-used order.
+
+namespace {
+
+class SetCache {
+ public:
+  SetCache(const L2Geometry& g)
+      : g_(g), tag_(static_cast<size_t>(g.sets * g.ways), 0), stamp_(tag_.size(), 0) {}
+
+  void read_range(uint64_t first, int64_t count) {
+    if (count <= 0) return;
+    const uint64_t l0 = first / g_.line_bytes, l1 = (first + count - 1) / g_.line_bytes;
+    for (uint64_t l = l0; l <= l1; ++l) read_line(l);
+  }
+
+  int64_t hits = 0, accesses = 0;
+
+ private:
+  void read_line(uint64_t line) {
+    const uint64_t fold =
+        g_.fold_width > 0 ? (line >> g_.fold_from) & ((uint64_t{1} << g_.fold_width) - 1) : 0;
+    const size_t base = static_cast<size_t>((line ^ fold) % static_cast<uint64_t>(g_.sets)) * g_.ways;
+    const uint64_t want = line + 1;
+    ++accesses;
+    ++now_;
+    size_t victim = base;
+    for (size_t w = base; w < base + g_.ways; ++w) {
+      if (tag_[w] == want) {
+        ++hits;
+        stamp_[w] = now_;
+        return;
+      }
+      if (stamp_[w] < stamp_[victim]) victim = w;  // empty ways carry stamp 0 and win
+    }
+    tag_[victim] = want;
+    stamp_[victim] = now_;
+  }
+
+  L2Geometry g_;
+  std::vector<uint64_t> tag_, stamp_;
+  uint64_t now_ = 0;
+};
+
+}  // namespace
+
+void predict_l2_lines(const TileOrder& o, const GemmReadShape& r, const L2Geometry& g, int num_caches,
+                      int64_t num_programs, int resident, int64_t* hits, int64_t* accesses) {
+  const int64_t T = o.tiles, P = num_programs;
+  const int64_t nk = (r.K + r.bk - 1) / r.bk;
+  const uint64_t e = static_cast<uint64_t>(r.elem_bytes);
+  struct Tile {
+    int64_t row0, row1, col0, col1;
+  };
+  std::vector<Tile> group;
+  *hits = 0;
+  *accesses = 0;
+  for (int c = 0; c < num_caches; ++c) {
+    SetCache cache(g);
+    const int64_t count = P > c ? (P - c + num_caches - 1) / num_caches : 0;
+    for (int64_t g0 = 0; g0 < count; g0 += resident) {
+      const int64_t g1 = g0 + resident < count ? g0 + resident : count;
+      for (int64_t it = 0;; ++it) {
+        group.clear();
+        for (int64_t j = g0; j < g1; ++j) {
+          const int64_t t = c + j * num_caches + it * P;
+          if (t >= T) continue;
+          int m = 0, n = 0;
+          order_tile(o, static_cast<int>(t), m, n);
+          const int64_t row0 = static_cast<int64_t>(m) * r.bm, col0 = static_cast<int64_t>(n) * r.bn;
+          group.push_back({row0, std::min(r.M, row0 + r.bm), col0, std::min(r.N, col0 + r.bn)});
+        }
+        if (group.empty()) break;
+        for (int64_t kb = 0; kb < nk; ++kb) {
+          const int64_t k0 = kb * r.bk, k1 = std::min(r.K, k0 + r.bk);
+          for (const Tile& tl : group) {
+            for (int64_t row = tl.row0; row < tl.row1; ++row)
+              cache.read_range(r.a_base + (static_cast<uint64_t>(row) * r.K + k0) * e, (k1 - k0) * r.elem_bytes);
+            for (int64_t k = k0; k < k1; ++k)
+              cache.read_range(r.b_base + (static_cast<uint64_t>(k) * r.N + tl.col0) * e,
+                               (tl.col1 - tl.col0) * r.elem_bytes);
+          }
+        }
+      }
+    }
+    *hits += cache.hits;
+    *accesses += cache.accesses;
   }
 }
 
