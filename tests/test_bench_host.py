@@ -88,3 +88,24 @@ def test_rank_corr_matches_the_oracles_and_the_page():
     pred = [float(r[3]) for r in rows]
     assert round(bench.rank_corr(pred, [float(r[4]) for r in rows]), 3) == 0.045
     assert round(bench.rank_corr(pred, [float(r[5]) for r in rows]), 3) == 0.064
+
+
+def test_l2_check_cases_are_the_committed_predictions():
+    cases = bench._l2_check_cases()
+    assert len(cases) == 23
+    assert sum(1 for c in cases if c["kind"] == "fit") == 7
+    # the fitted rows are the 8192^3 target's seven static orders, in the same order
+    assert [c["name"] for c in cases if c["kind"] == "fit"] == [n for n, _, _ in bench.C3_MODES]
+    shapes = bench._l2_check_shapes()
+    assert shapes == [(8192, 8192, 8192), (8192, 8192, 16384), (8192, 8192, 4096)]
+    # every case runs on a grid the persistent kernel tiles exactly
+    for c in cases:
+        assert c["M"] % 256 == 0 and c["N"] % 256 == 0 and c["K"] % 32 == 0
+
+
+def test_ranks_desc_and_line_fit():
+    assert bench._ranks_desc([87.5, 65.6, 87.5, 32.3]) == [1, 3, 1, 4]
+    fit = bench._line_model_fit({"a": {"hit_pct": 80.0, "fetch_mb": 100.0}, "b": {"hit_pct": 30.0, "fetch_mb": 400.0}},
+                                {"a": {"l2_hit_pct": 82.0, "fetch_mb": 110.0}, "b": {"l2_hit_pct": 33.0, "fetch_mb": 380.0}})
+    assert fit["spearman_vs_measured_hit"] == 1.0 and fit["max_abs_hit_err_pp"] == 3.0
+    assert fit["max_rel_fetch_err"] == round(10 / 110, 4)
