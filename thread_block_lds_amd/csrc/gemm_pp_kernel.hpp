@@ -49,13 +49,16 @@ __device__ __forceinline__ unsigned dyn_atomic_add(unsigned* p, unsigned v) {   
   asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(p), "v"(v) : "memory");
   return r;
 }
-__device__ __forceinline__ uint64_t dyn_load_wg(const uint64_t* p) {   // workgroup scope
-  uint64_t r;
-  asm volatile("global_load_dwordx2 %0, %1, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
 __device__ __forceinline__ void dyn_store_wg(uint64_t* p, uint64_t v) {   // workgroup scope
   asm volatile("global_store_dwordx2 %0, %1, off sc0" : : "v"(p), "v"(v) : "memory");
+}
+// A uniform 64-bit read through the scalar path with glc (the scalar cache is bypassed, the value
+// comes from L2). Scalar loads count on lgkmcnt, not vmcnt, so waiting for this one leaves the
+// wave's direct loads in flight. Reads only: the scalar path is never used to write.
+__device__ __forceinline__ uint64_t dyn_load_scalar(const uint64_t* p) {
+  uint64_t r;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+  return r;
 }
 __device__ __forceinline__ unsigned dyn_load_device(const unsigned* p) {   // device scope
   unsigned r;
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   };
   auto mailbox_take = [&](int k) -> int {   // other waves: read the slot, check its claim number
     for (int tries = 0; tries < 1024; ++tries) {
-      const uint64_t v = dyn_load_wg(mailbox + (k & 1));
+      const uint64_t v = dyn_load_scalar(mailbox + (k & 1));
       if (static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(v >> 32))) ==
           static_cast<unsigned>(k)) {
         const int pos = static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(v)));
@@ -260,7 +263,10 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   }
 
   // ---- load cursor (as gemm_kernel) ----
-  int ld_t = first, ld_kt = 0, ld_issued = 0, ld_stage = 0;
+  // the claimed positions are uniform over the workgroup (each is read through readfirstlane), but
+  // the compiler cannot see it through the claim code's lane-0 branches: said here, so the load
+  // cursor and its addresses stay scalar (in vector registers they cost every step ~25 VALU ops)
+  int ld_t = __builtin_amdgcn_readfirstlane(first), ld_kt = 0, ld_issued = 0, ld_stage = 0;
   uint64_t ld_a = 0, ld_b = 0;
   const unsigned a_step = kBK * 2;
   const uint64_t b_step = static_cast<uint64_t>(kBK) * static_cast<unsigned>(N) * 2;
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     if (++ld_kt == nk) {
       ld_kt = 0;
       if constexpr (kDyn) {
-        ld_t = nxt;
+        ld_t = __builtin_amdgcn_readfirstlane(nxt);
         if (ld_t >= 0) enter_tile();
       } else {
         ld_t += P;
@@ -481,11 +487,10 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   // dynamic: at the start of tile j's k step 0, wave 0 claims tile j + 1 and posts it in the
   // mailbox; the other waves read it at the start of step 4 (the post, issued before step 0's loads,
   // has landed by wave 0's wait at the end of step 2); the load cursor moves to tile j + 1 at the
-  // end of step nk - 5's loads, so nk >= 9. A claim or a read waits for its result at once, and
-  // with it for the wave's loads in flight: about one load latency per tile and wave. The hook is
-  // reached only from steps 0 .. 4, so every other step pays one compare: in the ping-pong schedule
-  // a memory half-period that grows beyond the other group's MFMAs lengthens the step. The claim
-  // number in each slot catches a stale read.
+  // end of step nk - 5's loads, so nk >= 9. The claim waits for its result at once, and with it for
+  // wave 0's loads in flight (about one load latency per tile); the other waves read the mailbox
+  // through the scalar path, whose wait leaves their loads in flight. The claim number in each
+  // slot catches a stale read.
   auto dyn_hook = [&](int kt) {
     const int k = c_iter + 1;
     if (wave == 0) {
@@ -499,10 +504,19 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
   };
   for (int tile = 0; kDyn || tile < my_tiles; ++tile) {
     zero_acc();
-    for (int kt = 0; kt < nk; ++kt) {
-      if constexpr (kDyn) {
-        if (kt <= 4) dyn_hook(kt);
+    int kt = 0;
+    if constexpr (kDyn) {
+      // steps 0 .. 4 carry the claim hook in a loop of their own, so the steady-state loop below
+      // is the static kernel's, with no per-step test
+      for (; kt < 5; ++kt) {
+        dyn_hook(kt);
+        memory_half();
+        compute_half();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    for (; kt < nk; ++kt) {
       memory_half();
       compute_half();
       lds_barrier();
@@ -515,7 +529,7 @@ __global__ __launch_bounds__(kPPThreads) void gemm_pp_kernel(const uint16_t* __r
     else
       store_tile<BM, BN, WM, WN, TM, TN, kBf16, kF32Out>(acc, Cv, M, N, c_m, c_n, grp, wn, lane);
     if constexpr (kDyn) {
-      c_t = nxt;
+      c_t = __builtin_amdgcn_readfirstlane(nxt);
       ++c_iter;
       if (c_t < 0) break;
       order_tile(order, c_t, c_m, c_n);
