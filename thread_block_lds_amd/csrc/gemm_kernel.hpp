@@ -444,18 +444,18 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __res
     }
   };
 
-  // Accumulators start from a zero the compiler cannot see through: a visible constant zero lets
-  // it peel the first k step (MFMA with a zero addend) and shuffle accumulators between registers.
-  f32x4_t acc[TM][TN];
+  // Accumulators are zeroed in place, each register through a tied asm operand: the compiler can
+  // neither see the zero (a visible constant lets it peel the first k step, an MFMA with a zero
+  // addend) nor give the zeroed value a register of its own (the tile-end merge inside the k loop
+  // then needs no copies of the accumulators).
+  f32x4_t acc[TM][TN] = {};
   auto zero_acc = [&]() {
-    float z;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = z;
+        for (int r = 0; r < 4; ++r) asm volatile("v_mov_b32 %0, 0" : "+v"(acc[i][j][r]));
   };
 
   // One 32-deep step: its TM x TN MFMAs (B fragments forward for even i, backward for odd i, so one
