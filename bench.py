@@ -721,6 +721,10 @@ def page_sweep(reps=10):
             h, acc, _ = tbl.predict_l2(mode, gm, gn, gk, g, block, block, l2, num_caches=xcds,
                                        num_programs=programs, resident=max(1, capacity // xcds))
             out[name][key]["pred_xcd_model_pct"] = round(100.0 * h / acc, 2)
+            lh, la, _, _ = tbl.predict_l2_lines(mode, PS, PS, PS, g, 2, PS_TILE, num_programs=programs,
+                                                resident=max(1, capacity // xcds), a_base=ad.data_ptr(),
+                                                b_base=bd.data_ptr(), **tbl.GFX950_L2)
+            out[name][key]["pred_line_model_pct"] = round(100.0 * lh / la, 2)
         out[name]["page_rtx5080"] = printed.get(name)
     names = [n for n, _, _ in PS_ORDERS]
     spear = {}
@@ -728,14 +732,19 @@ def page_sweep(reps=10):
         tf = [out[n][key]["tflops"] for n in names]
         spear[f"page_model_vs_tflops_{key}"] = round(rank_corr([out[n]["pred_page_model_pct"] for n in names], tf), 3)
         spear[f"xcd_model_vs_tflops_{key}"] = round(rank_corr([out[n][key]["pred_xcd_model_pct"] for n in names], tf), 3)
+        spear[f"line_model_vs_tflops_{key}"] = round(rank_corr([out[n][key]["pred_line_model_pct"] for n in names], tf), 3)
         if hits is not None:
             spear[f"xcd_model_vs_measured_hit_{key}"] = round(rank_corr(
                 [out[n][key]["pred_xcd_model_pct"] for n in names], [out[n][key]["l2_hit_pct"] for n in names]), 3)
+            spear[f"line_model_vs_measured_hit_{key}"] = round(rank_corr(
+                [out[n][key]["pred_line_model_pct"] for n in names], [out[n][key]["l2_hit_pct"] for n in names]), 3)
     print(json.dumps({"sweep": "swizzle page benchmark: 8192^3 fp16 N(0,1) -> fp16, 128x128x32 tiles, "
                                "cold launches (512 MiB eviction read before each)",
                       "measured_capacity": capacity, "page_model": {"caches": 1, "capacity_bytes": xcds * l2,
                                                                      "wave": capacity},
                       "xcd_model": {"caches": xcds, "capacity_bytes": l2, "resident_per_cache": max(1, capacity // xcds)},
+                      "line_model": {"caches": xcds, **{k: v for k, v in tbl.GFX950_L2.items() if k != "num_caches"},
+                                     "resident_per_cache": max(1, capacity // xcds)},
                       "orders": out, "spearman": spear, "counters_note": note}), flush=True)
 
 
