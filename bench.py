@@ -656,32 +656,30 @@ def page_sweep_pass():
     print("page sweep pass done", flush=True)
 
 
-def page_sweep(reps=10):
-    """The swizzle page's benchmark sweep on this GPU: 8192^3 fp16 N(0,1), 128x128x32 tiles, 11
-    orders, non-persistent and persistent, cold launches; measured TCC hit rates; the page's
-    one-cache model and the per-XCD model; Spearman coefficients as the page computes them."""
-    hits = None
-    note = None
-    if shutil.which("rocprofv3") is not None:
-        tmp = tempfile.mkdtemp(prefix="tbl_sweep_", dir="/tmp")
-        try:
-            rows = _run_pmc(["TCC_HIT_sum", "TCC_MISS_sum"], "ps", tmp, "--page-sweep-pass")
-            gemm = [r for r in rows if _is_gemm(r["kernel"])][1:]
-            if len(gemm) != 2 * len(PS_ORDERS):
-                raise RuntimeError(f"expected {2 * len(PS_ORDERS)} GEMM dispatches, got {len(gemm)}")
-            hits = [100.0 * r["TCC_HIT_sum"] / max(r["TCC_HIT_sum"] + r["TCC_MISS_sum"], 1.0) for r in gemm]
-        except Exception as e:
-            note = f"{type(e).__name__}: {e}"
-        finally:
-            shutil.rmtree(tmp, ignore_errors=True)
-    else:
-        note = "rocprofv3 not found"
+def page_sweep_hits():
+    """The page sweep's measured TCC hit rates (one rocprofv3 --pmc child run), in PS_ORDERS order,
+    non-persistent then persistent; (None, reason) when they cannot be collected."""
+    if shutil.which("rocprofv3") is None:
+        return None, "rocprofv3 not found"
+    tmp = tempfile.mkdtemp(prefix="tbl_sweep_", dir="/tmp")
+    try:
+        rows = _run_pmc(["TCC_HIT_sum", "TCC_MISS_sum"], "ps", tmp, "--page-sweep-pass")
+        gemm = [r for r in rows if _is_gemm(r["kernel"])][1:]
+        if len(gemm) != 2 * len(PS_ORDERS):
+            raise RuntimeError(f"expected {2 * len(PS_ORDERS)} GEMM dispatches, got {len(gemm)}")
+        return [100.0 * r["TCC_HIT_sum"] / max(r["TCC_HIT_sum"] + r["TCC_MISS_sum"], 1.0) for r in gemm], None
+    except Exception as e:
+        return None, f"{type(e).__name__}: {e}"
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
 
-    import torch
-    import thread_block_lds_amd as tbl
+
+def page_sweep_measure(tbl, torch, stream, hits=None, note=None, line_model=True, reps=10):
+    """The swizzle page's benchmark sweep on this GPU: 8192^3 fp16 N(0,1), 128x128x32 tiles, 11
+    orders, non-persistent and persistent, cold launches; measured TCC hit rates (``hits``, from
+    page_sweep_hits); the page's one-cache model, the per-XCD block model and (``line_model``) the
+    line model; Spearman coefficients as the page computes them."""
     from thread_block_lds_amd import synth
-    torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
     a, b = synth.gemm_operands(PS, PS, PS, "f16", "randn", seed=0)
     ad, bd = _dev16(a, torch, torch.float16), _dev16(b, torch, torch.float16)
     del a, b
@@ -721,31 +719,44 @@ def page_sweep(reps=10):
             h, acc, _ = tbl.predict_l2(mode, gm, gn, gk, g, block, block, l2, num_caches=xcds,
                                        num_programs=programs, resident=max(1, capacity // xcds))
             out[name][key]["pred_xcd_model_pct"] = round(100.0 * h / acc, 2)
-            lh, la, _, _ = tbl.predict_l2_lines(mode, PS, PS, PS, g, 2, PS_TILE, num_programs=programs,
-                                                resident=max(1, capacity // xcds), a_base=ad.data_ptr(),
-                                                b_base=bd.data_ptr(), **tbl.GFX950_L2)
-            out[name][key]["pred_line_model_pct"] = round(100.0 * lh / la, 2)
+            if line_model:
+                lh, la, _, _ = tbl.predict_l2_lines(mode, PS, PS, PS, g, 2, PS_TILE, num_programs=programs,
+                                                    resident=max(1, capacity // xcds), a_base=ad.data_ptr(),
+                                                    b_base=bd.data_ptr(), **tbl.GFX950_L2)
+                out[name][key]["pred_line_model_pct"] = round(100.0 * lh / la, 2)
         out[name]["page_rtx5080"] = printed.get(name)
+    del ad, bd, c, flush, trace
     names = [n for n, _, _ in PS_ORDERS]
     spear = {}
+    models = ["xcd_model"] + (["line_model"] if line_model else [])
     for key in ("nonpersistent", "persistent"):
         tf = [out[n][key]["tflops"] for n in names]
         spear[f"page_model_vs_tflops_{key}"] = round(rank_corr([out[n]["pred_page_model_pct"] for n in names], tf), 3)
-        spear[f"xcd_model_vs_tflops_{key}"] = round(rank_corr([out[n][key]["pred_xcd_model_pct"] for n in names], tf), 3)
-        spear[f"line_model_vs_tflops_{key}"] = round(rank_corr([out[n][key]["pred_line_model_pct"] for n in names], tf), 3)
-        if hits is not None:
-            spear[f"xcd_model_vs_measured_hit_{key}"] = round(rank_corr(
-                [out[n][key]["pred_xcd_model_pct"] for n in names], [out[n][key]["l2_hit_pct"] for n in names]), 3)
-            spear[f"line_model_vs_measured_hit_{key}"] = round(rank_corr(
-                [out[n][key]["pred_line_model_pct"] for n in names], [out[n][key]["l2_hit_pct"] for n in names]), 3)
-    print(json.dumps({"sweep": "swizzle page benchmark: 8192^3 fp16 N(0,1) -> fp16, 128x128x32 tiles, "
-                               "cold launches (512 MiB eviction read before each)",
-                      "measured_capacity": capacity, "page_model": {"caches": 1, "capacity_bytes": xcds * l2,
-                                                                     "wave": capacity},
-                      "xcd_model": {"caches": xcds, "capacity_bytes": l2, "resident_per_cache": max(1, capacity // xcds)},
-                      "line_model": {"caches": xcds, **{k: v for k, v in tbl.GFX950_L2.items() if k != "num_caches"},
-                                     "resident_per_cache": max(1, capacity // xcds)},
-                      "orders": out, "spearman": spear, "counters_note": note}), flush=True)
+        for mdl in models:
+            spear[f"{mdl}_vs_tflops_{key}"] = round(rank_corr([out[n][key][f"pred_{mdl}_pct"] for n in names], tf), 3)
+            if hits is not None:
+                spear[f"{mdl}_vs_measured_hit_{key}"] = round(rank_corr(
+                    [out[n][key][f"pred_{mdl}_pct"] for n in names], [out[n][key]["l2_hit_pct"] for n in names]), 3)
+    res = {"sweep": "swizzle page benchmark: 8192^3 fp16 N(0,1) -> fp16, 128x128x32 tiles, "
+                    "cold launches (512 MiB eviction read before each)",
+           "measured_capacity": capacity, "page_model": {"caches": 1, "capacity_bytes": xcds * l2,
+                                                          "wave": capacity},
+           "xcd_model": {"caches": xcds, "capacity_bytes": l2, "resident_per_cache": max(1, capacity // xcds)},
+           "orders": out, "spearman": spear, "counters_note": note}
+    if line_model:
+        res["line_model"] = {"caches": xcds, **{k: v for k, v in tbl.GFX950_L2.items() if k != "num_caches"},
+                             "resident_per_cache": max(1, capacity // xcds)}
+    return res
+
+
+def page_sweep(reps=10):
+    """bench.py --page-sweep: the page's sweep with all three models, as one JSON line."""
+    hits, note = page_sweep_hits()
+    import torch
+    import thread_block_lds_amd as tbl
+    torch.cuda.set_device(0)
+    print(json.dumps(page_sweep_measure(tbl, torch, torch.cuda.current_stream(), hits, note, True, reps)),
+          flush=True)
 
 
 def _l2_check_cases():
@@ -1039,6 +1050,7 @@ def main():
 
     # counters first, in child processes, before this process touches the GPU
     ctr, ctr_err = (None, "skipped (--no-counters)") if args.no_counters else counters()
+    ps_hits, ps_note = (None, "skipped (--no-counters)") if args.no_counters else page_sweep_hits()
 
     import torch
     import thread_block_lds_amd as tbl
@@ -1100,6 +1112,8 @@ def main():
     ceiling = mfma_ceiling(tbl, torch, stream, ad, bd)
     transpose = time_transpose(tbl, torch, stream)
     target = target_check(tbl, torch, stream, ctr.get("target_counters") if ctr else None)
+    # the page's own 8192^3 128x128x32 sweep (the line model's replays are left to --page-sweep)
+    page = page_sweep_measure(tbl, torch, stream, ps_hits, ps_note, line_model=False)
 
     ms_step = wall * 1e3 / args.steps
     per_mode = {}
@@ -1194,6 +1208,7 @@ def main():
                                            "with no memory traffic, at the clock the board holds for this data"},
         "transpose": transpose,
         "target_8192": target,
+        "page_sweep": page,
         "counters_note": ctr_err,
     }
     if not args.no_cpu:
