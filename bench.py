@@ -476,14 +476,18 @@ def mfma_ceiling(tbl, torch, stream, ad, bd, gemm_tflops=None, reps=5):
     return out
 
 
-def _trace_split(tbl, torch, ad, bd, c, mode, g, nk):
-    """One traced persistent launch: core-clock cycles per 32-deep k step (the MFMAs of one step
-    take 1024 cycles at the chip's peak issue rate) and the core clock, from the per-tile cycle and
-    100 MHz tick counts of the kernel's schedule trace."""
+def _trace_split(tbl, torch, ad, bd, c, mode, g, nk, workspace=None):
+    """One traced persistent launch (static schedule, or the dynamic one on ``workspace``):
+    core-clock cycles per 32-deep k step (the MFMAs of one step take 1024 cycles at the chip's peak
+    issue rate) and the core clock, from the per-tile cycle and 100 MHz tick counts of the kernel's
+    schedule trace."""
     M, N = ad.shape[0], bd.shape[1]
     T = (M // 256) * (N // 256)
     tr = torch.zeros(8 * T, dtype=torch.int32, device="cuda")
-    tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=True, trace=tr)
+    if workspace is None:
+        tbl.gemm(ad, bd, c, mode=mode, group=g, persistent=True, trace=tr)
+    else:
+        tbl.gemm_dynamic(ad, bd, c, mode=mode, group=g, workspace=workspace, trace=tr)
     torch.cuda.synchronize()
     r = tr.view(T, 8).cpu().double()
     cyc, ticks = float(r[:, 5].sum()), float(r[:, 6].sum())
@@ -570,6 +574,7 @@ def target_check(tbl, torch, stream, measured=None, reps=10):
         tf = flops / (ms * 1e-3) / 1e12
         res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2),
                      "schedule": "dynamic"}
+        res[name].update(_trace_split(tbl, torch, ad, bd, c, mode, g, C3 // 32, workspace=ws))
     # the north star's "gain over linear ordering" at this workload: measured L2 hit-rate points and
     # throughput of each static order against row-major (no remap)
     for name, _, _ in C3_MODES:
