@@ -66,3 +66,13 @@ def gemm_entries(a_bits, b_bits, dtype, rows, cols):
     a = decode(np.asarray(a_bits)[rows], dtype)            # (Q, K)
     b = decode(np.asarray(b_bits)[:, cols], dtype)         # (K, Q)
     return np.einsum("qk,kq->q", a, b)
+
+
+def abs_products_rows(a_bits, b_bits, dtype, rows):
+    """Rows ``rows`` of |A| @ |B| in fp64: for each output element the sum over k of
+    |A[i][k] B[k][j]|. It bounds the rounding error of every summation order of that element's
+    products: a sum of K terms, each addition rounded to a unit roundoff u, errs by at most about
+    K u times it, whatever the order."""
+    a = np.abs(decode(np.asarray(a_bits)[np.asarray(rows)], dtype))
+    b = np.abs(decode(b_bits, dtype))
+    return a @ b

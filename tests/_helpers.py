@@ -26,6 +26,31 @@ def bits16(t):
     return t.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+# unit roundoff of the output types (half an ulp relative to the value) and half their smallest
+# subnormal step
+_U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8, "f32": 2.0 ** -24}
+_TINY_OUT = {"f16": 2.0 ** -25, "bf16": 2.0 ** -134, "f32": 2.0 ** -150}
+
+
+def check_bound(gpu, ref, absprod, K, out, what=""):
+    """A bound derived from the arithmetic instead of a fixed tolerance. Products of fp16 or bf16
+    values are exact in fp32; an fp32 sum of K of them, in any order and whether each addition
+    rounds to nearest or toward zero, errs by at most 2 K 2^-24 sum|a b| (absprod, from
+    oracle.gemm.abs_products_rows); rounding to the output type then adds at most its unit roundoff
+    times the value, or half its smallest subnormal step:
+        |gpu - ref| <= (1 + u) 2 K 2^-24 absprod + u |ref| + tiny."""
+    u, tiny = _U_OUT[out], _TINY_OUT[out]
+    bound = (1 + u) * 2.0 * K * 2.0 ** -24 * absprod + u * np.abs(ref) + tiny
+    err = np.abs(gpu - ref)
+    ok = err <= bound
+    if not np.all(ok):
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} elements beyond the derived bound; first at {i}: "
+                             f"gpu {gpu[i]!r} ref {ref[i]!r} bound {bound[i]!r}")
+    return float(np.max(err / bound))
+
+
 def check_tol(gpu, ref, K, f32_out=False, what=""):
     err = np.abs(gpu - ref)
     if f32_out:

@@ -22,7 +22,7 @@ import pytest
 import torch
 
 import thread_block_lds_amd as tbl
-from _helpers import bits16, check_tol, dev16, host64
+from _helpers import bits16, check_bound, check_tol, dev16, host64
 from oracle import gemm as og
 from oracle import tile_maps as tm
 from thread_block_lds_amd import synth
@@ -153,6 +153,7 @@ def test_c2_4096_fp16_orders():
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     rows = _sample_rows(M, 256)
     ref = og.gemm_rows(a, b, "f16", rows)
+    absprod = og.abs_products_rows(a, b, "f16", rows)
     base = None
     for mode, g in [(tm.ROW, 1), (tm.PANEL, 4), (tm.PANEL, 8), (tm.PANEL, 16), (tm.MORTON, 1), (tm.XOR, 1)]:
         for remap in (0, tm.XCD_REMAP):
@@ -161,11 +162,13 @@ def test_c2_4096_fp16_orders():
             if base is None:
                 base = c
                 check_tol(host64(c)[rows], ref, K, what="4096^3 row")
+                check_bound(host64(c)[rows], ref, absprod, K, "f16", what="4096^3 row")
             else:
                 assert torch.equal(c, base), (mode, g, remap)
     c32 = tbl.gemm(ad, bd, out_dtype=torch.float32, mode=tm.PANEL, group=8)
     torch.cuda.synchronize()
     check_tol(host64(c32)[rows], ref, K, f32_out=True, what="4096^3 fp32 out")
+    check_bound(host64(c32)[rows], ref, absprod, K, "f32", what="4096^3 fp32 out")
 
 
 def test_c3_8192_bf16_persistent():
@@ -174,6 +177,7 @@ def test_c3_8192_bf16_persistent():
     ad, bd = dev16(a, "bf16"), dev16(b, "bf16")
     rows = _sample_rows(M, 256)
     ref = og.gemm_rows(a, b, "bf16", rows)
+    absprod = og.abs_products_rows(a, b, "bf16", rows)
     base = None
     for mode in (tm.PANEL, tm.SERPENTINE, tm.PANEL | tm.XCD_REMAP, tm.SERPENTINE | tm.XCD_REMAP):
         c = tbl.gemm(ad, bd, mode=mode, group=8, persistent=True)
@@ -181,6 +185,9 @@ def test_c3_8192_bf16_persistent():
         if base is None:
             base = c
             check_tol(host64(c)[rows], ref, K, what="8192^3 bf16")
+            # the outputs' spread is about 0.011, so the fixed bar above is one sigma wide; this
+            # one is about 6e-4 here
+            check_bound(host64(c)[rows], ref, absprod, K, "bf16", what="8192^3 bf16")
         else:
             assert torch.equal(c, base), mode
 

@@ -113,3 +113,21 @@ def test_synth_bf16_rounding_is_nearest_even():
     x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -9)], dtype=np.float32)
     bits = synth.f32_to_bf16_bits(x)
     assert list(og.decode_bf16(bits)) == [1.0, 1.0 + 2.0 ** -6, -1.0]
+
+
+def test_abs_products_by_hand_and_properties():
+    # A = [[1, -2]], B = [[3], [4]] (fp16): products 3 and -8; their absolute sum is 11, the product -5
+    a = np.array([[1.0, -2.0]], dtype=np.float16).view(np.uint16)
+    b = np.array([[3.0], [4.0]], dtype=np.float16).view(np.uint16)
+    assert og.abs_products_rows(a, b, "f16", [0])[0, 0] == 11.0
+    assert og.gemm_rows(a, b, "f16", [0])[0, 0] == -5.0
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((40, 70)).astype(np.float16)
+    y = rng.standard_normal((70, 30)).astype(np.float16)
+    rows = [0, 7, 39]
+    # nonnegative operands: the same as the product
+    xa, ya = np.abs(x).view(np.uint16), np.abs(y).view(np.uint16)
+    assert np.array_equal(og.abs_products_rows(xa, ya, "f16", rows), og.gemm_rows(xa, ya, "f16", rows))
+    # the triangle inequality: never below the product's magnitude
+    xs, ys = x.view(np.uint16), y.view(np.uint16)
+    assert np.all(og.abs_products_rows(xs, ys, "f16", rows) >= np.abs(og.gemm_rows(xs, ys, "f16", rows)))
