@@ -65,3 +65,14 @@ def check_tol(gpu, ref, K, f32_out=False, what=""):
         raise AssertionError(f"{what}: {len(bad)} elements out of tolerance; first at {i}: "
                              f"gpu {gpu[i]!r} ref {ref[i]!r}")
     return float(np.max(err))
+
+
+def check_gemm(gpu, a, b, dtype, K, out, rows=None, what=""):
+    """Both bars against the oracle for a GEMM result: the generic tolerance and the derived bound.
+    gpu: the result (all rows, or the sampled ``rows``) as fp64; a, b: the input bit patterns;
+    out: the output type ("f16", "bf16" or "f32")."""
+    from oracle import gemm as og
+    rows = np.arange(np.asarray(a).shape[0]) if rows is None else np.asarray(rows)
+    ref = og.gemm_rows(a, b, dtype, rows)
+    check_tol(gpu, ref, K, f32_out=out == "f32", what=what)
+    return check_bound(gpu, ref, og.abs_products_rows(a, b, dtype, rows), K, out, what=what)

@@ -20,8 +20,7 @@ import pytest
 import torch
 
 import thread_block_lds_amd as tbl
-from _helpers import check_tol, dev16, host64
-from oracle import gemm as og
+from _helpers import check_gemm, dev16, host64
 from oracle import schedule as sc
 from oracle import tile_maps as tm
 from thread_block_lds_amd import synth
@@ -54,8 +53,7 @@ def _check_trace(tr, mode, g, gm, gn):
 @pytest.fixture(scope="module")
 def square2048():
     M = N = K = 2048
-    a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
-    return a, b, og.gemm(a, b, "f16")
+    return synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
 
 
 @pytest.mark.parametrize("mode,g", [(tm.ROW, 1), (tm.PANEL, 4), (tm.SERPENTINE, 2), (tm.MORTON, 1),
@@ -63,10 +61,10 @@ def square2048():
                                     (tm.SERPENTINE | tm.XCD_REMAP, 2), (tm.XOR | tm.XCD_REMAP, 1)])
 @pytest.mark.parametrize("P", [16, 64, 0])
 def test_2048_orders_match_oracle_and_static(square2048, mode, g, P):
-    a, b, ref = square2048
+    a, b = square2048
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     c, tr = _run(ad, bd, mode, g, P)
-    check_tol(host64(c), ref, 2048, what=f"dynamic mode {mode:#x} g{g} P{P}")
+    check_gemm(host64(c), a, b, "f16", 2048, "f16", what=f"dynamic mode {mode:#x} g{g} P{P}")
     static = tbl.gemm(ad, bd, mode=mode & ~tm.XCD_REMAP, group=g, tile=(256, 256, 32))
     torch.cuda.synchronize()
     assert torch.equal(c, static)
@@ -75,7 +73,7 @@ def test_2048_orders_match_oracle_and_static(square2048, mode, g, P):
 
 
 def test_workspace_chains_launches(square2048):
-    a, b, ref = square2048
+    a, b = square2048
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     ws = tbl.dynamic_workspace(32)
     ws[:9] = 12345                 # whatever the counters hold, each launch starts from zero
@@ -87,7 +85,7 @@ def test_workspace_chains_launches(square2048):
     assert int(ws[9].item()) == 0
     for c in outs[1:]:
         assert torch.equal(c, outs[0])
-    check_tol(host64(outs[0]), ref, 2048, what="chained launches")
+    check_gemm(host64(outs[0]), a, b, "f16", 2048, "f16", what="chained launches")
 
 
 @pytest.mark.parametrize("K", [264, 288])
@@ -96,10 +94,9 @@ def test_one_workgroup_runs_every_tile_min_k(K):
     K = 288) are the fewest the dynamic schedule takes."""
     M, N = 2048, 2048
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=5)
-    ref = og.gemm(a, b, "f16")
     for mode in (tm.PANEL, tm.PANEL | tm.XCD_REMAP):
         c, tr = _run(dev16(a, "f16"), dev16(b, "f16"), mode, 4, 1)
-        check_tol(host64(c), ref, K, what=f"P=1 mode {mode:#x}")
+        check_gemm(host64(c), a, b, "f16", K, "f16", what=f"P=1 mode {mode:#x}")
         seqs = _check_trace(tr, mode, 4, 8, 8)
         assert len(seqs) == 1
         p = next(iter(seqs))
@@ -115,10 +112,9 @@ def test_one_workgroup_runs_every_tile_min_k(K):
 def test_more_workgroups_than_tiles():
     M, N, K = 1024, 768, 512      # 4 x 3 = 12 tiles, 64 workgroups
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=6)
-    ref = og.gemm(a, b, "f16")
     for mode in (tm.ROW, tm.ROW | tm.XCD_REMAP):
         c, tr = _run(dev16(a, "f16"), dev16(b, "f16"), mode, 1, 64)
-        check_tol(host64(c), ref, K, what=f"P > T mode {mode:#x}")
+        check_gemm(host64(c), a, b, "f16", K, "f16", what=f"P > T mode {mode:#x}")
         _check_trace(tr, mode, 1, 4, 3)
 
 
@@ -131,11 +127,10 @@ def test_more_workgroups_than_resident(mode):
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     static = tbl.gemm(ad, bd, mode=mode & ~tm.XCD_REMAP, group=4, tile=(256, 256, 32))
     rows = np.arange(3, M, 97)
-    ref = og.gemm_rows(a, b, "f16", rows)
     for P in (1024, 777):
         c, tr = _run(ad, bd, mode, 4, P)
         assert torch.equal(c, static), P
-        check_tol(host64(c)[rows], ref, K, what=f"P={P} mode {mode:#x}")
+        check_gemm(host64(c)[rows], a, b, "f16", K, "f16", rows, what=f"P={P} mode {mode:#x}")
         seqs = _check_trace(tr, mode, 4, 16, 16)
         assert max(seqs) < 256 and all(len(v) == 1 for v in seqs.values())
 
@@ -144,10 +139,9 @@ def test_more_workgroups_than_resident(mode):
 def test_ragged_fp32_out(dtype):
     M, N, K = 1000, 776, 1000     # partial tiles at M and N edges, a k tail of 8
     a, b = synth.gemm_operands(M, N, K, dtype, "uniform" if dtype == "f16" else "normal", seed=7)
-    ref = og.gemm(a, b, dtype)
     ad, bd = dev16(a, dtype), dev16(b, dtype)
     c, tr = _run(ad, bd, tm.SERPENTINE | tm.XCD_REMAP, 2, 3, out_dtype=torch.float32)
-    check_tol(host64(c), ref, K, f32_out=True, what=f"ragged {dtype} fp32 out")
+    check_gemm(host64(c), a, b, dtype, K, "f32", what=f"ragged {dtype} fp32 out")
     _check_trace(tr, tm.SERPENTINE | tm.XCD_REMAP, 2, 4, 4)
     static = tbl.gemm(ad, bd, mode=tm.SERPENTINE, group=2, out_dtype=torch.float32, tile=(256, 256, 32))
     torch.cuda.synchronize()
@@ -168,7 +162,7 @@ def test_queues_without_local_workgroups_are_stolen():
     for x in empty:                # every tile of an unserved block ran on another XCD
         assert np.all(run_on[blocks[x][0]:blocks[x][1]] != x)
     rows = np.arange(0, M, 61)
-    check_tol(host64(c)[rows], og.gemm_rows(a, b, "f16", rows), K, what="stolen blocks")
+    check_gemm(host64(c)[rows], a, b, "f16", K, "f16", rows, what="stolen blocks")
 
 
 def test_c3_8192_bf16_xcd_aware_equals_static_remap():
@@ -178,12 +172,12 @@ def test_c3_8192_bf16_xcd_aware_equals_static_remap():
     a, b = synth.gemm_operands(M, N, K, "bf16", "normal", seed=0)
     ad, bd = dev16(a, "bf16"), dev16(b, "bf16")
     rows = np.array(sorted({r * 256 + (r * 37) % 256 for r in range(32)}))
-    ref = og.gemm_rows(a, b, "bf16", rows)
     static = tbl.gemm(ad, bd, mode=tm.SERPENTINE | tm.XCD_REMAP, group=8, persistent=True)
     for mode in (tm.SERPENTINE | tm.XCD_REMAP, tm.PANEL | tm.XCD_REMAP, tm.PANEL):
         c, tr = _run(ad, bd, mode, 8, 0)
         assert torch.equal(c, static), mode
-        check_tol(host64(c[torch.from_numpy(rows).cuda()]), ref, K, what=f"8192^3 dynamic {mode:#x}")
+        check_gemm(host64(c[torch.from_numpy(rows).cuda()]), a, b, "bf16", K, "bf16", rows,
+                   what=f"8192^3 dynamic {mode:#x}")
         _check_trace(tr, mode, 8, 32, 32)
         del c
 
@@ -196,13 +190,13 @@ def test_c4_rectangular_partial_groups():
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     rows = np.array(sorted({r * 256 + (r * 53) % 256 for r in range(40)}))
-    ref = og.gemm_rows(a, b, "f16", rows)
     static = tbl.gemm(ad, bd, mode=tm.PANEL, group=16, persistent=True)
     for mode, g in ((tm.PANEL, 16), (tm.PANEL | tm.XCD_REMAP, 16), (tm.SERPENTINE, 16),
                     (tm.SERPENTINE | tm.XCD_REMAP, 16)):
         c, tr = _run(ad, bd, mode, g, 0)
         assert torch.equal(c, static), mode
-        check_tol(host64(c[torch.from_numpy(rows).cuda()]), ref, K, what=f"C4 dynamic {mode:#x} g{g}")
+        check_gemm(host64(c[torch.from_numpy(rows).cuda()]), a, b, "f16", K, "f16", rows,
+                   what=f"C4 dynamic {mode:#x} g{g}")
         _check_trace(tr, mode, g, 40, 24)
 
 

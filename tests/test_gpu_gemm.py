@@ -22,7 +22,7 @@ import pytest
 import torch
 
 import thread_block_lds_amd as tbl
-from _helpers import bits16, check_bound, check_tol, dev16, host64
+from _helpers import bits16, check_bound, check_gemm, check_tol, dev16, host64
 from oracle import gemm as og
 from oracle import tile_maps as tm
 from thread_block_lds_amd import synth
@@ -43,6 +43,7 @@ def test_c1_every_order_full_oracle():
     M = N = K = 512
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
     ref = og.gemm(a, b, "f16")
+    absprod = og.abs_products_rows(a, b, "f16", np.arange(M))
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     outs = []
     for mode, g in [(tm.ROW, 1), (tm.COL, 1), (tm.PANEL, 4), (tm.MORTON, 1), (tm.XOR, 1),
@@ -50,6 +51,7 @@ def test_c1_every_order_full_oracle():
         c = tbl.gemm(ad, bd, mode=mode, group=g)
         torch.cuda.synchronize()
         check_tol(host64(c), ref, K, what=f"512^3 mode {mode} g{g}")
+        check_bound(host64(c), ref, absprod, K, "f16", what=f"512^3 mode {mode} g{g}")
         outs.append(c)
     for c in outs[1:]:
         assert torch.equal(c, outs[0])
@@ -99,8 +101,8 @@ def test_tile_shapes_bit_identical(dtype, dist, out_dtype):
         outs[tile] = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=out_dtype)
     torch.cuda.synchronize()
     rows = _sample_rows(M, 64)
-    check_tol(host64(outs[256])[rows], og.gemm_rows(a, b, dtype, rows), K, f32_out=out_dtype is not None,
-              what=f"{dtype} tile 256")
+    check_gemm(host64(outs[256])[rows], a, b, dtype, K, "f32" if out_dtype is not None else dtype, rows,
+               what=f"{dtype} tile 256")
     assert torch.equal(outs[64], outs[256]) and torch.equal(outs[128], outs[256])
 
 
@@ -114,7 +116,7 @@ def test_schedule_variants_bit_identical(tile):
     base = tbl.gemm(ad, bd, tile=(tile, tile, 32))
     torch.cuda.synchronize()
     rows = _sample_rows(M, tile)
-    check_tol(host64(base)[rows], og.gemm_rows(a, b, "f16", rows), K, what=f"tile {tile}")
+    check_gemm(host64(base)[rows], a, b, "f16", K, "f16", rows, what=f"tile {tile}")
     for mode, g in [(tm.COL, 1), (tm.PANEL, 3), (tm.MORTON, 1), (tm.XOR, 1), (tm.SERPENTINE, 3)]:
         for remap in (0, tm.XCD_REMAP):
             for persistent, P in [(0, 0), (1, 0), (0, 1), (0, 7), (1, 13), (0, T + 5)]:
@@ -133,7 +135,7 @@ def test_cluster_orders_bit_identical(tile):
     base = tbl.gemm(ad, bd, tile=(tile, tile, 32))
     torch.cuda.synchronize()
     rows = _sample_rows(M, tile)
-    check_tol(host64(base)[rows], og.gemm_rows(a, b, "f16", rows), K, what=f"tile {tile}")
+    check_gemm(host64(base)[rows], a, b, "f16", K, "f16", rows, what=f"tile {tile}")
     for mode, g, (cm, cn) in [(tm.ROW, 1, (2, 1)), (tm.PANEL, 2, (2, 2)), (tm.SERPENTINE, 2, (1, 2)),
                               (tm.MORTON, 1, (2, 1)), (tm.COL, 1, (4, 4))]:
         for remap in (0, tm.XCD_REMAP):
@@ -221,7 +223,6 @@ def test_c4_rectangular_partial_groups():
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     rows = _sample_rows(M, 256)
-    ref = og.gemm_rows(a, b, "f16", rows)
     base = None
     for mode, g in [(tm.PANEL, 8), (tm.PANEL, 16), (tm.SERPENTINE, 8), (tm.SERPENTINE, 16)]:
         for persistent in (False, True):
@@ -229,7 +230,7 @@ def test_c4_rectangular_partial_groups():
             torch.cuda.synchronize()
             if base is None:
                 base = c
-                check_tol(host64(c)[rows], ref, K, what="10240x6144x2048")
+                check_gemm(host64(c)[rows], a, b, "f16", K, "f16", rows, what="10240x6144x2048")
             else:
                 assert torch.equal(c, base), (mode, g, persistent)
     with pytest.raises(tbl.TblError) as e:
@@ -281,15 +282,14 @@ RAGGED = [  # (M, N, K, tile): partial tiles at every edge, K tails of 8 .. 24, 
 @pytest.mark.parametrize("M,N,K,tile", RAGGED)
 def test_ragged_edges_full_oracle(M, N, K, tile):
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=M + N + K)
-    ref = og.gemm(a, b, "f16")
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     c = tbl.gemm(ad, bd, tile=(tile, tile, 32), mode=tm.PANEL, group=2)
     torch.cuda.synchronize()
-    check_tol(host64(c), ref, K, what=f"ragged {M}x{N}x{K} tile {tile}")
+    check_gemm(host64(c), a, b, "f16", K, "f16", what=f"ragged {M}x{N}x{K} tile {tile}")
     c32 = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=torch.float32, mode=tm.SERPENTINE,
                    group=3, persistent=True)
     torch.cuda.synchronize()
-    check_tol(host64(c32), ref, K, f32_out=True, what=f"ragged fp32 {M}x{N}x{K} tile {tile}")
+    check_gemm(host64(c32), a, b, "f16", K, "f32", what=f"ragged fp32 {M}x{N}x{K} tile {tile}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -340,14 +340,13 @@ ODD = [(257, 263, 259), (1, 1, 1), (1000, 1001, 1003), (3, 5, 7), (64, 63, 65), 
 @pytest.mark.parametrize("M,N,K", ODD)
 def test_odd_n_k_full_oracle(M, N, K, dtype, tile):
     a, b = synth.gemm_operands(M, N, K, dtype, "uniform" if dtype == "f16" else "normal", seed=M + 2 * N + 3 * K)
-    ref = og.gemm(a, b, dtype)
     ad, bd = dev16(a, dtype), dev16(b, dtype)
     c = tbl.gemm(ad, bd, tile=(tile, tile, 32), mode=tm.PANEL, group=2)
     c32 = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=torch.float32, mode=tm.SERPENTINE, group=3,
                    persistent=True)
     torch.cuda.synchronize()
-    check_tol(host64(c), ref, K, what=f"odd {M}x{N}x{K} {dtype} tile {tile}")
-    check_tol(host64(c32), ref, K, f32_out=True, what=f"odd fp32 {M}x{N}x{K} {dtype} tile {tile}")
+    check_gemm(host64(c), a, b, dtype, K, dtype, what=f"odd {M}x{N}x{K} {dtype} tile {tile}")
+    check_gemm(host64(c32), a, b, dtype, K, "f32", what=f"odd fp32 {M}x{N}x{K} {dtype} tile {tile}")
 
 
 @pytest.mark.parametrize("tile", [64, 128, 256])
@@ -436,11 +435,10 @@ def test_short_k_streams_across_tiles(K, tile):
     # the same bits and the oracle's product
     M, N = 3 * tile - 5, 3 * tile
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=K + tile)
-    ref = og.gemm(a, b, "f16")
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     base = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    check_tol(host64(base), ref, K, f32_out=True, what=f"K {K} tile {tile}")
+    check_gemm(host64(base), a, b, "f16", K, "f32", what=f"K {K} tile {tile}")
     for persistent, P in [(0, 1), (0, 2), (1, 4), (0, 9)]:
         c = tbl.gemm(ad, bd, tile=(tile, tile, 32), out_dtype=torch.float32, mode=tm.SERPENTINE,
                      group=2, persistent=bool(persistent), num_programs=P)

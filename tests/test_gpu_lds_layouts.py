@@ -14,8 +14,7 @@ import pytest
 import torch
 
 import thread_block_lds_amd as tbl
-from _helpers import check_tol, dev16, host64
-from oracle import gemm as og
+from _helpers import check_gemm, dev16, host64
 from oracle import tile_maps as tm
 from thread_block_lds_amd import synth
 
@@ -36,7 +35,7 @@ def test_layout_matches_oracle_on_ragged_shape(layout):
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     c = tbl.gemm_lds_layout(ad, bd, layout, mode=tm.PANEL, group=2)
     torch.cuda.synchronize()
-    check_tol(host64(c), og.gemm(a, b, "f16"), K, what=str(layout))
+    check_gemm(host64(c), a, b, "f16", K, "f16", what=str(layout))
     ref = tbl.gemm(ad, bd, mode=tm.PANEL, group=2, tile=TILE)
     torch.cuda.synchronize()
     assert torch.equal(c, ref), layout
@@ -56,7 +55,7 @@ def test_layouts_bit_identical_to_default(M, N, K, mode, group):
         assert torch.equal(c, ref), layout
     # and the result is the product: sampled rows against the oracle
     rows = np.arange(0, M, max(1, M // 7))
-    check_tol(host64(ref[torch.from_numpy(rows).cuda()]), og.gemm_rows(a, b, "f16", rows), K)
+    check_gemm(host64(ref[torch.from_numpy(rows).cuda()]), a, b, "f16", K, "f16", rows)
 
 
 # ---- the 16x16x32 form (tbl_gemm_lds_layout16) ----
@@ -73,7 +72,7 @@ def test_layout16_matches_oracle_on_ragged_shape(layout):
     ad, bd = dev16(a, "f16"), dev16(b, "f16")
     c = tbl.gemm_lds_layout(ad, bd, layout, mode=tm.SERPENTINE, group=2, mfma16=True)
     torch.cuda.synchronize()
-    check_tol(host64(c), og.gemm(a, b, "f16"), K, what=str(layout))
+    check_gemm(host64(c), a, b, "f16", K, "f16", what=str(layout))
     ref = tbl.gemm(ad, bd, mode=tm.SERPENTINE, group=2, tile=TILE)
     torch.cuda.synchronize()
     assert torch.equal(c, ref), layout

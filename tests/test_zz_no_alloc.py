@@ -14,8 +14,7 @@ import pytest
 import torch
 
 import thread_block_lds_amd as tbl
-from _helpers import check_tol, dev16, host64
-from oracle import gemm as og
+from _helpers import check_gemm, dev16, host64
 from oracle import schedule as sc
 from thread_block_lds_amd import synth
 
@@ -47,8 +46,8 @@ def test_noalloc_matches_dynamic_on_two_calls():
         torch.cuda.synchronize()
         print(f"noalloc {M}x{N}x{K} {dt} mode {mode:#x} P {Pr}", flush=True)
         assert torch.equal(_bits(out), _bits(ref)), "differs from tbl_gemm_dynamic"
-        check_tol(host64(out), og.gemm(a, b, dt), K, f32_out=out_dtype == torch.float32,
-                  what=f"noalloc {M}x{N}x{K}")
+        check_gemm(host64(out), a, b, dt, K, "f32" if out_dtype == torch.float32 else dt,
+                   what=f"noalloc {M}x{N}x{K}")
         r = tr.cpu().numpy().reshape(T, 8).astype(np.int64)
         sc.check_dynamic_trace(r[:, 0], r[:, 1], r[:, 4], T, bool(mode & tbl.XCD_REMAP))
         assert int(ws[9].item()) == 0
