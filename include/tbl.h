@@ -125,8 +125,9 @@ enum {
  * tbl_gemm -- C = A * B with a swizzled, optionally persistent tile schedule.
  *   A, B, C       device pointers (row-major M x K, K x N, M x N), 16-byte aligned, C not aliasing.
  *   M, N, K       sizes, > 0, each <= 2^20 (TBL_ERR_SHAPE otherwise); any values. The tile shape is
- *                 fixed by a rule (tbl_gemm_tile_shape): 64x64x32 when max(M, N) <= 1024, else
- *                 256x256x32 (k advances through LDS 32 deep). The tile grid is ceil(M/BM) x
+ *                 fixed by a rule (tbl_gemm_tile_shape): 256x256x32 when that grid has at least 128
+ *                 tiles (half of gfx950's 256 CUs), else 128x128x32 when its grid does, else 64x64x32
+ *                 (k advances through LDS 32 deep). The tile grid is ceil(M/BM) x
  *                 ceil(N/BN); loads and stores are masked at every edge, as the page's kernel masks
  *                 them. When N and K are multiples of 8 (rows of A and B are whole 16-byte chunks)
  *                 the fast kernels run, moving operands with 16-byte direct-to-LDS loads; otherwise

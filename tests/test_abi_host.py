@@ -154,10 +154,18 @@ def test_transpose_validation():
 
 
 def test_tile_shape_rule_and_default_programs():
-    assert tbl.gemm_tile_shape(512, 512, 512) == (64, 64, 32)
-    assert tbl.gemm_tile_shape(1024, 1024, 8192) == (64, 64, 32)
+    # the largest square tile whose grid has at least 128 tiles, else 64
+    assert tbl.gemm_tile_shape(512, 512, 512) == (64, 64, 32)         # 4 / 16 tiles
+    assert tbl.gemm_tile_shape(1024, 1024, 8192) == (64, 64, 32)      # 16 / 64 tiles
+    assert tbl.gemm_tile_shape(1536, 1536, 1536) == (128, 128, 32)    # 36 / 144
+    assert tbl.gemm_tile_shape(2048, 2048, 8192) == (128, 128, 32)    # 64 / 256
+    assert tbl.gemm_tile_shape(2560, 2560, 64) == (128, 128, 32)      # 100 / 400
+    assert tbl.gemm_tile_shape(2816, 2816, 64) == (128, 128, 32)      # 121 / 484
+    assert tbl.gemm_tile_shape(3072, 3072, 3072) == (256, 256, 32)    # 144
     assert tbl.gemm_tile_shape(4096, 4096, 4096) == (256, 256, 32)
     assert tbl.gemm_tile_shape(10240, 6144, 2048) == (256, 256, 32)
+    assert tbl.gemm_tile_shape(256 * 127, 256, 8) == (128, 128, 32)   # 127 tiles of 256: one short
+    assert tbl.gemm_tile_shape(256 * 128, 256, 8) == (256, 256, 32)   # exactly 128
     # non-persistent default needs no device: one workgroup per tile
     assert tbl.default_num_programs(512, 512, 512, persistent=False) == 64
     assert tbl.default_num_programs(8192, 8192, 8192, persistent=False) == 1024

@@ -397,7 +397,8 @@ def test_odd_n_k_tile_shapes_bit_identical():
 def test_odd_n_k_trace_matches_oracle_schedule():
     M, N, K = 2000, 1999, 37
     a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=9)
-    gm, gn = -(-M // 256), -(-N // 256)
+    bm, bn, _ = tbl.gemm_tile_shape(M, N, K)    # the default tile (128 x 128 here: 256 tiles)
+    gm, gn = -(-M // bm), -(-N // bn)
     T = gm * gn
     trace = torch.full((8 * T,), -1, dtype=torch.int32, device="cuda")
     tbl.gemm(dev16(a, "f16"), dev16(b, "f16"), mode=tm.SERPENTINE | tm.XCD_REMAP, group=2, persistent=True,

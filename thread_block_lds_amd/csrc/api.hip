@@ -91,8 +91,15 @@ tbl::TileOrder make_order(int swizzle_mode, int gm, int gn, int group) {
   return tbl::make_tile_order(mode, (swizzle_mode & TBL_XCD_REMAP) ? 1 : 0, cgm, cgn, g, cm, cn);
 }
 
+// The largest square tile whose grid has at least kFillTiles tiles, else 64: a grid of fewer tiles
+// than half of gfx950's 256 CUs leaves most of the chip idle, and below that the smaller tile's
+// extra parallelism outweighs its lower per-CU rate (measured over square and rectangular shapes
+// from 768 to 16384: the 256 tile wins from 128 tiles up, the 128 tile from 128 of its own).
+constexpr int64_t kFillTiles = 128;
+
 void tile_rule(int64_t M, int64_t N, int* bm, int* bn, int* bk) {
-  const int t = (M > 1024 || N > 1024) ? 256 : 64;
+  auto tiles = [&](int64_t t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
+  const int t = tiles(256) >= kFillTiles ? 256 : tiles(128) >= kFillTiles ? 128 : 64;
   *bm = t;
   *bn = t;
   *bk = 32;
