@@ -246,9 +246,7 @@ def _fixture_rows():
     return rows
 
 
-@pytest.mark.parametrize("row", [r for r in _fixture_rows()
-                                 if (r[0], r[4]) in {("xor", 8192), ("serpentine_s4", 8192),
-                                                     ("col+remap", 8192), ("serpentine_s8", 4096)}])
+@pytest.mark.parametrize("row", _fixture_rows(), ids=lambda r: f"{r[0]}-K{r[4]}")
 def test_library_reproduces_committed_line_predictions(row):
     # the fixture was written by the oracle (tests/golden/make_l2_lines_predictions.py); bench.py
     # reports the library's predictions, which must be the same numbers
