@@ -141,13 +141,14 @@ enum {
  *   persistent    0: one workgroup per tile (num_programs defaults to T). 1: num_programs defaults
  *                 to min(T, CUs x resident workgroups per CU).
  *   num_programs  0 = the default above; > 0 = exactly this many workgroups. Workgroup p computes
- *                 tiles p, p + num_programs, p + 2 num_programs, ... < T (page 1's static stride
- *                 schedule); < 0 is TBL_ERR_INVALID_ARG.
+ *                 tiles p, p + num_programs, p + 2 num_programs, ... < T (the static stride
+ *                 schedule of the swizzle page's persistent loop); < 0 is TBL_ERR_INVALID_ARG.
  *   stream        hipStream_t or NULL.
  * Every output element is computed by exactly one workgroup with fp32 accumulation over k in
- * ascending MFMA steps (16-deep 32x32x16, or 32-deep 16x16x32 in the 256x256 kernel and the
- * element-wise path, which on gfx950 leave the same bits), so the result does not depend on the
- * order, the remap flag, persistence, num_programs or the tile shape.
+ * ascending 32-deep 16x16x32 MFMA steps (every tile shape and the element-wise path; the 32x32x16
+ * form of tbl_gemm_lds_layout takes two 16-deep steps instead, which on gfx950 leave the same
+ * bits), so the result does not depend on the order, the remap flag, persistence, num_programs or
+ * the tile shape.
  */
 int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
              int swizzle_mode, int group_size, int persistent, int num_programs, void* stream);

@@ -21,11 +21,13 @@ Modules:
   gemm        fp16/bf16 decoding and the fp64 GEMM definition
   transpose   int32 transpose definition
   lds         LDS layout maps (naive / padded / XOR / chunk-XOR) and the bank-conflict model
-  l2_model    byte-granular LRU L2 model and Spearman rank check (page 1's offline predictor)
+  l2_model    byte-granular LRU L2 model and Spearman rank check (the offline predictor of "CUDA
+              Thread Block Swizzle")
   l2_lines    the same replay counted per cache line through set-associative per-XCD caches (a
               reading for gfx950), in plain C (l2_lines.c) compiled with gcc on first use
-  schedule    the static stride schedule and the dynamic (work-queue) schedule page 1 names as
-              missing: event simulation and the checks every GPU trace of it must pass
+  schedule    the static stride schedule and the dynamic (work-queue) schedule that "CUDA Thread
+              Block Swizzle" names as missing: event simulation and the checks every GPU trace of
+              it must pass
 """
 
 from . import tile_maps, gemm, transpose, lds, l2_model, l2_lines, schedule  # noqa: F401

@@ -1,4 +1,5 @@
-"""Oracle: the offline L2 hit-rate model of page 1 and its rank check, plus an XCD-aware variant.
+"""Oracle: the offline L2 hit-rate model of "CUDA Thread Block Swizzle" and its rank check, plus
+an XCD-aware variant.
 
 TEST INFRASTRUCTURE (see the package docstring): not imported by the library.
 

@@ -41,7 +41,7 @@ def panel(t, gm, gn, g):
 
     The grid is cut into groups of g tile rows (the last group keeps whatever rows remain). Groups
     are taken in row order; inside a group ids run down a column of the group, then move to the
-    next column. The row inside the group is the id modulo the group's actual height, as page 1's
+    next column. The row inside the group is the id modulo the group's actual height, as [P1]'s
     function computes it (not the id's offset inside the group modulo that height; the two differ
     only in a partial last group whose first id is not a multiple of its height).
     """
@@ -57,7 +57,7 @@ def morton(t, gm, gn):
     """[P1] Morton / Z-order swizzle.
 
     Bit 2i of the id becomes bit i of m and bit 2i+1 becomes bit i of n, for 16 bit pairs; the
-    results are then reduced modulo the grid (page 1 notes this is a bijection only on power-of-two
+    results are then reduced modulo the grid ([P1] notes this is a bijection only on power-of-two
     grids).
     """
     m = 0 * t
@@ -135,7 +135,7 @@ def cluster_expand(m_idx, n_idx, rank, cm, cn):
 def clustered(mode, t, gm, gn, group, cm, cn):
     """[P3] two-level schedule.  READING (gfx950 has no thread-block clusters).
 
-    Tile id t plays the CTA index of page 3's Example 2: its cluster id t div (cm*cn) is the
+    Tile id t plays the CTA index of [P3]'s Example 2: its cluster id t div (cm*cn) is the
     scheduler's work index, which ``order`` maps to a scheduler tile (m_idx, n_idx) of the
     (gm/cm) x (gn/cn) cluster-tile grid, and its rank t mod (cm*cn) picks the tile inside that
     cluster tile (``cluster_expand``). cm and cn must divide gm and gn.
