@@ -21,6 +21,8 @@
  *     "Case Study / Matrix Transpose").
  *   - tbl_mfma_rate: a measurement aid, the GEMM's inner MFMA stream on its own operand data with no
  *     memory traffic, which gives the matrix-pipe rate the chip sustains for that data.
+ *   - tbl_copy16: a measurement aid, a plain device copy that gives the HBM rate of the transpose's
+ *     read-once, write-once traffic.
  *   - tbl_predict_l2: the offline LRU prediction of an order's L2 hit rate ("CUDA Thread Block
  *     Swizzle", section "CUDA Thread Block Swizzle Benchmark"), generalised to several private
  *     caches; host code only. tbl_predict_l2_lines: the same replay per cache line through
@@ -369,6 +371,18 @@ int tbl_predict_l2_lines(int swizzle_mode, int64_t M, int64_t N, int64_t K, int 
  */
 int tbl_mfma_rate(const void* A, const void* B, int64_t elems, int dtype, int workgroups, int iters,
                   float* out, int64_t* cycles, void* stream);
+
+/*
+ * tbl_copy16 -- dst = src, ``bytes`` bytes, 16 per lane (a measurement aid for the transpose's
+ * roofline, not part of the method): the rate one read stream and one write stream of the same bytes
+ * reach on this device, the traffic of tbl_transpose_i32 ("CUDA Swizzle & bank conflict", section
+ * "Case Study / Matrix Transpose", reads and writes every element once).
+ *   src, dst      device pointers, 16-byte aligned (TBL_ERR_ALIGN), ranges not overlapping
+ *                 (TBL_ERR_INVALID_ARG).
+ *   bytes         > 0 (TBL_ERR_INVALID_ARG), a multiple of 16 and at most 2^40 (TBL_ERR_SHAPE).
+ *   nontemporal   0: ordinary loads and stores; 1: non-temporal ones (streaming hints to the caches).
+ */
+int tbl_copy16(const void* src, void* dst, int64_t bytes, int nontemporal, void* stream);
 
 /* tbl_gemm_tile_shape -- the tile shape tbl_gemm uses for these sizes (host only, no HIP call). */
 int tbl_gemm_tile_shape(int64_t M, int64_t N, int64_t K, int* block_m, int* block_n, int* block_k);

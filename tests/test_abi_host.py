@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(tbl.exported_names()) == declared
-    assert tbl.version() == 105
+    assert tbl.version() == 106
 
 
 def test_status_strings():
@@ -221,3 +221,22 @@ def _layout16(layout=(2, 4, 0, 0, 0), dtype=0, M=512, N=512, K=512, A=FAKE):
 ])
 def test_gemm_lds_layout16_rejects(kw, want):
     assert _layout16(**kw) == want
+
+
+def _copy(src=FAKE, dst=ctypes.c_void_p(0x20000), nbytes=4096, nt=0):
+    return tbl.lib().tbl_copy16(src, dst, nbytes, nt, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(src=NULL), tbl.ERR_INVALID_ARG), (dict(dst=NULL), tbl.ERR_INVALID_ARG),
+    (dict(nbytes=0), tbl.ERR_INVALID_ARG), (dict(nbytes=-16), tbl.ERR_INVALID_ARG),
+    (dict(nt=2), tbl.ERR_INVALID_ARG), (dict(nt=-1), tbl.ERR_INVALID_ARG),
+    (dict(nbytes=4100), tbl.ERR_SHAPE), (dict(nbytes=(1 << 40) + 16), tbl.ERR_SHAPE),
+    (dict(src=MISALIGNED), tbl.ERR_ALIGN), (dict(dst=ctypes.c_void_p(0x20008)), tbl.ERR_ALIGN),
+    # overlapping ranges, either way round, and the same buffer
+    (dict(dst=ctypes.c_void_p(0x10000 + 4080)), tbl.ERR_INVALID_ARG),
+    (dict(src=ctypes.c_void_p(0x20000 + 16), dst=ctypes.c_void_p(0x20000)), tbl.ERR_INVALID_ARG),
+    (dict(dst=FAKE), tbl.ERR_INVALID_ARG),
+])
+def test_copy16_rejects(kw, want):
+    assert _copy(**kw) == want

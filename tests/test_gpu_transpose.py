@@ -44,3 +44,22 @@ def test_transpose_rejects_ragged():
     with pytest.raises(tbl.TblError) as e:
         tbl.transpose_i32(xd)
     assert e.value.status == tbl.ERR_SHAPE
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, (1 << 26) + 48, (1 << 32) + 4096])
+def test_copy16_bit_exact(nbytes):
+    # the copy that measures the transpose's read-once, write-once HBM rate: identical bytes, with
+    # and without non-temporal accesses; the last size needs a second pass of the 2^20-workgroup grid
+    n = nbytes // 4
+    if nbytes < (1 << 30):
+        x = torch.from_numpy(synth.i32_uniform((n,), 21)).cuda()
+    else:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(21)
+        x = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda", generator=g)
+    for nt in (False, True):
+        y = torch.zeros_like(x)
+        tbl.copy16(x, y, nontemporal=nt)
+        torch.cuda.synchronize()
+        assert torch.equal(x, y), (nbytes, nt)
+    del x, y

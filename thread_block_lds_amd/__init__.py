@@ -84,6 +84,8 @@ _EXPORTS = {
     "tbl_mfma_rate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p]),
+    "tbl_copy16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_void_p]),
     "tbl_gemm_tile_shape": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                            ctypes.POINTER(ctypes.c_int)]),
@@ -388,6 +390,26 @@ def transpose_i32(x, out=None, layout=T_XOR, stream=None):
     st = lib().tbl_transpose_i32(_ptr(x), _ptr(out), rows, cols, int(layout), _stream(stream))
     _check(st, "tbl_transpose_i32")
     return out
+
+
+def copy16(src, dst=None, nontemporal=False, stream=None):
+    """dst = src for contiguous CUDA tensors of the same byte size (a multiple of 16), through
+    tbl_copy16: a measurement aid for the transpose's roofline. Returns dst."""
+    import torch
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    if dst is None:
+        dst = torch.empty_like(src)
+    if not dst.is_contiguous():
+        raise ValueError("dst must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _device_tensor(src, "src")
+    _device_tensor(dst, "dst", device=src.device)
+    st = lib().tbl_copy16(_ptr(src), _ptr(dst), nbytes, 1 if nontemporal else 0, _stream(stream))
+    _check(st, "tbl_copy16")
+    return dst
 
 
 def predict_l2(mode, grid_m, grid_n, grid_k, group=1, a_block_bytes=1, b_block_bytes=1,

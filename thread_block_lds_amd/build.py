@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtbl.so")
 SOURCES = ["api.hip", "gemm.hip", "gemm_any.hip", "gemm_layouts.hip", "transpose.hip", "tile_map.hip",
-           "mfma_rate.hip", "l2_predict.cpp"]
+           "mfma_rate.hip", "copy.hip", "l2_predict.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # packed-fp32-ops off: hipcc must not form packed fp32 instructions from scalar float code.

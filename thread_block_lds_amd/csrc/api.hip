@@ -20,6 +20,7 @@ constexpr int64_t kMaxDim = int64_t{1} << 20;
 constexpr int kMaxDynamicPrograms = 1 << 16;
 constexpr int kMinDynamicKSteps = 9;
 constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxCopyBytes = int64_t{1} << 40;
 
 struct DeviceInfo {
   bool valid = false;
@@ -159,7 +160,7 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
 
 extern "C" {
 
-int tbl_version(void) { return 105; }
+int tbl_version(void) { return 106; }
 
 const char* tbl_status_string(int status) {
   switch (status) {
@@ -478,6 +479,19 @@ int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t col
   if (!aligned16(in) || !aligned16(out)) return TBL_ERR_ALIGN;
   if (tbl::launch_transpose_i32(in, out, static_cast<int>(rows), static_cast<int>(cols), layout,
                                 static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TBL_ERR_HIP;
+  return TBL_OK;
+}
+
+int tbl_copy16(const void* src, void* dst, int64_t bytes, int nontemporal, void* stream) {
+  if (src == nullptr || dst == nullptr || bytes <= 0) return TBL_ERR_INVALID_ARG;
+  if (nontemporal != 0 && nontemporal != 1) return TBL_ERR_INVALID_ARG;
+  if (bytes % 16 != 0 || bytes > kMaxCopyBytes) return TBL_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return TBL_ERR_ALIGN;
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t n = static_cast<uintptr_t>(bytes);
+  if (s < d + n && d < s + n) return TBL_ERR_INVALID_ARG;   // the ranges overlap
+  if (tbl::launch_copy16(src, dst, bytes, nontemporal == 1, static_cast<hipStream_t>(stream)) != hipSuccess)
     return TBL_ERR_HIP;
   return TBL_OK;
 }

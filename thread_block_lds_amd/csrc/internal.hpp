@@ -72,4 +72,7 @@ hipError_t launch_mfma_rate(const void* A, const void* B, int64_t elems, bool bf
 hipError_t launch_transpose_i32(const int32_t* in, int32_t* out, int rows, int cols, int layout,
                                 hipStream_t s);
 
+// The plain 16-byte-per-lane copy (copy.hip); bytes a positive multiple of 16, arguments validated.
+hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, bool nontemporal, hipStream_t s);
+
 }  // namespace tbl
