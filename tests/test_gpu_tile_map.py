@@ -1,6 +1,6 @@
 """GPU parity: tbl_tile_map tables equal the oracle's, bit for bit, for every order, group size,
 remap flag and grid (the pages' 8x8 / 4x4 grids, the workloads' 8x8, 16x16, 32x32 and 40x24
-grids, odd rectangular grids and a large one)."""
+grids, odd rectangular grids, and large grids up to 2^26 ids and the largest accepted dimension)."""
 
 import numpy as np
 import pytest
@@ -91,3 +91,19 @@ def test_page3_example2_on_gpu():
     # and clusters of 2 rows over row-major reproduce the printed group-major 4x4 table
     m, n, _ = _gpu_table(tm.ROW | tbl.cluster(2, 1), 4, 4, 1)
     assert np.array_equal(tm.inverse_grid(m, n, 4, 4), golden_grid("p3_group_major_4x4_g2.txt"))
+
+
+@pytest.mark.parametrize("mode,gm,gn,g", [
+    (tm.MORTON, 8192, 8192, 1), (tm.MORTON | tm.XCD_REMAP, 8192, 8192, 1), (tm.XOR, 8192, 8192, 1),
+    (tm.ROW | tm.XCD_REMAP, 8192, 8192, 1),
+    (tm.PANEL, 3000, 5000, 7), (tm.PANEL | tm.XCD_REMAP, 3000, 5000, 7), (tm.SERPENTINE, 3000, 5000, 13),
+    (tm.SERPENTINE | tm.XCD_REMAP, 3000, 5000, 13), (tm.COL, 3000, 5000, 1),
+    (tm.SERPENTINE, 1 << 20, 3, 2), (tm.PANEL, 3, 1 << 20, 2), (tm.PANEL | tm.XCD_REMAP, 1 << 20, 1, 5),
+])
+def test_large_tables_match_oracle(mode, gm, gn, g):
+    # 2^26 ids at 8192 x 8192 (Morton's and XOR's bit operations on 26-bit ids), 15 M ids with
+    # groups and strips that leave partial last groups, and grids at the largest accepted dimension
+    m, n, st = _gpu_table(mode, gm, gn, g)
+    om, on = tm.tile_table(mode, gm, gn, g)
+    assert st == tbl.OK
+    assert np.array_equal(m, om) and np.array_equal(n, on), (mode, gm, gn, g)
