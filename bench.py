@@ -580,8 +580,8 @@ def target_check(tbl, torch, stream, measured=None, reps=10):
         res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_TFLOPS, 2),
                      "schedule": "dynamic"}
         res[name].update(_trace_split(tbl, torch, ad, bd, c, mode, g, C3 // 32, workspace=ws))
-    # the north star's "gain over linear ordering" at this workload: measured L2 hit-rate points and
-    # throughput of each static order against row-major (no remap)
+    # the gain over linear ordering at this workload: measured L2 hit-rate points and throughput of
+    # each static order against row-major (no remap)
     for name, _, _ in C3_MODES:
         r = res[name]
         if "l2_hit_pct" in r and "l2_hit_pct" in res["row"]:
