@@ -15,8 +15,9 @@ Printed: one JSON line with
                evicts the L2s and the memory-side cache, as the page's timing clears L2 first),
                TFLOP/s and % of the 2.5 PFLOP/s dense fp16 MFMA peak; the L2 (TCC) hit rate, its
                gain over row-major, HBM fetch bytes, LDS bank conflicts and MFMA busy fraction from
-               rocprofv3 --pmc passes (cold launches, not timed); and the offline L2 prediction of
-               the library's tbl_predict_l2 for eight private L2s;
+               rocprofv3 --pmc passes (cold launches, not timed), with the core clock that launch
+               held and its rate as a percentage of the peak at that clock; and the offline L2
+               prediction of the library's tbl_predict_l2 for eight private L2s;
   l2_model     Spearman rank correlations of the prediction with the measured hit rate, fetch bytes
                and cold throughput;
   roofline     the GEMM kernel: average launch time (two HIP events on the launch stream around the
@@ -69,6 +70,7 @@ if ROOT not in sys.path:
 M = N = K = 4096
 TILE, TILE_K = 256, 32
 PEAK_TFLOPS = 2500.0          # MI355X dense fp16/bf16 MFMA
+PEAK_CLOCK_GHZ = 2.4          # the engine clock that peak assumes (256 CUs x 4 SIMDs x 1024 flops)
 HBM_PEAK_GBS = 8000.0
 REMAP = 0x100
 ORDERS = [("row", 0, 1), ("panel_g4", 2, 4), ("panel_g8", 2, 8), ("panel_g16", 2, 16),
@@ -212,11 +214,33 @@ def _run_pmc(counters, tag, tmp, pass_flag="--counter-pass"):
     files = glob.glob(os.path.join(out, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise RuntimeError(f"rocprofv3 wrote no counter file for {tag}")
+    return _pmc_rows(files[0])
+
+
+def _pmc_rows(path):
+    """One dict per dispatch of a rocprofv3 counter CSV: kernel name, each counter's value, and the
+    dispatch's duration in ns when the file carries its timestamps."""
     rows = {}
-    for r in csv.DictReader(open(files[0])):
+    for r in csv.DictReader(open(path)):
         d = int(r["Dispatch_Id"])
-        rows.setdefault(d, {"kernel": r["Kernel_Name"]})[r["Counter_Name"]] = float(r["Counter_Value"])
+        row = rows.setdefault(d, {"kernel": r["Kernel_Name"]})
+        row[r["Counter_Name"]] = float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            row["dur_ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     return [rows[d] for d in sorted(rows)]
+
+
+def sustained_clock(grbm_gui_active, dur_ns, xcds=8):
+    """Core clock (GHz) a dispatch held: GRBM_GUI_ACTIVE sums the busy clocks of the XCDs, so one
+    XCD's clocks over the dispatch's duration."""
+    return grbm_gui_active / xcds / dur_ns if dur_ns > 0 else None
+
+
+def pct_peak_at_clock(flops, dur_ns, clock_ghz):
+    """Percent of the dense MFMA peak scaled to a clock: the 2.5 PFLOP/s spec assumes 2.4 GHz."""
+    if not clock_ghz or dur_ns <= 0:
+        return None
+    return 100.0 * flops / (dur_ns * 1e-9) / 1e12 / (PEAK_TFLOPS * clock_ghz / PEAK_CLOCK_GHZ)
 
 
 def counters():
@@ -253,6 +277,14 @@ def counters():
             # no MFMA beyond the product's own
             mops = r.get("SQ_INSTS_VALU_MFMA_MOPS_F16")
             per[name]["mfma_flops_over_algorithmic"] = mops * 512.0 / FLOPS if mops else None
+            # the clock this (cold, profiled) launch held, and its rate against the peak at that
+            # clock instead of the spec's 2.4 GHz
+            if r.get("dur_ns"):
+                clk = sustained_clock(r["GRBM_GUI_ACTIVE"], r["dur_ns"])
+                per[name]["pmc_launch_us"] = round(r["dur_ns"] / 1e3, 2)
+                per[name]["sustained_clock_ghz"] = round(clk, 3) if clk else None
+                pct = pct_peak_at_clock(FLOPS, r["dur_ns"], clk)
+                per[name]["pct_peak_at_clock"] = round(pct, 2) if pct else None
         # the 8192^3 target: measured L2 hit rate per static order (cold launches); a failure here
         # leaves only these figures out
         target = None
@@ -1160,6 +1192,9 @@ def main():
             per_mode[name]["mfma_busy_frac"] = round(per[name]["mfma_busy_frac"], 4)
             f = per[name].get("mfma_flops_over_algorithmic")
             per_mode[name]["mfma_flops_over_algorithmic"] = round(f, 4) if f is not None else None
+            for k in ("pmc_launch_us", "sustained_clock_ghz", "pct_peak_at_clock"):
+                if k in per[name]:
+                    per_mode[name][k] = per[name][k]
         if fac_f and fac_w:
             mb = [per_mode[n]["fetch_mb"] + per_mode[n]["write_mb"] for n, _, _ in MODES]
             traffic = round(1e6 * sum(mb) / len(mb))

@@ -109,3 +109,23 @@ def test_ranks_desc_and_line_fit():
                                 {"a": {"l2_hit_pct": 82.0, "fetch_mb": 110.0}, "b": {"l2_hit_pct": 33.0, "fetch_mb": 380.0}})
     assert fit["spearman_vs_measured_hit"] == 1.0 and fit["max_abs_hit_err_pp"] == 3.0
     assert fit["max_rel_fetch_err"] == round(10 / 110, 4)
+
+
+def test_counter_rows_clock_and_peak_at_clock(tmp_path):
+    # a two-dispatch counter CSV as rocprofv3 writes it: the dispatch duration comes from its
+    # timestamps; GRBM_GUI_ACTIVE sums the eight XCDs' busy clocks
+    path = tmp_path / "x_counter_collection.csv"
+    path.write_text(
+        '"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n'
+        '1,"k1","GRBM_GUI_ACTIVE",1600000,1000,101000\n'
+        '1,"k1","SQ_BUSY_CYCLES",5,1000,101000\n'
+        '2,"k2","GRBM_GUI_ACTIVE",8,0,4\n')
+    rows = bench._pmc_rows(str(path))
+    assert [r["kernel"] for r in rows] == ["k1", "k2"]
+    assert rows[0]["dur_ns"] == 100000.0 and rows[0]["SQ_BUSY_CYCLES"] == 5.0
+    clk = bench.sustained_clock(rows[0]["GRBM_GUI_ACTIVE"], rows[0]["dur_ns"])
+    assert clk == pytest.approx(2.0)               # 1.6e6 / 8 XCDs over 100 us
+    # 2 * 4096^3 flops in 100 us at 2.0 GHz: 1374.4 TFLOP/s against 2500 * 2.0 / 2.4 = 2083.3
+    pct = bench.pct_peak_at_clock(2 * 4096 ** 3, rows[0]["dur_ns"], clk)
+    assert pct == pytest.approx(100 * 1374.389534720 / (2500 * 2.0 / 2.4))
+    assert bench.pct_peak_at_clock(1.0, 0.0, 2.0) is None and bench.sustained_clock(1.0, 0.0) is None
