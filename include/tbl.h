@@ -198,6 +198,8 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  *   K             at least 257 (nine 32-deep k steps per tile: a tile's successor is claimed and
  *                 handed to all waves in its first five, before the loads run into it);
  *                 TBL_ERR_SHAPE otherwise. The tile grid may have at most 2^30 tiles.
+ *   N, K          multiples of 8 (this schedule runs only the fast kernel, whose direct loads move
+ *                 row chunks of 16 bytes); TBL_ERR_SHAPE otherwise.
  *   All other arguments as tbl_gemm. Errors: as tbl_gemm_tiled, plus TBL_ERR_INVALID_ARG for a NULL
  *   or short workspace, TBL_ERR_ALIGN for a misaligned one.
  */
@@ -244,6 +246,7 @@ int tbl_gemm_dynamic_noalloc(const void* A, const void* B, void* C, int64_t M, i
  *                 (1,1,...) no swizzle, (1,4), (2,4), (4,2), (8,4); B varied with A at its default:
  *                 (...,1,1,1) no swizzle, (1,1,4), (2,1,4), (4,1,2), (4,2,2), (8,1,4).
  *                 TBL_ERR_INVALID_ARG for any other combination.
+ *   N, K          multiples of 8, as for tbl_gemm_dynamic (TBL_ERR_SHAPE otherwise).
  *   All other arguments as tbl_gemm (num_programs = 0 resolves as for the 256x256 kernel).
  */
 int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
