@@ -31,8 +31,10 @@
  * Conventions shared by every entry point:
  *   - Matrices are dense and row-major with no padding: A is M x K, B is K x N, C is M x N.
  *   - Every pointer is device memory owned by the caller. The library never allocates or frees
- *     device memory in these calls and keeps no pointer after a call returns. Outputs must not alias
- *     inputs. GEMM and transpose base pointers must be 16-byte aligned.
+ *     device memory in these calls and keeps no pointer after a call returns. A buffer a call writes
+ *     must share no byte with the buffers it reads or its other outputs; the GEMM, transpose and copy
+ *     entry points check this from the sizes and return TBL_ERR_INVALID_ARG. GEMM and transpose
+ *     base pointers must be 16-byte aligned.
  *   - ``stream`` is a hipStream_t (NULL = the null stream). Calls enqueue work and return; only
  *     launch-time errors are reported, device-side faults surface at the caller's next
  *     synchronisation.
@@ -59,7 +61,7 @@ extern "C" {
 /* ---- status codes ---------------------------------------------------------------------------- */
 enum {
   TBL_OK = 0,
-  TBL_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, unknown mode/layout, bad group */
+  TBL_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, unknown mode/layout, bad group, overlapping buffers */
   TBL_ERR_DTYPE = -2,         /* unknown dtype code */
   TBL_ERR_SHAPE = -3,         /* sizes out of range, unsupported tile, or a cluster that does not tile the grid */
   TBL_ERR_NOT_BIJECTIVE = -4, /* GEMM with Morton/XOR on a (cluster) grid that is not a square power of two */
@@ -125,7 +127,8 @@ enum {
 
 /*
  * tbl_gemm -- C = A * B with a swizzled, optionally persistent tile schedule.
- *   A, B, C       device pointers (row-major M x K, K x N, M x N), 16-byte aligned, C not aliasing.
+ *   A, B, C       device pointers (row-major M x K, K x N, M x N), 16-byte aligned (TBL_ERR_ALIGN).
+ *                 C shares no byte with A or B (TBL_ERR_INVALID_ARG); A and B may overlap.
  *   M, N, K       sizes, > 0, each <= 2^20 (TBL_ERR_SHAPE otherwise); any values. The tile shape is
  *                 fixed by a rule (tbl_gemm_tile_shape): 256x256x32 when that grid has at least 128
  *                 tiles (half of gfx950's 256 CUs), else 128x128x32 when its grid does, else 64x64x32
@@ -166,7 +169,8 @@ int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_
  *                 before its prologue loads, a later tile where the previous tile's epilogue ends
  *                 (its operands are already loading then). Times are those of the workgroup's
  *                 first wave.
- *                 Caller-owned. Tracing adds a few instructions per tile.
+ *                 Caller-owned; shares no byte with A, B or C (TBL_ERR_INVALID_ARG). Tracing adds a
+ *                 few instructions per tile.
  *   All other arguments as tbl_gemm.
  */
 int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
@@ -193,8 +197,10 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  *                 first enqueues a one-workgroup kernel that zeroes the claim counters (ints 0..8),
  *                 so no initial contents are needed; calls that share a workspace must not overlap
  *                 in time (same stream, or synchronised). int 9 counts hand-over faults between a
- *                 workgroup's waves: never expected, never reset; zero it to watch it.
- *   trace         NULL or device int32[8 * T], as tbl_gemm_tiled, indexed by order position.
+ *                 workgroup's waves: never expected, never reset; zero it to watch it. The ints the
+ *                 kernels touch share no byte with A, B, C or the trace (TBL_ERR_INVALID_ARG).
+ *   trace         NULL or device int32[8 * T], as tbl_gemm_tiled (no byte shared with A, B or C),
+ *                 indexed by order position.
  *   K             at least 257 (nine 32-deep k steps per tile: a tile's successor is claimed and
  *                 handed to all waves in its first five, before the loads run into it);
  *                 TBL_ERR_SHAPE otherwise. The tile grid may have at most 2^30 tiles.
@@ -286,7 +292,8 @@ int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32
 /*
  * tbl_transpose_i32 -- out (cols x rows) = transpose of in (rows x cols), int32, bit-exact,
  * staged through a 64 x 64 LDS tile in the given layout.
- *   in, out       device pointers, 16-byte aligned, not aliasing.
+ *   in, out       device pointers, 16-byte aligned (TBL_ERR_ALIGN), sharing no byte
+ *                 (TBL_ERR_INVALID_ARG).
  *   rows, cols    > 0, multiples of 64, each <= 2^20 (TBL_ERR_SHAPE otherwise).
  *   layout        TBL_T_NAIVE, TBL_T_PADDED or TBL_T_XOR.
  */

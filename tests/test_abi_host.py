@@ -18,6 +18,8 @@ HEADER = os.path.join(ROOT, "include", "tbl.h")
 FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
 MISALIGNED = ctypes.c_void_p(0x10008)
 NULL = ctypes.c_void_p(0)
+# separate fake buffers, 2^44 bytes apart (more than any accepted operand), never dereferenced
+FA, FB, FC, FW = (ctypes.c_void_p(i << 44) for i in (1, 2, 3, 4))
 
 
 def _declared():
@@ -33,7 +35,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(tbl.exported_names()) == declared
-    assert tbl.version() == 106
+    assert tbl.version() == 107
 
 
 def test_status_strings():
@@ -41,12 +43,12 @@ def test_status_strings():
         assert isinstance(tbl.status_string(st), str) and tbl.status_string(st)
 
 
-def _gemm(A=FAKE, B=FAKE, C=FAKE, M=512, N=512, K=512, dtype=0, mode=0, group=1, persistent=0, P=0):
+def _gemm(A=FA, B=FB, C=FC, M=512, N=512, K=512, dtype=0, mode=0, group=1, persistent=0, P=0):
     return tbl.lib().tbl_gemm(A, B, C, M, N, K, dtype, mode, group, persistent, P, NULL)
 
 
-def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=32, A=FAKE, dtype=0):
-    return tbl.lib().tbl_gemm_tiled(A, FAKE, FAKE, M, N, K, dtype, mode, group, 0, 0, bm, bn, bk, NULL, NULL)
+def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=32, A=FA, dtype=0):
+    return tbl.lib().tbl_gemm_tiled(A, FB, FC, M, N, K, dtype, mode, group, 0, 0, bm, bn, bk, NULL, NULL)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -70,10 +72,11 @@ def test_gemm_validation(kw, want):
     assert _gemm(**kw) == want
 
 
-def _dyn(M=2048, N=2048, K=2048, dtype=0, mode=0, group=1, P=64, ws=FAKE, ws_ints=None, A=FAKE):
+def _dyn(M=2048, N=2048, K=2048, dtype=0, mode=0, group=1, P=64, ws=FW, ws_ints=None, A=FA, B=FB, C=FC,
+         trace=NULL):
     if ws_ints is None:
         ws_ints = 32 + 32 * max(P, 1)
-    return tbl.lib().tbl_gemm_dynamic(A, FAKE, FAKE, M, N, K, dtype, mode, group, P, ws, ws_ints, NULL, NULL)
+    return tbl.lib().tbl_gemm_dynamic(A, B, C, M, N, K, dtype, mode, group, P, ws, ws_ints, trace, NULL)
 
 
 def test_gemm_dynamic_workspace_size():
@@ -98,8 +101,8 @@ def test_gemm_dynamic_validation(kw, want):
     assert _dyn(**kw) == want
 
 
-def _dyn_noalloc(A=FAKE, M=2048, N=2048, K=2048, dtype=0, mode=0, group=1, P=0):
-    return tbl.lib().tbl_gemm_dynamic_noalloc(A, FAKE, FAKE, M, N, K, dtype, mode, group, P, NULL, NULL)
+def _dyn_noalloc(A=FA, M=2048, N=2048, K=2048, dtype=0, mode=0, group=1, P=0):
+    return tbl.lib().tbl_gemm_dynamic_noalloc(A, FB, FC, M, N, K, dtype, mode, group, P, NULL, NULL)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -120,6 +123,46 @@ def test_noalloc_limit_matches_header():
     src = open(HEADER).read()
     assert re.search(r"#define TBL_NOALLOC_MAX_PROGRAMS (\d+)", src).group(1) == str(tbl.NOALLOC_MAX_PROGRAMS)
     assert "scratch" in tbl.status_string(tbl.ERR_SCRATCH)
+
+
+def _p(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_overlapping_buffers_rejected():
+    """A buffer a call writes shares no byte with what it reads or its other outputs. Every case is
+    rejected before any HIP call; the cases that pass the check are stopped by a later one (a
+    misaligned workspace, TBL_ERR_ALIGN) so that nothing is launched."""
+    M = N = K = 2048
+    a, b = 1 << 44, 2 << 44
+    a_end = a + M * K * 2
+    # C on A, inside B, or reaching into B's first bytes
+    assert _gemm(C=_p(a), M=M, N=N, K=K) == tbl.ERR_INVALID_ARG
+    assert _gemm(C=_p(b + 4096), M=M, N=N, K=K) == tbl.ERR_INVALID_ARG
+    assert _gemm(C=_p(b - M * N * 2 + 16), M=M, N=N, K=K) == tbl.ERR_INVALID_ARG
+    # C right behind A, and A = B (both only read): no overlap, the workspace check comes next
+    assert _dyn(C=_p(a_end), M=M, N=N, K=K, ws=MISALIGNED) == tbl.ERR_ALIGN
+    assert _dyn(B=_p(a), M=M, N=N, K=K, ws=MISALIGNED) == tbl.ERR_ALIGN
+    # C just in front of A: its fp16 extent ends at A, its fp32 extent reaches into A
+    c = a - M * N * 2
+    assert _dyn(C=_p(c), M=M, N=N, K=K, ws=MISALIGNED, dtype=tbl.F16) == tbl.ERR_ALIGN
+    assert _dyn(C=_p(c), M=M, N=N, K=K, ws=MISALIGNED, dtype=tbl.F16_F32OUT) == tbl.ERR_INVALID_ARG
+    # the workspace (the ints the kernels touch) against the operands and the trace
+    P = 64
+    need = 4 * (32 + 32 * P)
+    assert _dyn(ws=_p(3 << 44), P=P) == tbl.ERR_INVALID_ARG            # on C
+    assert _dyn(ws=_p(a_end - need + 16), P=P) == tbl.ERR_INVALID_ARG  # reaches A's end
+    assert _dyn(ws=_p(a - need), P=P, trace=_p(a - need - 16)) == tbl.ERR_INVALID_ARG   # trace on it
+    # a trace on an operand or on C
+    assert _dyn(trace=_p(b + 64), ws=MISALIGNED) == tbl.ERR_INVALID_ARG
+    assert tbl.lib().tbl_gemm_tiled(FA, FB, FC, 512, 512, 512, 0, 0, 1, 0, 0, 64, 64, 32, _p((3 << 44) + 8),
+                                    NULL) == tbl.ERR_INVALID_ARG
+    assert tbl.lib().tbl_gemm_tiled(FA, FB, FC, 512, 512, 512, 0, 0, 1, 0, 0, 64, 64, 32, FC, NULL) == tbl.ERR_INVALID_ARG
+    # transpose: out on in, or overlapping its last row
+    f = tbl.lib().tbl_transpose_i32
+    assert f(FA, FA, 1024, 2048, 2, NULL) == tbl.ERR_INVALID_ARG
+    assert f(FA, _p(a + 1024 * 2048 * 4 - 64), 1024, 2048, 2, NULL) == tbl.ERR_INVALID_ARG
+    assert f(FA, _p(a - 1024 * 2048 * 4 + 16), 1024, 2048, 1, NULL) == tbl.ERR_INVALID_ARG
 
 
 def test_gemm_tiled_validation():
@@ -177,8 +220,8 @@ def test_tile_shape_rule_and_default_programs():
         tbl.default_num_programs(520, (1 << 20) + 1, 512)
 
 
-def _layout(layout=(4, 4, 4, 1, 4), dtype=0, M=512, N=512, K=512, A=FAKE, mode=0):
-    return tbl.lib().tbl_gemm_lds_layout(A, FAKE, FAKE, M, N, K, dtype, mode, 1, 0, 0, *layout, NULL)
+def _layout(layout=(4, 4, 4, 1, 4), dtype=0, M=512, N=512, K=512, A=FA, mode=0):
+    return tbl.lib().tbl_gemm_lds_layout(A, FB, FC, M, N, K, dtype, mode, 1, 0, 0, *layout, NULL)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -210,8 +253,8 @@ def test_mfma_rate_rejects(kw, want):
     assert _rate(**kw) == want
 
 
-def _layout16(layout=(2, 4, 0, 0, 0), dtype=0, M=512, N=512, K=512, A=FAKE):
-    return tbl.lib().tbl_gemm_lds_layout16(A, FAKE, FAKE, M, N, K, dtype, 0, 1, 0, 0, *layout, NULL)
+def _layout16(layout=(2, 4, 0, 0, 0), dtype=0, M=512, N=512, K=512, A=FA):
+    return tbl.lib().tbl_gemm_lds_layout16(A, FB, FC, M, N, K, dtype, 0, 1, 0, 0, *layout, NULL)
 
 
 @pytest.mark.parametrize("kw,want", [

@@ -54,6 +54,32 @@ int device_info(DeviceInfo* out) {
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Whether the byte ranges [p, p + pn) and [q, q + qn) share a byte (sizes > 0; an empty range or a
+// null pointer overlaps nothing).
+bool overlaps(const void* p, int64_t pn, const void* q, int64_t qn) {
+  if (p == nullptr || q == nullptr || pn <= 0 || qn <= 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b ? b - a < static_cast<uintptr_t>(pn) : a - b < static_cast<uintptr_t>(qn);
+}
+
+int64_t out_elem_bytes(int dtype) { return dtype == TBL_F16_F32OUT || dtype == TBL_BF16_F32OUT ? 4 : 2; }
+
+// Whether C shares a byte with A or B (A and B, which are only read, may overlap each other).
+// Sizes come from validated arguments (M, N, K <= 2^20: no overflow).
+bool c_overlaps_operands(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+                         int dtype) {
+  const int64_t cn = M * N * out_elem_bytes(dtype);
+  return overlaps(C, cn, A, M * K * 2) || overlaps(C, cn, B, K * N * 2);
+}
+
+// Whether another buffer the GEMM writes (a trace or a workspace, [w, w + wn)) shares a byte with
+// A, B or C.
+bool extra_overlaps(const void* w, int64_t wn, const void* A, const void* B, const void* C, int64_t M,
+                    int64_t N, int64_t K, int dtype) {
+  return overlaps(w, wn, A, M * K * 2) || overlaps(w, wn, B, K * N * 2) ||
+         overlaps(w, wn, C, M * N * out_elem_bytes(dtype));
+}
+
 // Cluster dimensions encoded in bits 16..19 (cm - 1) and 20..23 (cn - 1) of a swizzle mode.
 int cluster_m(int swizzle_mode) { return ((swizzle_mode >> 16) & 15) + 1; }
 int cluster_n(int swizzle_mode) { return ((swizzle_mode >> 20) & 15) + 1; }
@@ -130,6 +156,7 @@ int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, i
   if (rc != TBL_OK) return rc;
   if (!bijective_grid(swizzle_mode, gm, gn)) return TBL_ERR_NOT_BIJECTIVE;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return TBL_ERR_ALIGN;
+  if (c_overlaps_operands(A, B, C, M, N, K, dtype)) return TBL_ERR_INVALID_ARG;
   return TBL_OK;
 }
 
@@ -160,7 +187,7 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
 
 extern "C" {
 
-int tbl_version(void) { return 106; }
+int tbl_version(void) { return 107; }
 
 const char* tbl_status_string(int status) {
   switch (status) {
@@ -192,6 +219,7 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
   if (rc != TBL_OK) return rc;
   const int gm = static_cast<int>((M + block_m - 1) / block_m);
   const int gn = static_cast<int>((N + block_n - 1) / block_n);
+  if (extra_overlaps(trace, int64_t{32} * gm * gn, A, B, C, M, N, K, dtype)) return TBL_ERR_INVALID_ARG;
   const bool chunked = chunk_rows(N, K);
   int programs = 0;
   rc = resolve_programs(dtype, block_m, block_n, block_k, static_cast<int64_t>(gm) * gn, persistent,
@@ -279,10 +307,14 @@ int64_t tbl_gemm_dynamic_workspace(int num_programs) {
 
 namespace {
 
+// Bytes of a dynamic-schedule trace: 8 ints per 256 x 256 tile.
+int64_t dynamic_trace_bytes(int64_t M, int64_t N) { return int64_t{32} * ((M + 255) / 256) * ((N + 255) / 256); }
+
 // Checks the arguments of a dynamic-schedule GEMM and resolves its workgroup count; the workspace
 // is checked by the caller. Returns TBL_OK with *programs set, or the error.
+
 int prepare_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
-                    int swizzle_mode, int group_size, int num_programs, int* programs) {
+                    int swizzle_mode, int group_size, int num_programs, const int32_t* trace, int* programs) {
   int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, 1, num_programs, 256, 256, 32);
   if (rc != TBL_OK) return rc;
   // wave 0 posts the next tile at k step 0 and the others read it at step 4; the load cursor
@@ -290,6 +322,7 @@ int prepare_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N,
   if ((K + 31) / 32 < kMinDynamicKSteps) return TBL_ERR_SHAPE;
   const int gm = static_cast<int>((M + 255) / 256), gn = static_cast<int>((N + 255) / 256);
   if (static_cast<int64_t>(gm) * gn > (int64_t{1} << 30)) return TBL_ERR_SHAPE;
+  if (extra_overlaps(trace, dynamic_trace_bytes(M, N), A, B, C, M, N, K, dtype)) return TBL_ERR_INVALID_ARG;
   rc = resolve_programs(dtype, 256, 256, 32, static_cast<int64_t>(gm) * gn, 1, num_programs, programs);
   if (rc != TBL_OK) return rc;
   if (*programs > kMaxDynamicPrograms) return TBL_ERR_INVALID_ARG;
@@ -359,11 +392,15 @@ int tbl_gemm_dynamic(const void* A, const void* B, void* C, int64_t M, int64_t N
                      int swizzle_mode, int group_size, int num_programs, int32_t* workspace,
                      int64_t workspace_ints, int32_t* trace, void* stream) {
   int programs = 0;
-  int rc = prepare_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, num_programs, &programs);
+  int rc = prepare_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, num_programs, trace, &programs);
   if (rc != TBL_OK) return rc;
   if (workspace == nullptr || !aligned16(workspace)) return workspace == nullptr ? TBL_ERR_INVALID_ARG
                                                                                  : TBL_ERR_ALIGN;
   if (workspace_ints < tbl_gemm_dynamic_workspace(programs)) return TBL_ERR_INVALID_ARG;
+  // the part of the workspace the kernels touch
+  const int64_t ws_bytes = 4 * tbl_gemm_dynamic_workspace(programs);
+  if (extra_overlaps(workspace, ws_bytes, A, B, C, M, N, K, dtype)) return TBL_ERR_INVALID_ARG;
+  if (overlaps(trace, dynamic_trace_bytes(M, N), workspace, ws_bytes)) return TBL_ERR_INVALID_ARG;
   return launch_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, programs, workspace, trace,
                         stream);
 }
@@ -372,7 +409,7 @@ int tbl_gemm_dynamic_noalloc(const void* A, const void* B, void* C, int64_t M, i
                              int dtype, int swizzle_mode, int group_size, int num_programs,
                              int32_t* trace, void* stream) {
   int programs = 0;
-  int rc = prepare_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, num_programs, &programs);
+  int rc = prepare_dynamic(A, B, C, M, N, K, dtype, swizzle_mode, group_size, num_programs, trace, &programs);
   if (rc != TBL_OK) return rc;
   if (programs > TBL_NOALLOC_MAX_PROGRAMS) return TBL_ERR_SCRATCH;
   int32_t* ws = device_scratch(&rc);
@@ -477,6 +514,7 @@ int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t col
   if (layout < TBL_T_NAIVE || layout > TBL_T_XOR) return TBL_ERR_INVALID_ARG;
   if (rows % 64 || cols % 64 || rows > kMaxDim || cols > kMaxDim) return TBL_ERR_SHAPE;
   if (!aligned16(in) || !aligned16(out)) return TBL_ERR_ALIGN;
+  if (overlaps(in, rows * cols * 4, out, rows * cols * 4)) return TBL_ERR_INVALID_ARG;
   if (tbl::launch_transpose_i32(in, out, static_cast<int>(rows), static_cast<int>(cols), layout,
                                 static_cast<hipStream_t>(stream)) != hipSuccess)
     return TBL_ERR_HIP;
@@ -488,9 +526,7 @@ int tbl_copy16(const void* src, void* dst, int64_t bytes, int nontemporal, void*
   if (nontemporal != 0 && nontemporal != 1) return TBL_ERR_INVALID_ARG;
   if (bytes % 16 != 0 || bytes > kMaxCopyBytes) return TBL_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(dst)) return TBL_ERR_ALIGN;
-  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
-  const uintptr_t n = static_cast<uintptr_t>(bytes);
-  if (s < d + n && d < s + n) return TBL_ERR_INVALID_ARG;   // the ranges overlap
+  if (overlaps(src, bytes, dst, bytes)) return TBL_ERR_INVALID_ARG;
   if (tbl::launch_copy16(src, dst, bytes, nontemporal == 1, static_cast<hipStream_t>(stream)) != hipSuccess)
     return TBL_ERR_HIP;
   return TBL_OK;
