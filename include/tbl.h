@@ -129,7 +129,10 @@ enum {
  * tbl_gemm -- C = A * B with a swizzled, optionally persistent tile schedule.
  *   A, B, C       device pointers (row-major M x K, K x N, M x N), 16-byte aligned (TBL_ERR_ALIGN).
  *                 C shares no byte with A or B (TBL_ERR_INVALID_ARG); A and B may overlap.
- *   M, N, K       sizes, > 0, each <= 2^20 (TBL_ERR_SHAPE otherwise); any values. The tile shape is
+ *   M, N, K       sizes, >= 0 (TBL_ERR_INVALID_ARG otherwise), each <= 2^20 (TBL_ERR_SHAPE
+ *                 otherwise); any values. M = 0 or N = 0: C has no element and nothing is enqueued.
+ *                 K = 0 (M, N > 0): C is set to +0, the empty sum, by a fill kernel. A buffer with
+ *                 no element may be NULL. The tile shape is
  *                 fixed by a rule (tbl_gemm_tile_shape): 256x256x32 when that grid has at least 128
  *                 tiles (half of gfx950's 256 CUs), else 128x128x32 when its grid does, else 64x64x32
  *                 (k advances through LDS 32 deep). The tile grid is ceil(M/BM) x
@@ -171,7 +174,7 @@ int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_
  *                 first wave.
  *                 Caller-owned; shares no byte with A, B or C (TBL_ERR_INVALID_ARG). Tracing adds a
  *                 few instructions per tile.
- *   All other arguments as tbl_gemm.
+ *   All other arguments as tbl_gemm. With K = 0 no tile runs and the trace is left as it is.
  */
 int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
                    int swizzle_mode, int group_size, int persistent, int num_programs, int block_m,
@@ -206,6 +209,7 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  *                 TBL_ERR_SHAPE otherwise. The tile grid may have at most 2^30 tiles.
  *   N, K          multiples of 8 (this schedule runs only the fast kernel, whose direct loads move
  *                 row chunks of 16 bytes); TBL_ERR_SHAPE otherwise.
+ *   M, N          >= 1 (TBL_ERR_INVALID_ARG otherwise).
  *   All other arguments as tbl_gemm. Errors: as tbl_gemm_tiled, plus TBL_ERR_INVALID_ARG for a NULL
  *   or short workspace, TBL_ERR_ALIGN for a misaligned one.
  */
@@ -253,6 +257,7 @@ int tbl_gemm_dynamic_noalloc(const void* A, const void* B, void* C, int64_t M, i
  *                 (...,1,1,1) no swizzle, (1,1,4), (2,1,4), (4,1,2), (4,2,2), (8,1,4).
  *                 TBL_ERR_INVALID_ARG for any other combination.
  *   N, K          multiples of 8, as for tbl_gemm_dynamic (TBL_ERR_SHAPE otherwise).
+ *   M, N, K       >= 1 (TBL_ERR_INVALID_ARG otherwise).
  *   All other arguments as tbl_gemm (num_programs = 0 resolves as for the 256x256 kernel).
  */
 int tbl_gemm_lds_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
@@ -280,7 +285,8 @@ int tbl_gemm_lds_layout16(const void* A, const void* B, void* C, int64_t M, int6
 /*
  * tbl_tile_map -- write the forward table of an order: tile_m[t], tile_n[t] for t in [0, T).
  *   swizzle_mode  as tbl_gemm (TBL_XCD_REMAP and TBL_CLUSTER allowed).
- *   grid_m, grid_n  the tile grid, each in [1, 2^20], with grid_m * grid_n < 2^31.
+ *   grid_m, grid_n  the tile grid, each in [0, 2^20], with grid_m * grid_n < 2^31. An empty grid
+ *                 (either 0) has an empty table: nothing is written (the pointers may be NULL).
  *   group_size    as tbl_gemm (>= 1 for TBL_PANEL / TBL_SERPENTINE).
  *   tile_m, tile_n  device int32[T], caller-owned.
  * Returns TBL_WARN_NOT_BIJECTIVE (after enqueueing) for Morton/XOR on a grid that is not a square
@@ -294,7 +300,8 @@ int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32
  * staged through a 64 x 64 LDS tile in the given layout.
  *   in, out       device pointers, 16-byte aligned (TBL_ERR_ALIGN), sharing no byte
  *                 (TBL_ERR_INVALID_ARG).
- *   rows, cols    > 0, multiples of 64, each <= 2^20 (TBL_ERR_SHAPE otherwise).
+ *   rows, cols    >= 0 (TBL_ERR_INVALID_ARG otherwise), multiples of 64, each <= 2^20
+ *                 (TBL_ERR_SHAPE otherwise). Either 0: nothing to do, the pointers may be NULL.
  *   layout        TBL_T_NAIVE, TBL_T_PADDED or TBL_T_XOR.
  */
 int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t cols, int layout,
@@ -389,12 +396,14 @@ int tbl_mfma_rate(const void* A, const void* B, int64_t elems, int dtype, int wo
  * "Case Study / Matrix Transpose", reads and writes every element once).
  *   src, dst      device pointers, 16-byte aligned (TBL_ERR_ALIGN), ranges not overlapping
  *                 (TBL_ERR_INVALID_ARG).
- *   bytes         > 0 (TBL_ERR_INVALID_ARG), a multiple of 16 and at most 2^40 (TBL_ERR_SHAPE).
+ *   bytes         >= 0 (TBL_ERR_INVALID_ARG), a multiple of 16 and at most 2^40 (TBL_ERR_SHAPE);
+ *                 0 copies nothing (the pointers may then be NULL).
  *   nontemporal   0: ordinary loads and stores; 1: non-temporal ones (streaming hints to the caches).
  */
 int tbl_copy16(const void* src, void* dst, int64_t bytes, int nontemporal, void* stream);
 
-/* tbl_gemm_tile_shape -- the tile shape tbl_gemm uses for these sizes (host only, no HIP call). */
+/* tbl_gemm_tile_shape -- the tile shape tbl_gemm uses for these sizes (>= 0; host only, no HIP
+ * call). */
 int tbl_gemm_tile_shape(int64_t M, int64_t N, int64_t K, int* block_m, int* block_n, int* block_k);
 
 /*

@@ -53,7 +53,7 @@ def _tiled(M=512, N=512, K=512, mode=0, group=1, bm=64, bn=64, bk=32, A=FA, dtyp
 
 @pytest.mark.parametrize("kw,want", [
     (dict(A=NULL), tbl.ERR_INVALID_ARG), (dict(B=NULL), tbl.ERR_INVALID_ARG), (dict(C=NULL), tbl.ERR_INVALID_ARG),
-    (dict(M=0), tbl.ERR_INVALID_ARG), (dict(N=-64), tbl.ERR_INVALID_ARG), (dict(K=0), tbl.ERR_INVALID_ARG),
+    (dict(M=-1), tbl.ERR_INVALID_ARG), (dict(N=-64), tbl.ERR_INVALID_ARG), (dict(K=-8), tbl.ERR_INVALID_ARG),
     (dict(dtype=4), tbl.ERR_DTYPE), (dict(dtype=-1), tbl.ERR_DTYPE),
     (dict(mode=6), tbl.ERR_INVALID_ARG), (dict(mode=0x200), tbl.ERR_INVALID_ARG), (dict(mode=-1), tbl.ERR_INVALID_ARG),
     (dict(mode=tbl.PANEL, group=0), tbl.ERR_INVALID_ARG), (dict(mode=tbl.SERPENTINE, group=-2), tbl.ERR_INVALID_ARG),
@@ -125,6 +125,40 @@ def test_noalloc_limit_matches_header():
     assert "scratch" in tbl.status_string(tbl.ERR_SCRATCH)
 
 
+def test_empty_gemms_need_no_launch():
+    """M = 0 or N = 0: C has no element; the call succeeds with nothing enqueued (no HIP call, so
+    this runs without a GPU), empty buffers may be NULL, and what does not depend on the (empty)
+    tile grid is still checked. K = 0 with M, N > 0 launches the fill kernel, covered on the GPU;
+    here only its argument checks."""
+    g = tbl.lib().tbl_gemm
+    for M, N, K in [(0, 512, 512), (512, 0, 512), (0, 0, 0), (0, 7, 0), (3, 0, 0), (0, 0, 9)]:
+        a = NULL if M * K == 0 else FA
+        b = NULL if K * N == 0 else FB
+        for persistent in (0, 1):
+            assert g(a, b, NULL, M, N, K, 0, 0, 1, persistent, 0, NULL) == tbl.OK, (M, N, K)
+    # Morton on an empty grid is not a question of bijectivity
+    assert g(NULL, FB, NULL, 0, 512, 512, 1, tbl.MORTON, 1, 0, 0, NULL) == tbl.OK
+    assert g(NULL, FB, NULL, 0, 512, 512, 7, 0, 1, 0, 0, NULL) == tbl.ERR_DTYPE
+    assert g(NULL, FB, NULL, 0, 512, 512, 0, 6, 1, 0, 0, NULL) == tbl.ERR_INVALID_ARG
+    assert g(NULL, FB, NULL, 0, 512, 512, 0, tbl.PANEL, 0, 0, 0, NULL) == tbl.ERR_INVALID_ARG
+    assert g(NULL, FB, NULL, 0, 512, 512, 0, 0, 1, 2, 0, NULL) == tbl.ERR_INVALID_ARG
+    assert g(NULL, FB, NULL, 0, 512, (1 << 20) + 1, 0, 0, 1, 0, 0, NULL) == tbl.ERR_SHAPE
+    # a buffer with elements may not be NULL: B (512 x 512) here, though M = 0 leaves C empty
+    assert g(NULL, NULL, NULL, 0, 512, 512, 0, 0, 1, 0, 0, NULL) == tbl.ERR_INVALID_ARG
+    # K = 0: A and B may be NULL, C may not; the grid checks apply
+    assert g(NULL, NULL, NULL, 512, 512, 0, 0, 0, 1, 0, 0, NULL) == tbl.ERR_INVALID_ARG
+    assert g(NULL, NULL, MISALIGNED, 512, 512, 0, 0, 0, 1, 0, 0, NULL) == tbl.ERR_ALIGN
+    assert g(NULL, NULL, FC, 1024, 512, 0, 0, tbl.XOR, 1, 0, 0, NULL) == tbl.ERR_NOT_BIJECTIVE
+    t = tbl.lib().tbl_gemm_tiled
+    assert t(NULL, FB, NULL, 0, 300, 77, 0, 0, 1, 0, 0, 128, 128, 32, NULL, NULL) == tbl.OK
+    assert t(NULL, FB, NULL, 0, 300, 77, 0, 0, 1, 0, 0, 128, 64, 32, NULL, NULL) == tbl.ERR_SHAPE
+    assert tbl.gemm_tile_shape(0, 0, 0) == (64, 64, 32) and tbl.gemm_tile_shape(0, 8192, 8192) == (64, 64, 32)
+    # the dynamic schedule and the LDS-layout variants keep M, N, K >= 1
+    assert _dyn(M=0) == tbl.ERR_INVALID_ARG and _dyn(N=0) == tbl.ERR_INVALID_ARG
+    assert _dyn_noalloc(M=0) == tbl.ERR_INVALID_ARG
+    assert _layout(K=0) == tbl.ERR_INVALID_ARG and _layout16(M=0) == tbl.ERR_INVALID_ARG
+
+
 def _p(addr):
     return ctypes.c_void_p(addr)
 
@@ -181,7 +215,10 @@ def test_tile_map_validation():
     assert f(0, 8, 8, 1, NULL, FAKE, NULL) == tbl.ERR_INVALID_ARG
     assert f(7, 8, 8, 1, FAKE, FAKE, NULL) == tbl.ERR_INVALID_ARG
     assert f(tbl.PANEL, 8, 8, 0, FAKE, FAKE, NULL) == tbl.ERR_INVALID_ARG
-    assert f(0, 0, 8, 1, FAKE, FAKE, NULL) == tbl.ERR_SHAPE
+    assert f(0, -1, 8, 1, FAKE, FAKE, NULL) == tbl.ERR_SHAPE
+    # an empty grid has an empty table: nothing written, NULL allowed, the mode still checked
+    assert f(0, 0, 8, 1, NULL, NULL, NULL) == tbl.OK and f(tbl.SERPENTINE, 8, 0, 2, NULL, NULL, NULL) == tbl.OK
+    assert f(tbl.PANEL, 0, 8, 0, NULL, NULL, NULL) == tbl.ERR_INVALID_ARG and f(9, 0, 0, 1, NULL, NULL, NULL) == tbl.ERR_INVALID_ARG
     assert f(0, 8, -1, 1, FAKE, FAKE, NULL) == tbl.ERR_SHAPE
     assert f(0, 1 << 16, 1 << 16, 1, FAKE, FAKE, NULL) == tbl.ERR_SHAPE     # 2^32 tiles
 
@@ -189,7 +226,9 @@ def test_tile_map_validation():
 def test_transpose_validation():
     f = tbl.lib().tbl_transpose_i32
     assert f(NULL, FAKE, 64, 64, 0, NULL) == tbl.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, 0, 64, 0, NULL) == tbl.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, -64, 64, 0, NULL) == tbl.ERR_INVALID_ARG
+    assert f(NULL, NULL, 0, 64, 0, NULL) == tbl.OK and f(NULL, NULL, 128, 0, 2, NULL) == tbl.OK   # no element
+    assert f(NULL, NULL, 0, 64, 3, NULL) == tbl.ERR_INVALID_ARG and f(NULL, NULL, 0, 65, 0, NULL) == tbl.ERR_SHAPE
     assert f(FAKE, FAKE, 64, 64, 3, NULL) == tbl.ERR_INVALID_ARG
     assert f(FAKE, FAKE, 100, 64, 0, NULL) == tbl.ERR_SHAPE
     assert f(FAKE, FAKE, 64, 96, 2, NULL) == tbl.ERR_SHAPE
@@ -272,7 +311,7 @@ def _copy(src=FAKE, dst=ctypes.c_void_p(0x20000), nbytes=4096, nt=0):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(src=NULL), tbl.ERR_INVALID_ARG), (dict(dst=NULL), tbl.ERR_INVALID_ARG),
-    (dict(nbytes=0), tbl.ERR_INVALID_ARG), (dict(nbytes=-16), tbl.ERR_INVALID_ARG),
+    (dict(nbytes=-16), tbl.ERR_INVALID_ARG), (dict(nbytes=0, src=NULL, dst=NULL), tbl.OK),
     (dict(nt=2), tbl.ERR_INVALID_ARG), (dict(nt=-1), tbl.ERR_INVALID_ARG),
     (dict(nbytes=4100), tbl.ERR_SHAPE), (dict(nbytes=(1 << 40) + 16), tbl.ERR_SHAPE),
     (dict(src=MISALIGNED), tbl.ERR_ALIGN), (dict(dst=ctypes.c_void_p(0x20008)), tbl.ERR_ALIGN),

@@ -84,11 +84,18 @@ bool extra_overlaps(const void* w, int64_t wn, const void* A, const void* B, con
 int cluster_m(int swizzle_mode) { return ((swizzle_mode >> 16) & 15) + 1; }
 int cluster_n(int swizzle_mode) { return ((swizzle_mode >> 20) & 15) + 1; }
 
-int check_order(int swizzle_mode, int64_t gm, int64_t gn, int group) {
+// The checks of an order that do not depend on the grid.
+int check_mode(int swizzle_mode, int group) {
   const int mode = swizzle_mode & 0xFF;
   if ((swizzle_mode & ~(0xFF | TBL_XCD_REMAP | 0xFF0000)) != 0) return TBL_ERR_INVALID_ARG;
   if (mode < TBL_ROW || mode > TBL_SERPENTINE) return TBL_ERR_INVALID_ARG;
   if ((mode == TBL_PANEL || mode == TBL_SERPENTINE) && group < 1) return TBL_ERR_INVALID_ARG;
+  return TBL_OK;
+}
+
+int check_order(int swizzle_mode, int64_t gm, int64_t gn, int group) {
+  const int rc = check_mode(swizzle_mode, group);
+  if (rc != TBL_OK) return rc;
   if (gm < 1 || gn < 1 || gm > kMaxDim || gn > kMaxDim || gm * gn > INT32_MAX) return TBL_ERR_SHAPE;
   // a cluster of cm x cn tiles must tile the grid exactly
   if (gm % cluster_m(swizzle_mode) || gn % cluster_n(swizzle_mode)) return TBL_ERR_SHAPE;
@@ -136,21 +143,26 @@ void tile_rule(int64_t M, int64_t N, int* bm, int* bn, int* bk) {
 // element-wise path (gemm_any.hip) runs.
 bool chunk_rows(int64_t N, int64_t K) { return N % 8 == 0 && K % 8 == 0; }
 
-// any_shape: N and K need not be multiples of 8 (tbl_gemm, tbl_gemm_tiled); the dynamic schedule
-// and the LDS-layout variants run only the fast kernel and keep that requirement.
+// general: the entry points for any shape (tbl_gemm, tbl_gemm_tiled): N and K need not be
+// multiples of 8, and sizes may be 0 (an operand with no elements may then be NULL). The dynamic
+// schedule and the LDS-layout variants run only the fast kernel and keep both requirements.
 int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
                   int swizzle_mode, int group, int persistent, int num_programs, int bm, int bn,
-                  int bk, bool any_shape = false) {
-  if (A == nullptr || B == nullptr || C == nullptr) return TBL_ERR_INVALID_ARG;
-  if (M <= 0 || N <= 0 || K <= 0) return TBL_ERR_INVALID_ARG;
+                  int bk, bool general = false) {
+  if (M < 0 || N < 0 || K < 0) return TBL_ERR_INVALID_ARG;
+  if (!general && (M == 0 || N == 0 || K == 0)) return TBL_ERR_INVALID_ARG;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
+  if ((A == nullptr && M * K > 0) || (B == nullptr && K * N > 0) || (C == nullptr && M * N > 0))
+    return TBL_ERR_INVALID_ARG;
   if (dtype < TBL_F16 || dtype > TBL_BF16_F32OUT) return TBL_ERR_DTYPE;
   if (persistent != 0 && persistent != 1) return TBL_ERR_INVALID_ARG;
   if (num_programs < 0) return TBL_ERR_INVALID_ARG;
   if (!tbl::gemm_tile_supported(bm, bn, bk)) return TBL_ERR_SHAPE;
-  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
-  // partial tiles at the M, N and K edges are masked; without any_shape rows of B and A must be
-  // whole 16-byte chunks
-  if (!any_shape && !chunk_rows(N, K)) return TBL_ERR_SHAPE;
+  // partial tiles at the M, N and K edges are masked; outside the general entry points rows of B
+  // and A must be whole 16-byte chunks
+  if (!general && !chunk_rows(N, K)) return TBL_ERR_SHAPE;
+  // no output element, an empty tile grid: only what does not depend on the grid can be checked
+  if (M == 0 || N == 0) return check_mode(swizzle_mode, group);
   const int64_t gm = (M + bm - 1) / bm, gn = (N + bn - 1) / bn;
   int rc = check_order(swizzle_mode, gm, gn, group);
   if (rc != TBL_OK) return rc;
@@ -206,7 +218,7 @@ const char* tbl_status_string(int status) {
 
 int tbl_gemm_tile_shape(int64_t M, int64_t N, int64_t K, int* block_m, int* block_n, int* block_k) {
   if (block_m == nullptr || block_n == nullptr || block_k == nullptr) return TBL_ERR_INVALID_ARG;
-  if (M <= 0 || N <= 0 || K <= 0) return TBL_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return TBL_ERR_INVALID_ARG;
   tile_rule(M, N, block_m, block_n, block_k);
   return TBL_OK;
 }
@@ -217,9 +229,15 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
   int rc = validate_gemm(A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent, num_programs,
                          block_m, block_n, block_k, true);
   if (rc != TBL_OK) return rc;
+  if (M == 0 || N == 0) return TBL_OK;   // C has no element: nothing to compute
   const int gm = static_cast<int>((M + block_m - 1) / block_m);
   const int gn = static_cast<int>((N + block_n - 1) / block_n);
   if (extra_overlaps(trace, int64_t{32} * gm * gn, A, B, C, M, N, K, dtype)) return TBL_ERR_INVALID_ARG;
+  // K = 0: every element of C is the empty sum; no tile runs, so a trace is left as it is
+  if (K == 0)
+    return tbl::launch_gemm_zero(C, M * N * out_elem_bytes(dtype), static_cast<hipStream_t>(stream)) == hipSuccess
+               ? TBL_OK
+               : TBL_ERR_HIP;
   const bool chunked = chunk_rows(N, K);
   int programs = 0;
   rc = resolve_programs(dtype, block_m, block_n, block_k, static_cast<int64_t>(gm) * gn, persistent,
@@ -419,7 +437,7 @@ int tbl_gemm_dynamic_noalloc(const void* A, const void* B, void* C, int64_t M, i
 
 int tbl_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int dtype,
              int swizzle_mode, int group_size, int persistent, int num_programs, void* stream) {
-  if (M <= 0 || N <= 0 || K <= 0) return TBL_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return TBL_ERR_INVALID_ARG;
   int bm, bn, bk;
   tile_rule(M, N, &bm, &bn, &bk);
   return tbl_gemm_tiled(A, B, C, M, N, K, dtype, swizzle_mode, group_size, persistent, num_programs,
@@ -440,6 +458,8 @@ int tbl_default_num_programs(int64_t M, int64_t N, int64_t K, int dtype, int per
 
 int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32_t* tile_m,
                  int32_t* tile_n, void* stream) {
+  if (grid_m < 0 || grid_n < 0) return TBL_ERR_SHAPE;
+  if (grid_m == 0 || grid_n == 0) return check_mode(swizzle_mode, group_size);   // an empty table
   if (tile_m == nullptr || tile_n == nullptr) return TBL_ERR_INVALID_ARG;
   int rc = check_order(swizzle_mode, grid_m, grid_n, group_size);
   if (rc != TBL_OK) return rc;
@@ -509,10 +529,11 @@ int tbl_predict_l2_lines(int swizzle_mode, int64_t M, int64_t N, int64_t K, int 
 
 int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t cols, int layout,
                       void* stream) {
-  if (in == nullptr || out == nullptr) return TBL_ERR_INVALID_ARG;
-  if (rows <= 0 || cols <= 0) return TBL_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 0) return TBL_ERR_INVALID_ARG;
+  if ((in == nullptr || out == nullptr) && rows * cols > 0) return TBL_ERR_INVALID_ARG;
   if (layout < TBL_T_NAIVE || layout > TBL_T_XOR) return TBL_ERR_INVALID_ARG;
   if (rows % 64 || cols % 64 || rows > kMaxDim || cols > kMaxDim) return TBL_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return TBL_OK;   // no element
   if (!aligned16(in) || !aligned16(out)) return TBL_ERR_ALIGN;
   if (overlaps(in, rows * cols * 4, out, rows * cols * 4)) return TBL_ERR_INVALID_ARG;
   if (tbl::launch_transpose_i32(in, out, static_cast<int>(rows), static_cast<int>(cols), layout,
@@ -522,9 +543,10 @@ int tbl_transpose_i32(const int32_t* in, int32_t* out, int64_t rows, int64_t col
 }
 
 int tbl_copy16(const void* src, void* dst, int64_t bytes, int nontemporal, void* stream) {
-  if (src == nullptr || dst == nullptr || bytes <= 0) return TBL_ERR_INVALID_ARG;
+  if (bytes < 0 || ((src == nullptr || dst == nullptr) && bytes > 0)) return TBL_ERR_INVALID_ARG;
   if (nontemporal != 0 && nontemporal != 1) return TBL_ERR_INVALID_ARG;
   if (bytes % 16 != 0 || bytes > kMaxCopyBytes) return TBL_ERR_SHAPE;
+  if (bytes == 0) return TBL_OK;
   if (!aligned16(src) || !aligned16(dst)) return TBL_ERR_ALIGN;
   if (overlaps(src, bytes, dst, bytes)) return TBL_ERR_INVALID_ARG;
   if (tbl::launch_copy16(src, dst, bytes, nontemporal == 1, static_cast<hipStream_t>(stream)) != hipSuccess)
