@@ -7,13 +7,18 @@
 // N or K is not a multiple of 8 they do not, and this kernel runs instead. It keeps what the orders
 // are about -- the same tile grid, the same stride schedule over the same order_tile, the same
 // optional trace -- and moves operands element by element:
-//   * one 32-deep k step at a time, single-buffered: every thread fetches 8-element runs of A (along
-//     k, row-major in LDS) and of B (along k for one column, so B lands transposed, n-major), each
-//     element with 2-byte loads guarded by m < M, n < N, k < K (zero otherwise), and writes a run
-//     with one 16-byte LDS store; LDS rows are padded to 40 values so runs stay 16-byte aligned;
-//   * both operand fragments are then plain 16-byte LDS reads, fed to v_mfma_f32_16x16x32 with B as
-//     the first operand (as in the fast kernels: each lane holds 4 consecutive output columns of one
-//     row) and fp32 accumulators, k ascending;
+//   * every element with a 2-byte load, A as pairs along k (a wave reads 4 rows x 64 contiguous
+//     bytes per instruction), B as 8-deep runs along k of one column (consecutive threads,
+//     consecutive columns: 128 contiguous bytes per instruction); an element outside the matrices
+//     (m >= M, n >= N or k >= K) loads element 0 instead and a mask bit turns it into a zero, so
+//     no load is skipped and none waits;
+//   * software-pipelined by one k step in registers: step s + 1's loads are issued right after step
+//     s is written to LDS and land while step s's MFMAs run; the barriers wait for LDS accesses
+//     only, never for those loads;
+//   * in LDS, A row-major (k along a row) and B n-major (B transposed), rows padded to 40 values so
+//     a wave's 16-byte reads stay aligned; both operand fragments are plain 16-byte LDS reads, fed
+//     to v_mfma_f32_16x16x32 with B as the first operand (as in the fast kernels: each lane holds 4
+//     consecutive output columns of one row) and fp32 accumulators, k ascending;
 //   * every output element is stored on its own, guarded by row < M and column < N.
 // Wave grid: 2 x 2 waves of 32 x 32 (64 tiles) or 64 x 64 (128 tiles), 2 x 4 waves of 128 x 64
 // (256 tiles). This path trades speed for generality; the aligned shapes never reach it.
@@ -40,9 +45,11 @@ __global__ __launch_bounds__(AnyShape<BM>::kThreads) void gemm_any_kernel(
   using S = AnyShape<BM>;
   constexpr int BN = BM;
   constexpr int WM = S::WM, WN = S::WN, TM = S::TM, TN = S::TN, kPitch = S::kPitch;
-  constexpr int kRunsA = BM * kBK / 8;          // 8-element runs per step
-  constexpr int kRunsB = BN * kBK / 8;
-  static_assert(kRunsA % S::kThreads == 0 && kRunsB % S::kThreads == 0, "whole runs per thread");
+  constexpr int kPairsA = BM * kBK / 2 / S::kThreads;   // (row, 2 k) pairs of A per thread and step
+  constexpr int kRunsB = BN * kBK / 8 / S::kThreads;    // (column, 8 k) runs of B per thread and step
+  static_assert(kPairsA * S::kThreads == BM * kBK / 2 && kRunsB * S::kThreads == BN * kBK / 8,
+                "whole pairs and runs per thread");
+  static_assert(2 * kPairsA <= 32 && 8 * kRunsB <= 32, "one mask bit per fetched element");
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[BM * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t lds_b[BN * kPitch];
 
@@ -53,6 +60,59 @@ __global__ __launch_bounds__(AnyShape<BM>::kThreads) void gemm_any_kernel(
   const int P = num_programs;
   if (static_cast<int>(blockIdx.x) >= order.tiles) return;
   const int nk = (K + kBK - 1) / kBK;
+
+  // One k step's operand elements as loaded. They come through buffer loads: a descriptor (in
+  // scalar registers) per tile for A and per k step for B whose range ends after the last element
+  // of the matrix that the tile or step may touch, so elements past it read as zero; an element
+  // inside the range but outside the matrix (k >= K in A, a column >= N in B) gets an offset past
+  // the range. No load is skipped and none is waited for until the values are written to LDS.
+  constexpr int kOut = 0x7FFFFFF0;   // an offset past every range
+  constexpr int kRsrcFlags = 0x00020000;
+  uint16_t ra[2 * kPairsA], rb[8 * kRunsB];
+  // A pair p of this thread: row g / 16 of the tile, k 2 (g mod 16) and the next (g = p threads +
+  // tid): a wave reads 4 rows x 64 contiguous bytes per load instruction
+  auto fetch = [&](__amdgpu_buffer_rsrc_t rsrc_a, int n0, int k0) {
+#pragma unroll
+    for (int p = 0; p < kPairsA; ++p) {
+      const int g = p * S::kThreads + tid;
+      const int k = k0 + 2 * (g & 15);
+      const int off = ((g >> 4) * K + k) * 2;   // rows past M lie past the range
+      ra[2 * p] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_a, k < K ? off : kOut, 0, 0);
+      ra[2 * p + 1] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_a, k + 1 < K ? off + 2 : kOut, 0, 0);
+    }
+    // B run q: column g mod BN of the tile (consecutive threads, consecutive columns: 128
+    // contiguous bytes per load instruction), k 8 (g / BN) .. + 7 of the step; the step's
+    // descriptor starts at (k0, n0) and ends after element (min(k0 + 32, K) - 1, N - 1), so
+    // k >= K lies past it
+    const int rows_k = K - k0 < kBK ? K - k0 : kBK;
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(B + static_cast<size_t>(k0) * N + n0), 0, (rows_k * N - n0) * 2, kRsrcFlags);
+#pragma unroll
+    for (int q = 0; q < kRunsB; ++q) {
+      const int g = q * S::kThreads + tid;
+      const int c = g % BN, kc = (g / BN) * 8;
+      const bool col_in = n0 + c < N;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        rb[8 * q + e] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_b, col_in ? ((kc + e) * N + c) * 2 : kOut, 0, 0);
+    }
+  };
+  // the fetched step into LDS: A row-major (k along a row), B n-major (k along a column's row)
+  auto stash = [&]() {
+    auto pack = [](uint16_t lo, uint16_t hi) { return uint32_t{lo} | (uint32_t{hi} << 16); };
+#pragma unroll
+    for (int p = 0; p < kPairsA; ++p) {
+      const int g = p * S::kThreads + tid;
+      *reinterpret_cast<uint32_t*>(lds_a + (g >> 4) * kPitch + 2 * (g & 15)) = pack(ra[2 * p], ra[2 * p + 1]);
+    }
+#pragma unroll
+    for (int q = 0; q < kRunsB; ++q) {
+      const int g = q * S::kThreads + tid;
+      const uint16_t* v = rb + 8 * q;
+      *reinterpret_cast<uint4*>(lds_b + (g % BN) * kPitch + (g / BN) * 8) =
+          make_uint4(pack(v[0], v[1]), pack(v[2], v[3]), pack(v[4], v[5]), pack(v[6], v[7]));
+    }
+  };
 
   int iter = 0;
   for (int t = blockIdx.x; t < order.tiles; t += P, ++iter) {
@@ -69,48 +129,21 @@ __global__ __launch_bounds__(AnyShape<BM>::kThreads) void gemm_any_kernel(
       rec[4] = xcc_id();
     }
     const int m0 = tm * BM, n0 = tn * BN;
+    // A's rows of this tile: [m0, min(m0 + BM, M)), K elements each
+    const int rows_a = M - m0 < BM ? M - m0 : BM;
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(A + static_cast<size_t>(m0) * K), 0, rows_a * K * 2, kRsrcFlags);
     f32x4_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    fetch(rsrc_a, n0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      const int k0 = kt * kBK;
-      // A run q: row q / 4 of the tile, k offset 8 (q mod 4)
-#pragma unroll
-      for (int it = 0; it < kRunsA / S::kThreads; ++it) {
-        const int q = tid + it * S::kThreads;
-        const int r = q >> 2, kc = (q & 3) * 8;
-        const int row = m0 + r;
-        uint16_t v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = k0 + kc + e;
-          v[e] = (row < M && k < K) ? A[static_cast<size_t>(row) * K + k] : uint16_t{0};
-        }
-        *reinterpret_cast<uint4*>(lds_a + r * kPitch + kc) =
-            make_uint4(v[0] | (uint32_t{v[1]} << 16), v[2] | (uint32_t{v[3]} << 16),
-                       v[4] | (uint32_t{v[5]} << 16), v[6] | (uint32_t{v[7]} << 16));
-      }
-      // B run q: column q mod BN of the tile (consecutive threads, consecutive columns), k offset
-      // 8 (q / BN); stored n-major
-#pragma unroll
-      for (int it = 0; it < kRunsB / S::kThreads; ++it) {
-        const int q = tid + it * S::kThreads;
-        const int c = q % BN, kc = (q / BN) * 8;
-        const int col = n0 + c;
-        uint16_t v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = k0 + kc + e;
-          v[e] = (col < N && k < K) ? B[static_cast<size_t>(k) * N + col] : uint16_t{0};
-        }
-        *reinterpret_cast<uint4*>(lds_b + c * kPitch + kc) =
-            make_uint4(v[0] | (uint32_t{v[1]} << 16), v[2] | (uint32_t{v[3]} << 16),
-                       v[4] | (uint32_t{v[5]} << 16), v[6] | (uint32_t{v[7]} << 16));
-      }
-      __syncthreads();
+      stash();
+      lds_barrier();   // the step's operands are in LDS (and no load is waited for here)
+      if (kt + 1 < nk) fetch(rsrc_a, n0, (kt + 1) * kBK);
       // fragments: lane l takes row (col) l mod 16 of a 16-block, k 8 (l / 16) .. + 7
       uint4 af[TM], bf[TN];
 #pragma unroll
@@ -123,7 +156,7 @@ __global__ __launch_bounds__(AnyShape<BM>::kThreads) void gemm_any_kernel(
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32<kBf16>(bf[j], af[i], acc[i][j]);
-      __syncthreads();
+      lds_barrier();   // every wave has read the step before the next one is written
     }
     if (trace != nullptr && tid == 0) {
       int32_t* rec = trace + kTraceInts * static_cast<size_t>(t);
