@@ -72,13 +72,23 @@ __global__ __launch_bounds__(AnyShape<BM>::kThreads) void gemm_any_kernel(
   // A pair p of this thread: row g / 16 of the tile, k 2 (g mod 16) and the next (g = p threads +
   // tid): a wave reads 4 rows x 64 contiguous bytes per load instruction
   auto fetch = [&](__amdgpu_buffer_rsrc_t rsrc_a, int n0, int k0) {
+    if (k0 + kBK <= K) {   // every k of the step lies inside the rows: one offset per pair
 #pragma unroll
-    for (int p = 0; p < kPairsA; ++p) {
-      const int g = p * S::kThreads + tid;
-      const int k = k0 + 2 * (g & 15);
-      const int off = ((g >> 4) * K + k) * 2;   // rows past M lie past the range
-      ra[2 * p] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_a, k < K ? off : kOut, 0, 0);
-      ra[2 * p + 1] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_a, k + 1 < K ? off + 2 : kOut, 0, 0);
+      for (int p = 0; p < kPairsA; ++p) {
+        const int g = p * S::kThreads + tid;
+        const int off = ((g >> 4) * K + k0 + 2 * (g & 15)) * 2;   // rows past M lie past the range
+        ra[2 * p] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_a, off, 0, 0);
+        ra[2 * p + 1] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_a, off + 2, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < kPairsA; ++p) {
+        const int g = p * S::kThreads + tid;
+        const int k = k0 + 2 * (g & 15);
+        const int off = ((g >> 4) * K + k) * 2;
+        ra[2 * p] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_a, k < K ? off : kOut, 0, 0);
+        ra[2 * p + 1] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_a, k + 1 < K ? off + 2 : kOut, 0, 0);
+      }
     }
     // B run q: column g mod BN of the tile (consecutive threads, consecutive columns: 128
     // contiguous bytes per load instruction), k 8 (g / BN) .. + 7 of the step; the step's
@@ -99,7 +109,13 @@ __global__ __launch_bounds__(AnyShape<BM>::kThreads) void gemm_any_kernel(
   };
   // the fetched step into LDS: A row-major (k along a row), B n-major (k along a column's row)
   auto stash = [&]() {
-    auto pack = [](uint16_t lo, uint16_t hi) { return uint32_t{lo} | (uint32_t{hi} << 16); };
+    // packed by an asm statement, which consumes the loaded registers here and no earlier: left to
+    // itself the compiler packs (and so waits) right after the loads, before the MFMAs
+    auto pack = [](uint16_t lo, uint16_t hi) {
+      uint32_t r;
+      asm volatile("v_lshl_or_b32 %0, %1, 16, %2" : "=v"(r) : "v"(uint32_t{hi}), "v"(uint32_t{lo}));
+      return r;
+    };
 #pragma unroll
     for (int p = 0; p < kPairsA; ++p) {
       const int g = p * S::kThreads + tid;
@@ -144,18 +160,18 @@ __global__ __launch_bounds__(AnyShape<BM>::kThreads) void gemm_any_kernel(
       stash();
       lds_barrier();   // the step's operands are in LDS (and no load is waited for here)
       if (kt + 1 < nk) fetch(rsrc_a, n0, (kt + 1) * kBK);
-      // fragments: lane l takes row (col) l mod 16 of a 16-block, k 8 (l / 16) .. + 7
-      uint4 af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(lds_a + (wm * WM + i * 16 + (lane & 15)) * kPitch + 8 * (lane >> 4));
+      // fragments: lane l takes row (col) l mod 16 of a 16-block, k 8 (l / 16) .. + 7; all of B's,
+      // then A's one block row at a time
+      uint4 bf[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         bf[j] = *reinterpret_cast<const uint4*>(lds_b + (wn * WN + j * 16 + (lane & 15)) * kPitch + 8 * (lane >> 4));
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        const uint4 af = *reinterpret_cast<const uint4*>(lds_a + (wm * WM + i * 16 + (lane & 15)) * kPitch + 8 * (lane >> 4));
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32<kBf16>(bf[j], af[i], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32<kBf16>(bf[j], af, acc[i][j]);
+      }
       lds_barrier();   // every wave has read the step before the next one is written
     }
     if (trace != nullptr && tid == 0) {
