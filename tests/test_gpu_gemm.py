@@ -332,7 +332,7 @@ def test_ragged_integer_16bit_out_is_the_rounded_exact_sum(dtype, tile):
 # N or K not a multiple of 8: rows of A or B are not whole 16-byte chunks and the element-wise path
 # runs (every load and store masked at the edges, as the swizzle page's kernel masks them)
 ODD = [(257, 263, 259), (1, 1, 1), (1000, 1001, 1003), (3, 5, 7), (64, 63, 65), (129, 130, 31),
-       (300, 256, 100), (520, 8, 13)]
+       (300, 256, 100), (520, 8, 13), (200, 520, 97), (77, 16, 33)]
 
 
 @pytest.mark.parametrize("tile", [64, 128, 256])
@@ -349,13 +349,16 @@ def test_odd_n_k_full_oracle(M, N, K, dtype, tile):
     check_gemm(host64(c32), a, b, dtype, K, "f32", what=f"odd fp32 {M}x{N}x{K} {dtype} tile {tile}")
 
 
+@pytest.mark.parametrize("N", [263, 264])
 @pytest.mark.parametrize("tile", [64, 128, 256])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_odd_n_k_integer_exact_untouched_padding_and_schedules(dtype, tile):
+def test_odd_n_k_integer_exact_untouched_padding_and_schedules(dtype, tile, N):
     # integer inputs in [-7, 7]: fp32 sums are exact, 16-bit outputs the exact sum rounded to nearest
     # even; the output sits inside a larger buffer whose other elements must stay untouched; every
-    # order, remap and launch style gives the same bits
-    M, N, K = 301, 263, 1001
+    # order, remap and launch style gives the same bits. N = 263 moves B element by element, N = 264
+    # (a multiple of 8, K odd) in 16-byte chunks, A in both in unaligned 16-byte chunks and a last
+    # partial k step
+    M, K = 301, 1001
     a = synth.int_valued((M, K), 45, -7, 7, dtype)
     b = synth.int_valued((K, N), 46, -7, 7, dtype)
     exact = og.gemm(a, b, dtype)

@@ -173,7 +173,7 @@ int validate_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, i
 }
 
 int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persistent,
-                     int num_programs, int* out, bool chunked = true) {
+                     int num_programs, int* out, bool chunked = true, int64_t N = 0) {
   if (num_programs > 0) {
     *out = num_programs;
     return TBL_OK;
@@ -187,7 +187,7 @@ int resolve_programs(int dtype, int bm, int bn, int bk, int64_t tiles, int persi
   if (rc != TBL_OK) return rc;
   int per_cu = 0;
   const hipError_t e = chunked ? tbl::gemm_blocks_per_cu(dtype, bm, bn, bk, &per_cu)
-                               : tbl::gemm_any_blocks_per_cu(dtype, bm, &per_cu);
+                               : tbl::gemm_any_blocks_per_cu(dtype, bm, static_cast<int>(N), &per_cu);
   if (e != hipSuccess) return TBL_ERR_HIP;
   if (per_cu < 1) per_cu = 1;
   const int64_t cap = static_cast<int64_t>(d.cus) * per_cu;
@@ -241,7 +241,7 @@ int tbl_gemm_tiled(const void* A, const void* B, void* C, int64_t M, int64_t N, 
   const bool chunked = chunk_rows(N, K);
   int programs = 0;
   rc = resolve_programs(dtype, block_m, block_n, block_k, static_cast<int64_t>(gm) * gn, persistent,
-                        num_programs, &programs, chunked);
+                        num_programs, &programs, chunked, N);
   if (rc != TBL_OK) return rc;
   tbl::GemmLaunch a;
   a.A = A;
@@ -453,7 +453,7 @@ int tbl_default_num_programs(int64_t M, int64_t N, int64_t K, int dtype, int per
   tile_rule(M, N, &bm, &bn, &bk);
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TBL_ERR_SHAPE;
   return resolve_programs(dtype, bm, bn, bk, ((M + bm - 1) / bm) * ((N + bn - 1) / bn), persistent, 0,
-                          num_programs, chunk_rows(N, K));
+                          num_programs, chunk_rows(N, K), N);
 }
 
 int tbl_tile_map(int swizzle_mode, int grid_m, int grid_n, int group_size, int32_t* tile_m,

@@ -28,7 +28,8 @@ bool gemm_tile_supported(int bm, int bn, int bk);
 // Shapes whose rows are not whole 16-byte chunks (N or K not a multiple of 8): the element-wise
 // load path of gemm_any.hip, for the tile shapes gemm_tile_supported accepts (bm == bn).
 hipError_t launch_gemm_any(int dtype, int bm, const GemmLaunch& a, hipStream_t s);
-hipError_t gemm_any_blocks_per_cu(int dtype, int bm, int* out);
+// Its two forms: B moved in 16-byte chunks when N is a multiple of 8, element by element otherwise.
+hipError_t gemm_any_blocks_per_cu(int dtype, int bm, int N, int* out);
 // C = 0 for K = 0 (the empty sum): zeroes ``bytes`` bytes of C (16-byte aligned, an even count).
 hipError_t launch_gemm_zero(void* C, int64_t bytes, hipStream_t s);
 // The 256 x 256 x 32 kernel with the dynamic (work-queue) schedule; a.work and a.xcd_aware set.
