@@ -139,8 +139,10 @@ enum {
  *                 ceil(N/BN); loads and stores are masked at every edge, as the page's kernel masks
  *                 them. When N and K are multiples of 8 (rows of A and B are whole 16-byte chunks)
  *                 the fast kernels run, moving operands with 16-byte direct-to-LDS loads; otherwise
- *                 an element-wise load path with the same tile grid, schedule and trace (far
- *                 slower: it exists for generality).
+ *                 a general path with the same tile grid, schedule and trace, which moves
+ *                 operands through registers (A in unaligned 16-byte chunks, B in 16-byte chunks
+ *                 when N is a multiple of 8, else element by element) and runs at roughly 40-65 %
+ *                 of the fast kernels' rate at 4096-sized shapes.
  *   dtype         TBL_F16, TBL_BF16, TBL_F16_F32OUT or TBL_BF16_F32OUT.
  *   swizzle_mode  a TBL_* order, optionally | TBL_XCD_REMAP and | TBL_CLUSTER(cm, cn). Morton and
  *                 XOR need a square power-of-two grid of (cluster) tiles (TBL_ERR_NOT_BIJECTIVE
@@ -153,7 +155,7 @@ enum {
  *                 schedule of the swizzle page's persistent loop); < 0 is TBL_ERR_INVALID_ARG.
  *   stream        hipStream_t or NULL.
  * Every output element is computed by exactly one workgroup with fp32 accumulation over k in
- * ascending 32-deep 16x16x32 MFMA steps (every tile shape and the element-wise path; the 32x32x16
+ * ascending 32-deep 16x16x32 MFMA steps (every tile shape and the general path; the 32x32x16
  * form of tbl_gemm_lds_layout takes two 16-deep steps instead, which on gfx950 leave the same
  * bits), so the result does not depend on the order, the remap flag, persistence, num_programs or
  * the tile shape.

@@ -203,7 +203,7 @@ def test_gemm_tiled_validation():
     assert _tiled(bm=32, bn=32) == tbl.ERR_SHAPE
     assert _tiled(bm=64, bn=128) == tbl.ERR_SHAPE
     assert _tiled(bk=64) == tbl.ERR_SHAPE
-    # N and K need not be multiples of 8 here (the element-wise path); the other checks still apply
+    # N and K need not be multiples of 8 here (the general path); the other checks still apply
     assert _tiled(K=513, bk=64) == tbl.ERR_SHAPE and _tiled(N=515, bm=32, bn=32) == tbl.ERR_SHAPE
     assert _tiled(mode=tbl.MORTON, M=1024, N=512, bm=128, bn=128) == tbl.ERR_NOT_BIJECTIVE
     assert _tiled(A=MISALIGNED) == tbl.ERR_ALIGN

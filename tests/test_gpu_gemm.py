@@ -12,7 +12,7 @@ Workloads (inputs from thread_block_lds_amd.synth, A seed s, B seed s+1):
   4096^3 fp16 uniform[-1,1], 256x256 tiles (16x16 grid), row / panel 4,8,16 / Morton / XOR;
   8192^3 bf16 N(0,1)/sqrt(K), persistent group-major 8 and serpentine 8;
   10240 x 6144 x 2048 fp16, 40x24 grid, panel 8/16 and serpentine 8/16, both launch styles;
-  ragged shapes, N and K included (odd N or K run the element-wise path), every tile shape.
+  ragged shapes, N and K included (odd N or K run the general path), every tile shape.
 Large workloads are checked on sampled rows that touch every tile row (every tile column is in
 every row), plus bit-identity of the whole output across orders.
 """
@@ -329,7 +329,7 @@ def test_ragged_integer_16bit_out_is_the_rounded_exact_sum(dtype, tile):
     assert torch.all(big[M:] == -5.0), (dtype, tile)
 
 
-# N or K not a multiple of 8: rows of A or B are not whole 16-byte chunks and the element-wise path
+# N or K not a multiple of 8: rows of A or B are not whole 16-byte chunks and the general path
 # runs (every load and store masked at the edges, as the swizzle page's kernel masks them)
 ODD = [(257, 263, 259), (1, 1, 1), (1000, 1001, 1003), (3, 5, 7), (64, 63, 65), (129, 130, 31),
        (300, 256, 100), (520, 8, 13), (200, 520, 97), (77, 16, 33)]
@@ -388,7 +388,7 @@ def test_odd_n_k_integer_exact_untouched_padding_and_schedules(dtype, tile, N):
 
 
 def test_odd_n_k_tile_shapes_bit_identical():
-    # the element-wise path takes 32-deep 16x16x32 steps in every tile shape
+    # the general path takes 32-deep 16x16x32 steps in every tile shape
     M, N, K = 257, 263, 259
     a, b = synth.gemm_operands(M, N, K, "bf16", "normal", seed=8)
     ad, bd = dev16(a, "bf16"), dev16(b, "bf16")
@@ -417,7 +417,7 @@ def test_odd_n_k_trace_matches_oracle_schedule():
 def test_k_tail_does_not_mix_rows():
     # A K tail reads past the end of each row of A; those elements belong to the next row. An Inf
     # placed at the start of row 1 must only reach row 1 of C.
-    # (K = 41: the element-wise path, whose per-element guards must do the same)
+    # (K = 41: the general path, whose masked last k step must do the same)
     for K in (40, 41):
         M, N = 64, 64
         a = synth.f16_uniform((M, K), 51)

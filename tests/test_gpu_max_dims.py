@@ -87,7 +87,7 @@ def test_max_n():
 
 
 def test_max_k_elementwise_path():
-    # N and K not multiples of 8 take the element-wise load path; K one below the maximum
+    # N and K not multiples of 8 take the general path; K one below the maximum
     M, N, K = 3, 5, BIG - 1
     a, b = _ints(M, N, K, 77)
     ad, bd = dev16(a, "bf16"), dev16(b, "bf16")

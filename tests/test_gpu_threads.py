@@ -1,7 +1,7 @@
 """GPU test: the C-ABI called from several host threads at once. Its only global state is the
 per-device property cache, guarded by a lock, so calls from four threads, each on its own stream,
 must give the same bits as the same calls made one after the other (GEMMs of every tile shape,
-the element-wise path, the dynamic schedule, tile maps and transposes; ctypes releases the
+the general path, the dynamic schedule, tile maps and transposes; ctypes releases the
 interpreter lock during each call, so the threads do overlap inside the library)."""
 
 import threading
@@ -19,7 +19,7 @@ from _helpers import dev16
 pytestmark = pytest.mark.gpu
 
 # (M, N, K, mode, group, persistent) per job; shapes pick the 64, 128 and 256 tiles and the
-# element-wise path (N = 100)
+# general path (N = 100)
 JOBS = [(512, 512, 512, tm.PANEL, 4, False), (2048, 2048, 512, tm.SERPENTINE | tm.XCD_REMAP, 2, True),
         (4096, 4096, 512, tm.MORTON, 1, False), (700, 100, 300, tm.ROW, 1, True),
         (2048, 2048, 1024, tm.XOR | tm.XCD_REMAP, 1, False)]

@@ -140,7 +140,7 @@ void tile_rule(int64_t M, int64_t N, int* bm, int* bn, int* bk) {
 }
 
 // Rows of A and B are whole 16-byte chunks: the fast kernels' direct loads apply; otherwise the
-// element-wise path (gemm_any.hip) runs.
+// general path (gemm_any.hip) runs.
 bool chunk_rows(int64_t N, int64_t K) { return N % 8 == 0 && K % 8 == 0; }
 
 // general: the entry points for any shape (tbl_gemm, tbl_gemm_tiled): N and K need not be
