@@ -1,6 +1,6 @@
 """GPU parity on IEEE special values, through every GEMM path (64, 128 and 256 tiles, the
-general path for N and K that are not multiples of 8, and the dynamic schedule): subnormal
-fp16 and bf16 operands, NaN and infinities among the operands, and results beyond the fp16 range.
+general path for N and K that are not multiples of 8, with B element by element or in 16-byte
+chunks, and the dynamic schedule): subnormal fp16 and bf16 operands, NaN and infinities among the operands, and results beyond the fp16 range.
 
 The oracle is the fp64 definition of C = A B that "CUDA Thread Block Swizzle" (section "CUDA
 Thread Block Swizzle Benchmark") computes with fp32 accumulation, in IEEE arithmetic. Every case
@@ -21,9 +21,10 @@ from _helpers import host64
 
 pytestmark = pytest.mark.gpu
 
-# (tile, M, N, K): the three fast kernels with partial tiles, and the general path
+# (tile, M, N, K): the three fast kernels with partial tiles, and the general path (B element by
+# element for N = 9, in 16-byte chunks for N = 136 and 264 with K odd)
 PATHS = [((64, 64, 32), 70, 72, 96), ((128, 128, 32), 130, 136, 64), ((256, 256, 32), 260, 264, 40),
-         ((64, 64, 32), 37, 9, 77)]
+         ((64, 64, 32), 37, 9, 77), ((128, 128, 32), 130, 136, 77), ((256, 256, 32), 260, 264, 45)]
 DT = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 
