@@ -1,6 +1,7 @@
 """GPU parity on IEEE special values, through every GEMM path (64, 128 and 256 tiles, the
 general path for N and K that are not multiples of 8, with B element by element or in 16-byte
-chunks, and the dynamic schedule): subnormal fp16 and bf16 operands, NaN and infinities among the operands, and results beyond the fp16 range.
+chunks, and the dynamic schedule): subnormal fp16 and bf16 operands, NaN and infinities among
+the operands, and results beyond the fp16 range.
 
 The oracle is the fp64 definition of C = A B that "CUDA Thread Block Swizzle" (section "CUDA
 Thread Block Swizzle Benchmark") computes with fp32 accumulation, in IEEE arithmetic. Every case
