@@ -49,6 +49,8 @@ Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-counters] [--n
        python bench.py --page-sweep        (the swizzle page's own 8192^3 128x128x32 sweep: one
                                             JSON line with TFLOP/s, TCC hit rates, both L2 models
                                             and the Spearman coefficients)
+       python bench.py --general-sweep     (shapes whose N or K is not a multiple of 8, per tile
+                                            shape, with the aligned 4096^3 beside them)
 """
 
 import argparse
@@ -989,6 +991,50 @@ def lds_sweep_pass():
     print("lds sweep pass done", flush=True)
 
 
+# shapes whose N or K is not a multiple of 8 (the general path), with the aligned 4096^3 beside them
+GENERAL_SHAPES = [(4096, 4095, 4096), (4096, 4096, 4095), (8192, 8192, 1020), (8192, 8190, 1022),
+                  (2048, 2047, 2049), (1000, 1001, 1003)]
+
+
+def general_sweep(reps=10):
+    """bench.py --general-sweep: the GEMM on shapes whose N or K is not a multiple of 8, fp16
+    uniform[-1, 1] inputs, fp16 output, panel g4: the default tile and each tile shape, median of
+    ``reps`` launches timed one by one with HIP events on the launch stream; one JSON line."""
+    import torch
+    import thread_block_lds_amd as tbl
+    from thread_block_lds_amd import synth
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    out = {"workload": "fp16 uniform[-1,1] -> fp16 (fp32 accumulate), panel g4, non-persistent",
+           "shapes": {}}
+
+    def timed(ad, bd, c, tile):
+        for _ in range(2):
+            tbl.gemm(ad, bd, c, tile=tile, mode=2, group=4, stream=stream.cuda_stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            tbl.gemm(ad, bd, c, tile=tile, mode=2, group=4, stream=stream.cuda_stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
+
+    for M, N, K in GENERAL_SHAPES + [(4096, 4096, 4096)]:
+        a, b = synth.gemm_operands(M, N, K, "f16", "uniform", seed=0)
+        ad, bd = _dev16(a, torch, torch.float16), _dev16(b, torch, torch.float16)
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        row = {"path": "fast" if N % 8 == 0 and K % 8 == 0 else
+               ("general, B in 16-byte chunks" if N % 8 == 0 else "general, B element by element"),
+               "default_tile": list(tbl.gemm_tile_shape(M, N, K))}
+        for tile in (None, (64, 64, 32), (128, 128, 32), (256, 256, 32)):
+            ms = timed(ad, bd, c, tile)
+            row["default" if tile is None else f"{tile[0]}x{tile[1]}x{tile[2]}"] = {
+                "ms": round(ms, 4), "tflops": round(2.0 * M * N * K / ms / 1e9, 1)}
+        out["shapes"][f"{M}x{N}x{K}"] = row
+        print(f"{M}x{N}x{K}: {row}", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
 def lds_sweep(reps=10):
     """Every compiled LDS-layout variant at 4096^3 (row order): measured SQ_LDS_BANK_CONFLICT per
     launch against the oracle's prediction, and the median kernel time."""
@@ -1047,6 +1093,7 @@ def main():
     ap.add_argument("--page-sweep", action="store_true")
     ap.add_argument("--page-sweep-pass", action="store_true")
     ap.add_argument("--lds-sweep", action="store_true")
+    ap.add_argument("--general-sweep", action="store_true")
     ap.add_argument("--lds-sweep-pass", action="store_true")
     ap.add_argument("--l2-check", action="store_true")
     ap.add_argument("--l2-check-pass", action="store_true")
@@ -1085,6 +1132,9 @@ def main():
         return
     if args.lds_sweep:
         lds_sweep()
+        return
+    if args.general_sweep:
+        general_sweep()
         return
     if args.l2_check:
         l2_check()
