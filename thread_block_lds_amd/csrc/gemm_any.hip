@@ -9,8 +9,8 @@
 // optional trace -- and moves operands through registers with buffer loads whose ranges (and
 // offsets past them) give zeros outside the matrices:
 //   * A in 16-byte chunks along k in every full k step, at whatever 2-byte alignment the rows have
-//     (gfx950 serves unaligned buffer loads; checked on the device); in a last, partial k step,
-//     element pairs with k >= K masked;
+//     (gfx950 serves unaligned buffer loads; the odd-K parity tests depend on it); in a last,
+//     partial k step, element pairs with k >= K masked;
 //   * B in 16-byte chunks along n when N is a multiple of 8 (rows then stay 16-byte aligned), laid
 //     out k-major in LDS and read with transposing reads as in the four-wave kernel; otherwise
 //     element by element along k for each column (consecutive threads, consecutive columns), laid
