@@ -88,9 +88,9 @@ __global__ __launch_bounds__(AnyShape<BM>::kThreads) void gemm_any_kernel(
   // A in full k steps (k0 + 32 <= K): 16-byte chunks, chunk c of this thread row g / 4 of the tile,
   // k 8 (g mod 4) .. + 7 (g = c threads + tid; a wave reads 16 rows x 64 contiguous bytes per
   // instruction). A row of A starts on a 16-byte boundary only when K is a multiple of 8; the
-  // loads take any 2-byte alignment (gfx950 runs them unaligned; the odd-K parity tests depend on it), and each
-  // chunk lies inside its row, so none straddles the end of the range (the range check zeroes
-  // whole dwords)
+  // loads take any 2-byte alignment (gfx950 runs them unaligned; the odd-K parity tests depend on
+  // it), and each chunk lies inside its row, so none straddles the end of the range (the range
+  // check zeroes whole dwords)
   i32x4v_t wa[kChunksA], wb[kWideB ? kChunksB : 1];
   uint16_t rb[kWideB ? 1 : 8 * kRunsB];
   auto fetch = [&](__amdgpu_buffer_rsrc_t rsrc_a, int n0, int k0) {
